@@ -1,0 +1,254 @@
+"""Python binding of libfp8bq (FP8 blockwise-quantized linear layer for MI355X / gfx950).
+
+Argument marshalling only: every function below passes torch tensors' device pointers, sizes,
+leading dimensions and the current HIP stream to the C-ABI entry point of the same name declared in
+``include/fp8bq.h``; all computation happens in the library's HIP kernels.  PyTorch provides device
+memory and streams.  If the library is not built, importing the binding's functions raises.
+
+Raw entry points (same names and argument order as the C ABI, tensors in place of pointers):
+
+    fp8bq_quantize_act_1x128(x, fmt, q, s)
+    fp8bq_quantize_act_128x1(x, fmt, qt, st)
+    fp8bq_quantize_weight_128x128(w, fmt, q, s)
+    fp8bq_gemm_fprop(qx, sx, fx, qw, sw, fw, y, ws=None)
+    fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws=None)
+    fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None)
+    fp8bq_gemm_workspace_size(op, M, N, K)
+
+Allocating helpers (outputs created with torch on the input's device):
+
+    quantize_act_1x128(x, fmt) -> (q [R, C] uint8, s [C/128, R] float32)
+    quantize_act_128x1(x, fmt) -> (qt [C, R] uint8, st [R/128, C] float32)
+    quantize_weight_128x128(w, fmt) -> (q [N, K] uint8, s [N/128, K/128] float32)
+    gemm_fprop(qx, sx, qw, sw, fx=E4M3, fw=E4M3, out_dtype=bf16) -> y [M, N]
+    gemm_dgrad(qdy, sdy, qw, sw, fdy=E4M3, fw=E4M3, out_dtype=bf16) -> dx [M, K]
+    gemm_wgrad(qdyt, sdyt, qxt, sxt, fdy=E4M3, fx=E4M3, out_dtype=bf16) -> dw [N, K]
+"""
+
+import ctypes
+import os
+
+import torch
+
+E4M3 = 0
+E5M2 = 1
+IN_BF16 = 0
+IN_F32 = 1
+OUT_BF16 = 0
+OUT_F32 = 1
+OP_FPROP = 0
+OP_DGRAD = 1
+OP_WGRAD = 2
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfp8bq.so")
+
+_c_i64 = ctypes.c_int64
+_c_int = ctypes.c_int
+_c_vp = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
+
+_SIGS = {
+    "fp8bq_quantize_act_1x128": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
+    "fp8bq_quantize_act_128x1": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
+    "fp8bq_quantize_weight_128x128": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
+                                      _c_vp],
+    "fp8bq_gemm_fprop": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
+                         _c_int, _c_vp, _c_int, _c_i64, _c_vp, _c_sz, _c_vp],
+    "fp8bq_gemm_dgrad": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
+                         _c_int, _c_vp, _c_int, _c_i64, _c_vp, _c_sz, _c_vp],
+    "fp8bq_gemm_wgrad": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
+                         _c_int, _c_vp, _c_int, _c_i64, _c_vp, _c_sz, _c_vp],
+    "fp8bq_gemm_workspace_size": [_c_int, _c_i64, _c_i64, _c_i64],
+    "fp8bq_status_string": [_c_int],
+    "fp8bq_version": [],
+}
+_RESTYPES = {"fp8bq_gemm_workspace_size": _c_sz, "fp8bq_status_string": ctypes.c_char_p}
+
+_lib = None
+
+
+class Fp8bqError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def lib():
+    """The loaded ctypes library (loads it on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"libfp8bq.so is not built ({LIB_PATH}); run `python -m fp8_blockwise_quantized_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = _RESTYPES.get(name, _c_int)
+        _lib = handle
+    return _lib
+
+
+def status_string(status):
+    return lib().fp8bq_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != 0:
+        raise Fp8bqError(status, where)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ld(t):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
+
+
+def _in_type(t):
+    if t.dtype == torch.bfloat16:
+        return IN_BF16
+    if t.dtype == torch.float32:
+        return IN_F32
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def _out_type(t):
+    if t.dtype == torch.bfloat16:
+        return OUT_BF16
+    if t.dtype == torch.float32:
+        return OUT_F32
+    raise TypeError(f"unsupported output dtype {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+# ---------------------------------------------------------------------------------------------
+# raw entry points
+# ---------------------------------------------------------------------------------------------
+
+def fp8bq_quantize_act_1x128(x, fmt, q, s):
+    R, C = x.shape
+    _check(lib().fp8bq_quantize_act_1x128(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(q), _ld(q), _ptr(s), _ld(s),
+                                          _stream(x)), "fp8bq_quantize_act_1x128")
+
+
+def fp8bq_quantize_act_128x1(x, fmt, qt, st):
+    R, C = x.shape
+    _check(lib().fp8bq_quantize_act_128x1(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(qt), _ld(qt), _ptr(st),
+                                          _ld(st), _stream(x)), "fp8bq_quantize_act_128x1")
+
+
+def fp8bq_quantize_weight_128x128(w, fmt, q, s):
+    N, K = w.shape
+    _check(lib().fp8bq_quantize_weight_128x128(_ptr(w), _in_type(w), N, K, _ld(w), fmt, _ptr(q), _ld(q), _ptr(s),
+                                               _ld(s), _stream(w)), "fp8bq_quantize_weight_128x128")
+
+
+def fp8bq_gemm_workspace_size(op, M, N, K):
+    return int(lib().fp8bq_gemm_workspace_size(int(op), int(M), int(N), int(K)))
+
+
+def _ws_args(ws):
+    if ws is None:
+        return ctypes.c_void_p(0), 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def fp8bq_gemm_fprop(qx, sx, fx, qw, sw, fw, y, ws=None):
+    M, K = qx.shape
+    N = qw.shape[0]
+    wsp, wsb = _ws_args(ws)
+    _check(lib().fp8bq_gemm_fprop(M, N, K, _ptr(qx), _ld(qx), _ptr(sx), _ld(sx), fx, _ptr(qw), _ld(qw), _ptr(sw),
+                                  _ld(sw), fw, _ptr(y), _out_type(y), _ld(y), wsp, wsb, _stream(y)),
+           "fp8bq_gemm_fprop")
+
+
+def fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws=None):
+    M, N = qdy.shape
+    K = qw.shape[1]
+    wsp, wsb = _ws_args(ws)
+    _check(lib().fp8bq_gemm_dgrad(M, N, K, _ptr(qdy), _ld(qdy), _ptr(sdy), _ld(sdy), fdy, _ptr(qw), _ld(qw),
+                                  _ptr(sw), _ld(sw), fw, _ptr(dx), _out_type(dx), _ld(dx), wsp, wsb, _stream(dx)),
+           "fp8bq_gemm_dgrad")
+
+
+def fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None):
+    N, M = qdyt.shape
+    K = qxt.shape[0]
+    wsp, wsb = _ws_args(ws)
+    _check(lib().fp8bq_gemm_wgrad(M, N, K, _ptr(qdyt), _ld(qdyt), _ptr(sdyt), _ld(sdyt), fdy, _ptr(qxt), _ld(qxt),
+                                  _ptr(sxt), _ld(sxt), fx, _ptr(dw), _out_type(dw), _ld(dw), wsp, wsb, _stream(dw)),
+           "fp8bq_gemm_wgrad")
+
+
+# ---------------------------------------------------------------------------------------------
+# allocating helpers
+# ---------------------------------------------------------------------------------------------
+
+def _pad4(n):
+    return max(4, (n + 3) // 4 * 4)
+
+
+def quantize_act_1x128(x, fmt=E4M3):
+    R, C = x.shape
+    q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    s = torch.empty((C // 128, _pad4(R)), dtype=torch.float32, device=x.device)[:, :R]
+    fp8bq_quantize_act_1x128(x, fmt, q, s)
+    return q, s
+
+
+def quantize_act_128x1(x, fmt=E4M3):
+    R, C = x.shape
+    qt = torch.empty((C, R), dtype=torch.uint8, device=x.device)
+    st = torch.empty((R // 128, _pad4(C)), dtype=torch.float32, device=x.device)[:, :C]
+    fp8bq_quantize_act_128x1(x, fmt, qt, st)
+    return qt, st
+
+
+def quantize_weight_128x128(w, fmt=E4M3):
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    fp8bq_quantize_weight_128x128(w, fmt, q, s)
+    return q, s
+
+
+def _workspace(op, M, N, K, device):
+    n = fp8bq_gemm_workspace_size(op, M, N, K)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def gemm_fprop(qx, sx, qw, sw, fx=E4M3, fw=E4M3, out_dtype=torch.bfloat16, out=None, ws=None):
+    M, K = qx.shape
+    N = qw.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=qx.device)
+    if ws is None:
+        ws = _workspace(OP_FPROP, M, N, K, qx.device)
+    fp8bq_gemm_fprop(qx, sx, fx, qw, sw, fw, y, ws)
+    return y
+
+
+def gemm_dgrad(qdy, sdy, qw, sw, fdy=E4M3, fw=E4M3, out_dtype=torch.bfloat16, out=None, ws=None):
+    M, N = qdy.shape
+    K = qw.shape[1]
+    dx = out if out is not None else torch.empty((M, K), dtype=out_dtype, device=qdy.device)
+    if ws is None:
+        ws = _workspace(OP_DGRAD, M, N, K, qdy.device)
+    fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws)
+    return dx
+
+
+def gemm_wgrad(qdyt, sdyt, qxt, sxt, fdy=E4M3, fx=E4M3, out_dtype=torch.bfloat16, out=None, ws=None):
+    N, M = qdyt.shape
+    K = qxt.shape[0]
+    dw = out if out is not None else torch.empty((N, K), dtype=out_dtype, device=qdyt.device)
+    if ws is None:
+        ws = _workspace(OP_WGRAD, M, N, K, qdyt.device)
+    fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws)
+    return dw

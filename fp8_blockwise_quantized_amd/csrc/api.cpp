@@ -1,0 +1,195 @@
+// C-ABI entry points declared in include/fp8bq.h: validate, plan, launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/fp8bq.h"
+#include "launch.hpp"
+#include "plan.hpp"
+#include "validate.hpp"
+
+namespace fp8bq {
+
+constexpr int kMaxDevices = 64;
+// Per-device cache: 0 = unknown, 1 = gfx950, 2 = other architecture.  Benign races (all writers
+// store the same value).
+static std::atomic<int> g_dev_state[kMaxDevices];
+static std::atomic<int> g_dev_cus[kMaxDevices];
+
+// Returns kOk if the current device is a gfx950; fills *cus with its compute-unit count.
+static int current_device(int* cus) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kErrDevice;
+  }
+  int state = g_dev_state[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return kErrDevice;
+    }
+    state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    g_dev_state[dev].store(state, std::memory_order_relaxed);
+  }
+  if (cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return state == 1 ? kOk : kErrDevice;
+}
+
+static int cu_count_or_default() {
+  int cus = 0;
+  if (current_device(&cus) == kOk && cus > 0) return cus;
+  return 256;
+}
+
+static int launched(hipError_t e) { return e == hipSuccess ? kOk : kErrLaunch; }
+
+static int run_gemm(const GemmArgs& g, void* stream) {
+  const int cus = cu_count_or_default();
+  const GemmPlan plan = plan_gemm(g.op, g.M, g.N, g.K, cus);
+  bool empty = false, zero = false;
+  int st = validate_gemm(g, plan.ws_total(), &empty, &zero);
+  if (st != kOk || empty) return st;
+  if ((st = current_device(nullptr)) != kOk) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int oes = g.out_t == 0 ? 2 : 4;
+  int64_t out_rows, out_cols;
+  if (g.op == kOpFprop) {
+    out_rows = g.M; out_cols = g.N;
+  } else if (g.op == kOpDgrad) {
+    out_rows = g.M; out_cols = g.K;
+  } else {
+    out_rows = g.N; out_cols = g.K;
+  }
+  if (zero) return launched(launch_zero_fill(const_cast<void*>(g.out), out_rows, out_cols * oes, g.ldout * oes, s));
+
+  GemmDesc d;
+  d.c = const_cast<void*>(g.out);
+  d.ldc = g.ldout;
+  d.out_f32 = g.out_t;
+  d.fa = g.fa;
+  d.fb = g.fb;
+  d.M = out_rows;
+  d.N = out_cols;
+  d.a = (const uint8_t*)g.qa;
+  d.lda = g.ldqa;
+  d.sa = (const float*)g.sa;
+  d.ldsa = g.ldsa;
+  d.sb = (const float*)g.sb;
+  if (g.op == kOpFprop) {
+    d.K = g.K;
+    d.b = (const uint8_t*)g.qb;
+    d.ldb = g.ldqb;
+    d.sb_mode = kSbBlock128;
+    d.sb_kstride = 1;          // sw[nb * ldsw + kb]
+    d.sb_nstride = g.ldsb;
+  } else if (g.op == kOpDgrad) {
+    // W[N, K] is read along its rows (contraction over N): transpose the codes once into the
+    // workspace so both operands are contiguous along the contraction.
+    uint8_t* wt = (uint8_t*)g.ws;
+    hipError_t e = launch_transpose_u8((const uint8_t*)g.qb, g.ldqb, wt, g.N, g.N, g.K, s);
+    if (e != hipSuccess) return kErrLaunch;
+    d.K = g.N;
+    d.b = wt;
+    d.ldb = g.N;
+    d.sb_mode = kSbBlock128;
+    d.sb_kstride = g.ldsb;     // sw[nb * ldsw + k / 128]
+    d.sb_nstride = 1;
+  } else {
+    d.K = g.M;
+    d.b = (const uint8_t*)g.qb;
+    d.ldb = g.ldqb;
+    d.sb_mode = kSbColumn;
+    d.sb_kstride = g.ldsb;     // sxt[mb * ldsxt + k]
+    d.sb_nstride = 0;
+  }
+  void* ws_gemm = plan.ws_gemm ? (uint8_t*)g.ws + plan.ws_transpose : nullptr;
+  return launched(launch_gemm(d, plan, ws_gemm, s));
+}
+
+}  // namespace fp8bq
+
+using namespace fp8bq;
+
+extern "C" {
+
+int fp8bq_quantize_act_1x128(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx, fp8bq_fp8 fmt,
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+  bool empty = false;
+  int st = validate_quant_1x128(x, (int)xt, R, C, ldx, (int)fmt, q, ldq, s, lds, &empty);
+  if (st != kOk || empty) return st;
+  if ((st = current_device(nullptr)) != kOk) return st;
+  return launched(launch_quant_1x128(x, (int)xt, R, C, ldx, (int)fmt, q, ldq, s, lds, (hipStream_t)stream));
+}
+
+int fp8bq_quantize_act_128x1(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx, fp8bq_fp8 fmt,
+                             uint8_t* qt, int64_t ldqt, float* st_, int64_t ldst, void* stream) {
+  bool empty = false;
+  int st = validate_quant_128x1(x, (int)xt, R, C, ldx, (int)fmt, qt, ldqt, st_, ldst, &empty);
+  if (st != kOk || empty) return st;
+  if ((st = current_device(nullptr)) != kOk) return st;
+  return launched(launch_quant_128x1(x, (int)xt, R, C, ldx, (int)fmt, qt, ldqt, st_, ldst, (hipStream_t)stream));
+}
+
+int fp8bq_quantize_weight_128x128(const void* w, fp8bq_in wt, int64_t N, int64_t K, int64_t ldw, fp8bq_fp8 fmt,
+                                  uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+  bool empty = false;
+  int st = validate_quant_128x128(w, (int)wt, N, K, ldw, (int)fmt, q, ldq, s, lds, &empty);
+  if (st != kOk || empty) return st;
+  if ((st = current_device(nullptr)) != kOk) return st;
+  return launched(launch_quant_128x128(w, (int)wt, N, K, ldw, (int)fmt, q, ldq, s, lds, (hipStream_t)stream));
+}
+
+int fp8bq_gemm_fprop(int64_t M, int64_t N, int64_t K, const uint8_t* qx, int64_t ldqx, const float* sx, int64_t ldsx,
+                     fp8bq_fp8 fx, const uint8_t* qw, int64_t ldqw, const float* sw, int64_t ldsw, fp8bq_fp8 fw,
+                     void* y, fp8bq_out yt, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  GemmArgs g{kOpFprop, M, N, K, qx, ldqx, sx, ldsx, (int)fx, qw, ldqw, sw, ldsw, (int)fw, y, (int)yt, ldy, ws,
+             ws_bytes};
+  return run_gemm(g, stream);
+}
+
+int fp8bq_gemm_dgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, int64_t ldqdy, const float* sdy,
+                     int64_t ldsdy, fp8bq_fp8 fdy, const uint8_t* qw, int64_t ldqw, const float* sw, int64_t ldsw,
+                     fp8bq_fp8 fw, void* dx, fp8bq_out dxt, int64_t lddx, void* ws, size_t ws_bytes, void* stream) {
+  GemmArgs g{kOpDgrad, M, N, K, qdy, ldqdy, sdy, ldsdy, (int)fdy, qw, ldqw, sw, ldsw, (int)fw, dx, (int)dxt, lddx,
+             ws, ws_bytes};
+  return run_gemm(g, stream);
+}
+
+int fp8bq_gemm_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdyt, int64_t ldqdyt, const float* sdyt,
+                     int64_t ldsdyt, fp8bq_fp8 fdy, const uint8_t* qxt, int64_t ldqxt, const float* sxt,
+                     int64_t ldsxt, fp8bq_fp8 fx, void* dw, fp8bq_out dwt, int64_t lddw, void* ws, size_t ws_bytes,
+                     void* stream) {
+  GemmArgs g{kOpWgrad, M, N, K, qdyt, ldqdyt, sdyt, ldsdyt, (int)fdy, qxt, ldqxt, sxt, ldsxt, (int)fx, dw, (int)dwt,
+             lddw, ws, ws_bytes};
+  return run_gemm(g, stream);
+}
+
+size_t fp8bq_gemm_workspace_size(fp8bq_op op, int64_t M, int64_t N, int64_t K) {
+  if ((int)op < 0 || (int)op > 2 || M < 0 || N < 0 || K < 0) return 0;
+  return plan_gemm((int)op, M, N, K, cu_count_or_default()).ws_total();
+}
+
+const char* fp8bq_status_string(int status) {
+  switch (status) {
+    case kOk: return "FP8BQ_OK";
+    case kErrNull: return "FP8BQ_ERR_NULL: a required pointer is NULL";
+    case kErrShape: return "FP8BQ_ERR_SHAPE: negative size or a grouped/contracted size not a multiple of 128";
+    case kErrLd: return "FP8BQ_ERR_LD: leading dimension too small or misaligned";
+    case kErrAlign: return "FP8BQ_ERR_ALIGN: pointer not 16-byte aligned";
+    case kErrDtype: return "FP8BQ_ERR_DTYPE: unknown element type";
+    case kErrFormat: return "FP8BQ_ERR_FORMAT: unknown FP8 format";
+    case kErrWorkspace: return "FP8BQ_ERR_WORKSPACE: workspace missing or too small";
+    case kErrDevice: return "FP8BQ_ERR_DEVICE: no current HIP device or it is not gfx950";
+    case kErrLaunch: return "FP8BQ_ERR_LAUNCH: kernel launch failed";
+    case kErrOverlap: return "FP8BQ_ERR_OVERLAP: an output overlaps an input";
+    default: return "FP8BQ_ERR_UNKNOWN";
+  }
+}
+
+int fp8bq_version(void) { return 100; }
+
+}  // extern "C"

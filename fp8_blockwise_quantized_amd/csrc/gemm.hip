@@ -1,0 +1,342 @@
+// Scaled FP8 GEMM for gfx950 (CDNA4): fprop, dgrad and wgrad of the blockwise-quantized linear layer.
+//
+// The product ("小团队也能预训练！普罗2B：RTX5090训练成本不到5090美元", paragraph
+// "FP8发挥RTX 5090的低精度效率优势"; "Puro-2B: Poor Lab's Qwen2-1.5B Trained on RTX 5090 within $5090",
+// "方法关键点", bullet "FP8 blockwise 混合精度") is, in the kernel's TN frame,
+//     C[m, n] = sum_kb sa(kb, m) * sb(kb, n) * sum_{k in kb} dec(A[m, k]) * dec(B[n, k])
+// with FP32 accumulation and BF16 (or FP32) output.  One v_mfma_f32_16x16x128_f8f6f4 covers exactly
+// one 128-long scale block of the contraction for a 16x16 output patch, so the kernel issues each
+// MFMA with a zero accumulator and folds its result into the running FP32 sum with one FMA per
+// output element: acc += mfma * (sa * sb).  Mixed formats (E5M2 gradients x E4M3 weights) are the
+// instruction's per-operand format fields.
+//
+// Operand roles: the MFMA's first operand is the B patch (16 output columns) and its second the A
+// patch (16 output rows).  A lane then holds output row (lane % 16) and four consecutive output
+// columns 4*(lane / 16) + 0..3, so the A-side scale is one value per lane and patch, and the epilogue
+// writes four adjacent BF16 values (8 bytes) per lane.
+//
+// Data movement: per 128-long contraction block the workgroup stages a BM x 128 A tile and a
+// BN x 128 B tile in LDS (double-buffered, one barrier per block), with 16-byte chunks XOR-swizzled
+// by row so the 16-byte fragment reads of 64 lanes spread over all banks.  Global loads for block
+// kb+1 (and its scales) are issued before the MFMAs of block kb.  Workgroup ids are remapped so that
+// each XCD (its own L2) works on a contiguous, row-grouped region of output tiles.
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp8bq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// 16-byte chunk swizzle inside a 128-byte LDS row (conflict-free for 8- and 16-lane phases).
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+constexpr int kGroupRows = 8;  // output tile rows per L2 group
+constexpr int kXcds = 8;
+
+// Bijective remap of the hardware workgroup id (dispatched round-robin over the XCDs) to a logical
+// tile id so each XCD processes a contiguous range of logical ids, then row-grouped tile ordering.
+__device__ __forceinline__ void tile_of(int64_t w, int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  const int64_t nblk = tiles_m * tiles_n;
+  const int64_t q8 = nblk / kXcds, r8 = nblk % kXcds;
+  const int64_t x = w % kXcds;
+  const int64_t L = x * q8 + (x < r8 ? x : r8) + w / kXcds;
+  const int64_t group = (int64_t)kGroupRows * tiles_n;
+  const int64_t gid = L / group;
+  const int64_t first = gid * kGroupRows;
+  const int64_t gsz = (tiles_m - first) < kGroupRows ? (tiles_m - first) : kGroupRows;
+  const int64_t rem = L - gid * group;
+  tm = first + rem % gsz;
+  tn = rem / gsz;
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ v4f mfma_block(const v8i& bpatch, const v8i& apatch) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  // cbsz = format of the first operand (B patch), blgp = format of the second (A patch);
+  // zero E8M0 scale operands select the unscaled instruction.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bpatch, apatch, zero, FB, FA, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v8i lds_patch(const uint8_t* tile, int row, int lane) {
+  const uint8_t* base = tile + row * 128;
+  const int c0 = 2 * (lane >> 4);
+  const int s = swz(row);
+  const v4i lo = *reinterpret_cast<const v4i*>(base + ((c0 ^ s) << 4));
+  const v4i hi = *reinterpret_cast<const v4i*>(base + (((c0 + 1) ^ s) << 4));
+  v8i r = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  return r;
+}
+
+template <int BM, int BN, int WGM, int WGN, int SBM, int FA, int FB, int OUTF32>
+__global__ __launch_bounds__(WGM* WGN * 64) void gemm_tn_kernel(GemmDesc d, int64_t tiles_m, int64_t tiles_n) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WTM = BM / WGM;
+  constexpr int WTN = BN / WGN;
+  constexpr int MI = WTM / 16;
+  constexpr int NI = WTN / 16;
+  constexpr int ACH = BM * 8 / NT;  // 16-byte chunks per thread per stage
+  constexpr int BCH = BN * 8 / NT;
+  constexpr int STAGE = (BM + BN) * 128;
+  static_assert(ACH >= 1 && BCH >= 1, "tile too small for the workgroup");
+  static_assert(SBM != kSbBlock128 || WTN <= 128, "a wave's columns must share one weight block");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  int64_t tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wid / WGN, wn = wid % WGN;
+  const int64_t M = d.M, N = d.N;
+  const int nkb = (int)(d.K / kGroup);
+
+  // global -> LDS assignments
+  const uint8_t* ga[ACH];
+  int la[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int cid = t + NT * i, row = cid >> 3, ch = cid & 7;
+    int64_t gr = m0 + row;
+    gr = gr < M ? gr : M - 1;
+    ga[i] = d.a + gr * d.lda + ch * 16;
+    la[i] = row * 128 + ((ch ^ swz(row)) << 4);
+  }
+  const uint8_t* gb[BCH];
+  int lb[BCH];
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    const int cid = t + NT * i, row = cid >> 3, ch = cid & 7;
+    int64_t gr = n0 + row;
+    gr = gr < N ? gr : N - 1;
+    gb[i] = d.b + gr * d.ldb + ch * 16;
+    lb[i] = BM * 128 + row * 128 + ((ch ^ swz(row)) << 4);
+  }
+  // per-lane scale addressing
+  int64_t sa_row[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    int64_t m = m0 + wm * WTM + 16 * i + (lane & 15);
+    sa_row[i] = m < M ? m : M - 1;
+  }
+  const int64_t ncol_wave = n0 + wn * WTN;
+  const int64_t sb_blk = (ncol_wave / kGroup) * d.sb_nstride;  // kSbBlock128
+  int64_t sb_col[NI];                                           // kSbColumn
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    int64_t n = ncol_wave + 16 * j + 4 * (lane >> 4);
+    sb_col[j] = n < N ? n : N - 4;
+  }
+
+  v4i ra[ACH], rb[BCH];
+  float sav[MI], nsav[MI];
+  float sbb = 0.0f, nsbb = 0.0f;
+  v4f sbc[SBM == kSbColumn ? NI : 1], nsbc[SBM == kSbColumn ? NI : 1];
+
+#define FP8BQ_LOAD_STAGE(KB)                                                                  \
+  do {                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < ACH; ++i) ra[i] =                                   \
+        *reinterpret_cast<const v4i*>(ga[i] + (int64_t)(KB) * kGroup);                        \
+    _Pragma("unroll") for (int i = 0; i < BCH; ++i) rb[i] =                                   \
+        *reinterpret_cast<const v4i*>(gb[i] + (int64_t)(KB) * kGroup);                        \
+  } while (0)
+#define FP8BQ_STORE_STAGE(STG)                                                                \
+  do {                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < ACH; ++i) *reinterpret_cast<v4i*>((STG) + la[i]) = ra[i]; \
+    _Pragma("unroll") for (int i = 0; i < BCH; ++i) *reinterpret_cast<v4i*>((STG) + lb[i]) = rb[i]; \
+  } while (0)
+#define FP8BQ_LOAD_SCALES(KB, SA, SBB, SBC)                                                   \
+  do {                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) SA[i] = d.sa[(int64_t)(KB) * d.ldsa + sa_row[i]]; \
+    if constexpr (SBM == kSbBlock128) {                                                       \
+      SBB = d.sb[(int64_t)(KB) * d.sb_kstride + sb_blk];                                      \
+    } else {                                                                                  \
+      _Pragma("unroll") for (int j = 0; j < NI; ++j) SBC[j] =                                 \
+          *reinterpret_cast<const v4f*>(d.sb + (int64_t)(KB) * d.sb_kstride + sb_col[j]);     \
+    }                                                                                         \
+  } while (0)
+
+  v4f acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+  FP8BQ_LOAD_STAGE(0);
+  FP8BQ_LOAD_SCALES(0, sav, sbb, sbc);
+  FP8BQ_STORE_STAGE(smem);
+  __syncthreads();
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const uint8_t* stage = smem + (kb & 1) * STAGE;
+    const bool more = kb + 1 < nkb;
+    if (more) {
+      FP8BQ_LOAD_STAGE(kb + 1);
+      FP8BQ_LOAD_SCALES(kb + 1, nsav, nsbb, nsbc);
+    }
+    v8i ap[MI], bp[NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) ap[i] = lds_patch(stage, wm * WTM + 16 * i + (lane & 15), lane);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) bp[j] = lds_patch(stage + BM * 128, wn * WTN + 16 * j + (lane & 15), lane);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const v4f p = mfma_block<FA, FB>(bp[j], ap[i]);
+        if constexpr (SBM == kSbBlock128) {
+          const float sc = sav[i] * sbb;
+          acc[i][j][0] = __builtin_fmaf(p[0], sc, acc[i][j][0]);
+          acc[i][j][1] = __builtin_fmaf(p[1], sc, acc[i][j][1]);
+          acc[i][j][2] = __builtin_fmaf(p[2], sc, acc[i][j][2]);
+          acc[i][j][3] = __builtin_fmaf(p[3], sc, acc[i][j][3]);
+        } else {
+          acc[i][j][0] = __builtin_fmaf(p[0], sav[i] * sbc[j].x, acc[i][j][0]);
+          acc[i][j][1] = __builtin_fmaf(p[1], sav[i] * sbc[j].y, acc[i][j][1]);
+          acc[i][j][2] = __builtin_fmaf(p[2], sav[i] * sbc[j].z, acc[i][j][2]);
+          acc[i][j][3] = __builtin_fmaf(p[3], sav[i] * sbc[j].w, acc[i][j][3]);
+        }
+      }
+    }
+    if (more) {
+      FP8BQ_STORE_STAGE(smem + ((kb + 1) & 1) * STAGE);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) sav[i] = nsav[i];
+      if constexpr (SBM == kSbBlock128) {
+        sbb = nsbb;
+      } else {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) sbc[j] = nsbc[j];
+      }
+    }
+    __syncthreads();
+  }
+#undef FP8BQ_LOAD_STAGE
+#undef FP8BQ_STORE_STAGE
+#undef FP8BQ_LOAD_SCALES
+
+  // epilogue
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int64_t m = m0 + wm * WTM + 16 * i + (lane & 15);
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int64_t n = ncol_wave + 16 * j + 4 * (lane >> 4);
+      if (n >= N) continue;
+      if constexpr (OUTF32) {
+        float* c = reinterpret_cast<float*>(d.c) + m * d.ldc + n;
+        *reinterpret_cast<float4*>(c) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      } else {
+        uint16_t* c = reinterpret_cast<uint16_t*>(d.c) + m * d.ldc + n;
+        *reinterpret_cast<uint2*>(c) =
+            make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int SBM, int FA, int FB, int OUTF32>
+static hipError_t launch_variant(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_tn_kernel<BM, BN, WGM, WGN, SBM, FA, FB, OUTF32>), dim3((unsigned)p.grid),
+                     dim3(WGM * WGN * 64), 0, st, d, p.tiles_m, p.tiles_n);
+  return hipGetLastError();
+}
+
+template <int SBM, int FA, int FB, int OUTF32>
+static hipError_t launch_fmt(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
+  return launch_variant<128, 128, 2, 2, SBM, FA, FB, OUTF32>(d, p, st);
+}
+
+template <int SBM, int OUTF32>
+static hipError_t launch_sbm(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
+  if (d.fa == kE4M3 && d.fb == kE4M3) return launch_fmt<SBM, kE4M3, kE4M3, OUTF32>(d, p, st);
+  if (d.fa == kE5M2 && d.fb == kE4M3) return launch_fmt<SBM, kE5M2, kE4M3, OUTF32>(d, p, st);
+  if (d.fa == kE4M3 && d.fb == kE5M2) return launch_fmt<SBM, kE4M3, kE5M2, OUTF32>(d, p, st);
+  return launch_fmt<SBM, kE5M2, kE5M2, OUTF32>(d, p, st);
+}
+
+hipError_t launch_gemm(const GemmDesc& d, const GemmPlan& p, void* ws, hipStream_t st) {
+  (void)ws;
+  if (d.sb_mode == kSbBlock128)
+    return d.out_f32 ? launch_sbm<kSbBlock128, 1>(d, p, st) : launch_sbm<kSbBlock128, 0>(d, p, st);
+  return d.out_f32 ? launch_sbm<kSbColumn, 1>(d, p, st) : launch_sbm<kSbColumn, 0>(d, p, st);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Byte transpose, 128x128 tiles: each thread loads a 4-row x 16-byte patch, transposes 4x4 byte
+// blocks with v_perm_b32, stages dwords (4 source rows of one column) in LDS, and writes 16-byte
+// runs of the destination rows.
+// ---------------------------------------------------------------------------------------------
+constexpr int kTrStride = 33;
+
+__device__ __forceinline__ void transpose4x4(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3, uint32_t (&o)[4]) {
+  // v_perm_b32(hi, lo, sel): byte i of the result is byte sel_i of the 8-byte value {hi, lo}.
+  const uint32_t p01l = __builtin_amdgcn_perm(d1, d0, 0x05010400u);  // d0.b0 d1.b0 d0.b1 d1.b1
+  const uint32_t p01h = __builtin_amdgcn_perm(d1, d0, 0x07030602u);  // d0.b2 d1.b2 d0.b3 d1.b3
+  const uint32_t p23l = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+  const uint32_t p23h = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(p23l, p01l, 0x05040100u);  // d0.b0 d1.b0 d2.b0 d3.b0
+  o[1] = __builtin_amdgcn_perm(p23l, p01l, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(p23h, p01h, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(p23h, p01h, 0x07060302u);
+}
+
+__global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __restrict__ src, int64_t lds,
+                                                           uint8_t* __restrict__ dst, int64_t ldd) {
+  __shared__ uint32_t tileT[128 * kTrStride];
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
+  const int rq = t >> 3, cq = t & 7;
+  uint4 d[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) d[p] = *reinterpret_cast<const uint4*>(src + (r0 + 4 * rq + p) * lds + c0 + 16 * cq);
+  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&d[0]);
+  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&d[1]);
+  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&d[2]);
+  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&d[3]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t o[4];
+    transpose4x4(w0[w], w1[w], w2[w], w3[w], o);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tileT[(16 * cq + 4 * w + b) * kTrStride + rq] = o[b];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int id = t + 256 * pass, k = id >> 3, ch = id & 7;
+    const uint32_t* s4 = tileT + k * kTrStride + 4 * ch;
+    *reinterpret_cast<uint4*>(dst + (c0 + k) * ldd + r0 + 16 * ch) = make_uint4(s4[0], s4[1], s4[2], s4[3]);
+  }
+}
+
+hipError_t launch_transpose_u8(const uint8_t* src, int64_t lds, uint8_t* dst, int64_t ldd, int64_t R, int64_t C,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(transpose_u8_kernel, dim3((unsigned)(C / 128), (unsigned)(R / 128)), dim3(256), 0, st, src, lds,
+                     dst, ldd);
+  return hipGetLastError();
+}
+
+__global__ void zero_fill_kernel(uint8_t* dst, int64_t rows, int64_t row_bytes, int64_t ld_bytes) {
+  const int64_t total = rows * row_bytes;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / row_bytes, c = i - r * row_bytes;
+    dst[r * ld_bytes + c] = 0;
+  }
+}
+
+hipError_t launch_zero_fill(void* dst, int64_t rows, int64_t row_bytes, int64_t ld_bytes, hipStream_t st) {
+  const int64_t total = rows * row_bytes;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (uint8_t*)dst, rows, row_bytes,
+                     ld_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace fp8bq

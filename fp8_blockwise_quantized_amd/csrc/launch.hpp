@@ -1,0 +1,51 @@
+// Host-side kernel launchers (internal).  Arguments are validated by the C-ABI layer before these
+// are called; every size passed here is non-empty.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.hpp"
+
+namespace fp8bq {
+
+hipError_t launch_quant_1x128(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, uint8_t* q,
+                              int64_t ldq, float* s, int64_t lds, hipStream_t st);
+hipError_t launch_quant_128x1(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, uint8_t* qt,
+                              int64_t ldqt, float* st_, int64_t ldst, hipStream_t st);
+hipError_t launch_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
+                                int64_t ldq, float* s, int64_t lds, hipStream_t st);
+
+// One scaled FP8 GEMM in "TN" form: C[m, n] = sum_kb sa(kb, m) * sb(kb, n) * sum_{k in kb} A[m, k] B[n, k],
+// where A [Mr, K] and B [Nc, K] are both contiguous along the contraction.
+//   sa(kb, m) = sa[kb * ldsa + m]
+//   sb(kb, n) = sb[kb * sb_kstride + (n / 128) * sb_nstride]   (SbMode::kBlock128)
+//   sb(kb, n) = sb[kb * sb_kstride + n]                         (SbMode::kColumn)
+struct GemmDesc {
+  const uint8_t* a;
+  int64_t lda;
+  const uint8_t* b;
+  int64_t ldb;
+  const float* sa;
+  int64_t ldsa;
+  const float* sb;
+  int64_t sb_kstride;
+  int64_t sb_nstride;
+  void* c;
+  int64_t ldc;
+  int64_t M, N, K;
+  int fa, fb;    // FP8 format of A and B
+  int out_f32;   // 0: BF16 output, 1: FP32 output
+  int sb_mode;   // SbMode
+};
+
+hipError_t launch_gemm(const GemmDesc& d, const GemmPlan& plan, void* ws, hipStream_t st);
+
+// Byte-matrix transpose: dst[c * ldd + r] = src[r * lds + c] for r < R, c < C (R, C multiples of 128).
+hipError_t launch_transpose_u8(const uint8_t* src, int64_t lds, uint8_t* dst, int64_t ldd, int64_t R, int64_t C,
+                               hipStream_t st);
+
+// Fill n bytes of dst with zeros (used when a GEMM's contraction length is 0).
+hipError_t launch_zero_fill(void* dst, int64_t rows, int64_t row_bytes, int64_t ld_bytes, hipStream_t st);
+
+}  // namespace fp8bq

@@ -1,0 +1,271 @@
+// Blockwise FP8 quantize kernels for gfx950: 1x128 (activations), 128x1 (token axis, transposed
+// output for wgrad) and 128x128 (weights).
+//
+// Rule per group ("用 RTX 5090 花 $7000 训练 2B 大模型：Puro-2B 低成本预训练技术解析", section
+// "核心挑战：Scale Factor 管理", FP8Linear._quantize): amax = max|x|; s = max(RN(amax/fmt_max), 1e-12);
+// q = RNE code of clamp(RN(x/s), +-fmt_max).  Group shapes: activations 1-D groups of 128, weights
+// 128x128 tiles ("Puro-2B: Poor Lab's Qwen2-1.5B Trained on RTX 5090 within $5090", "方法关键点",
+// bullet "FP8 blockwise 混合精度").
+//
+// All three passes are HBM-bound (about 3 bytes moved per element from BF16).  Each reads its input
+// once with 16-byte coalesced loads, keeps the group in registers, reduces amax with DPP row
+// rotations (1x128, 128x128) or through LDS (128x1, whose groups run down columns), and writes codes
+// with 8- or 16-byte stores.  The division x/s uses the exact reciprocal-and-residual form in
+// div_by_scale (3 VALU ops instead of an IEEE divide sequence), which returns the IEEE quotient bit
+// for bit wherever it can change a code.
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp8bq {
+
+// Load 8 consecutive input elements (16 bytes of BF16 or 32 bytes of FP32) as fp32.
+template <typename TIn>
+struct Load8;
+template <>
+struct Load8<uint16_t> {
+  static __device__ __forceinline__ void run(const uint16_t* p, float (&v)[8]) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16lo(w.x); v[1] = bf16hi(w.x);
+    v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
+    v[4] = bf16lo(w.z); v[5] = bf16hi(w.z);
+    v[6] = bf16lo(w.w); v[7] = bf16hi(w.w);
+  }
+};
+template <>
+struct Load8<float> {
+  static __device__ __forceinline__ void run(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *(reinterpret_cast<const float4*>(p) + 1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+// Quantize 8 values with the group's (s, r) into two dwords of codes.
+template <int FMT>
+__device__ __forceinline__ uint2 quant8(const float (&v)[8], float s, float r) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = clamp_fmt<FMT>(div_by_scale(v[i], s, r));
+  return make_uint2(pack4<FMT>(y[0], y[1], y[2], y[3]), pack4<FMT>(y[4], y[5], y[6], y[7]));
+}
+
+// ---------------------------------------------------------------------------------------------
+// 1x128: grid (ceil(R/64), C/128).  A block owns one 128-column group for 64 rows.  16 lanes (one
+// DPP row) hold one group, 8 elements each; the 256 threads cover 16 rows per pass, 4 passes.
+// ---------------------------------------------------------------------------------------------
+constexpr int kQ1Rows = 64;
+
+template <typename TIn, int FMT>
+__global__ __launch_bounds__(256) void quant_1x128_kernel(const TIn* __restrict__ x, int64_t R, int64_t ldx,
+                                                          uint8_t* __restrict__ q, int64_t ldq,
+                                                          float* __restrict__ s, int64_t lds) {
+  const int t = threadIdx.x;
+  const int l16 = t & 15;
+  const int rsub = t >> 4;
+  const int64_t g = blockIdx.y;
+  const int64_t r0 = (int64_t)blockIdx.x * kQ1Rows;
+  const int64_t col = g * kGroup + 8 * l16;
+
+  float v[4][8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int64_t r = r0 + rsub + 16 * p;
+    if (r < R) {
+      Load8<TIn>::run(x + r * ldx + col, v[p]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[p][i] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int64_t r = r0 + rsub + 16 * p;
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
+    const float amax = row16_max(m);
+    const float sc = group_scale<FMT>(amax);
+    const float rc = 1.0f / sc;
+    if (r < R) {
+      const uint2 w = quant8<FMT>(v[p], sc, rc);
+      *reinterpret_cast<uint2*>(q + r * ldq + col) = w;
+      if (l16 == 0) s[g * lds + r] = sc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 128x1: grid (ceil(C/64), R/128).  A block owns rows 128*rb .. +127 and 64 columns.  Thread t
+// holds a 4-row x 8-column patch (rows 4*(t>>3)+0..3, columns 8*(t&7)+0..7).  Column amax goes
+// through LDS; codes are packed 4 rows to a dword, staged transposed in LDS, and written as 16-byte
+// runs along the token axis.
+// ---------------------------------------------------------------------------------------------
+constexpr int kQtCols = 64;
+constexpr int kQtStride = 33;  // dwords per staged column (32 + 1 pad against bank conflicts)
+
+template <typename TIn, int FMT>
+__global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict__ x, int64_t C, int64_t ldx,
+                                                          uint8_t* __restrict__ qt, int64_t ldqt,
+                                                          float* __restrict__ st, int64_t ldst) {
+  __shared__ float red[32][kQtCols + 1];
+  __shared__ float ssc[kQtCols];
+  __shared__ float src[kQtCols];
+  __shared__ uint32_t tileT[kQtCols * kQtStride];
+
+  const int t = threadIdx.x;
+  const int cc = t & 7;
+  const int rg = t >> 3;
+  const int64_t rb = blockIdx.y;
+  const int64_t c0 = (int64_t)blockIdx.x * kQtCols;
+  const int64_t col = c0 + 8 * cc;
+  const bool cvalid = col < C;  // C % 8 == 0, so a chunk is all in or all out
+
+  float v[4][8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int64_t r = rb * kGroup + 4 * rg + p;
+    if (cvalid) {
+      Load8<TIn>::run(x + r * ldx + col, v[p]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[p][i] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float m = __builtin_fabsf(v[0][i]);
+    m = __builtin_fmaxf(m, __builtin_fabsf(v[1][i]));
+    m = __builtin_fmaxf(m, __builtin_fabsf(v[2][i]));
+    m = __builtin_fmaxf(m, __builtin_fabsf(v[3][i]));
+    red[rg][8 * cc + i] = m;
+  }
+  __syncthreads();
+  if (t < kQtCols) {
+    float m = 0.0f;
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) m = __builtin_fmaxf(m, red[k][t]);
+    const float sc = group_scale<FMT>(m);
+    ssc[t] = sc;
+    src[t] = 1.0f / sc;
+    if (c0 + t < C) st[rb * ldst + c0 + t] = sc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = 8 * cc + i;
+    const float sc = ssc[c], rc = src[c];
+    const float y0 = clamp_fmt<FMT>(div_by_scale(v[0][i], sc, rc));
+    const float y1 = clamp_fmt<FMT>(div_by_scale(v[1][i], sc, rc));
+    const float y2 = clamp_fmt<FMT>(div_by_scale(v[2][i], sc, rc));
+    const float y3 = clamp_fmt<FMT>(div_by_scale(v[3][i], sc, rc));
+    tileT[c * kQtStride + rg] = pack4<FMT>(y0, y1, y2, y3);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int c = (t >> 3) + 32 * pass;
+    const int ch = t & 7;
+    if (c0 + c < C) {
+      const uint32_t* src4 = tileT + c * kQtStride + 4 * ch;
+      const uint4 w = make_uint4(src4[0], src4[1], src4[2], src4[3]);
+      *reinterpret_cast<uint4*>(qt + (c0 + c) * ldqt + rb * kGroup + 16 * ch) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 128x128: grid (K/128, N/128), one block per weight tile.  Thread t holds rows (t>>4) + 16*p,
+// p = 0..7, columns 8*(t&15)+0..7 (64 values).  amax: DPP within rows of 16 lanes, readlane across
+// the wave, LDS across the 4 waves.
+// ---------------------------------------------------------------------------------------------
+template <typename TIn, int FMT>
+__global__ __launch_bounds__(256) void quant_128x128_kernel(const TIn* __restrict__ w, int64_t ldw,
+                                                            uint8_t* __restrict__ q, int64_t ldq,
+                                                            float* __restrict__ s, int64_t lds) {
+  __shared__ float wmax[4];
+  const int t = threadIdx.x;
+  const int l16 = t & 15;
+  const int rsub = t >> 4;
+  const int64_t kb = blockIdx.x, nb = blockIdx.y;
+  const int64_t col = kb * kGroup + 8 * l16;
+
+  float v[8][8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) Load8<TIn>::run(w + (nb * kGroup + rsub + 16 * p) * ldw + col, v[p]);
+  float m = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
+  m = wave_max(m);
+  if ((t & 63) == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  const float amax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+  const float sc = group_scale<FMT>(amax);
+  const float rc = 1.0f / sc;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint2 c = quant8<FMT>(v[p], sc, rc);
+    *reinterpret_cast<uint2*>(q + (nb * kGroup + rsub + 16 * p) * ldq + col) = c;
+  }
+  if (t == 0) s[nb * lds + kb] = sc;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host launchers (arguments already validated; sizes non-empty).
+// ---------------------------------------------------------------------------------------------
+template <typename TIn, int FMT>
+static hipError_t launch_1x128_t(const void* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq,
+                                 float* s, int64_t lds, hipStream_t st) {
+  dim3 grid((unsigned)((R + kQ1Rows - 1) / kQ1Rows), (unsigned)(C / kGroup));
+  hipLaunchKernelGGL((quant_1x128_kernel<TIn, FMT>), grid, dim3(256), 0, st, (const TIn*)x, R, ldx, q, ldq, s, lds);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_1x128(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, uint8_t* q,
+                              int64_t ldq, float* s, int64_t lds, hipStream_t st) {
+  if (xt == 0)
+    return fmt == kE4M3 ? launch_1x128_t<uint16_t, kE4M3>(x, R, C, ldx, q, ldq, s, lds, st)
+                        : launch_1x128_t<uint16_t, kE5M2>(x, R, C, ldx, q, ldq, s, lds, st);
+  return fmt == kE4M3 ? launch_1x128_t<float, kE4M3>(x, R, C, ldx, q, ldq, s, lds, st)
+                      : launch_1x128_t<float, kE5M2>(x, R, C, ldx, q, ldq, s, lds, st);
+}
+
+template <typename TIn, int FMT>
+static hipError_t launch_128x1_t(const void* x, int64_t R, int64_t C, int64_t ldx, uint8_t* qt, int64_t ldqt,
+                                 float* st_, int64_t ldst, hipStream_t st) {
+  dim3 grid((unsigned)((C + kQtCols - 1) / kQtCols), (unsigned)(R / kGroup));
+  hipLaunchKernelGGL((quant_128x1_kernel<TIn, FMT>), grid, dim3(256), 0, st, (const TIn*)x, C, ldx, qt, ldqt, st_,
+                     ldst);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_128x1(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, uint8_t* qt,
+                              int64_t ldqt, float* st_, int64_t ldst, hipStream_t st) {
+  if (xt == 0)
+    return fmt == kE4M3 ? launch_128x1_t<uint16_t, kE4M3>(x, R, C, ldx, qt, ldqt, st_, ldst, st)
+                        : launch_128x1_t<uint16_t, kE5M2>(x, R, C, ldx, qt, ldqt, st_, ldst, st);
+  return fmt == kE4M3 ? launch_128x1_t<float, kE4M3>(x, R, C, ldx, qt, ldqt, st_, ldst, st)
+                      : launch_128x1_t<float, kE5M2>(x, R, C, ldx, qt, ldqt, st_, ldst, st);
+}
+
+template <typename TIn, int FMT>
+static hipError_t launch_128x128_t(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, int64_t ldq,
+                                   float* s, int64_t lds, hipStream_t st) {
+  dim3 grid((unsigned)(K / kGroup), (unsigned)(N / kGroup));
+  hipLaunchKernelGGL((quant_128x128_kernel<TIn, FMT>), grid, dim3(256), 0, st, (const TIn*)w, ldw, q, ldq, s, lds);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
+                                int64_t ldq, float* s, int64_t lds, hipStream_t st) {
+  if (wt == 0)
+    return fmt == kE4M3 ? launch_128x128_t<uint16_t, kE4M3>(w, N, K, ldw, q, ldq, s, lds, st)
+                        : launch_128x128_t<uint16_t, kE5M2>(w, N, K, ldw, q, ldq, s, lds, st);
+  return fmt == kE4M3 ? launch_128x128_t<float, kE4M3>(w, N, K, ldw, q, ldq, s, lds, st)
+                      : launch_128x128_t<float, kE5M2>(w, N, K, ldw, q, ldq, s, lds, st);
+}
+
+}  // namespace fp8bq

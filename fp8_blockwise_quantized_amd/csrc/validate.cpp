@@ -1,0 +1,144 @@
+// Argument validation (pure host C++).
+#include "validate.hpp"
+
+namespace fp8bq {
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool fmt_ok(int f) { return f == 0 || f == 1; }
+static int in_esize(int t) { return t == 0 ? 2 : (t == 1 ? 4 : 0); }
+
+int check_mat(const Mat& m, bool align_ld) {
+  if (m.p == nullptr) return kErrNull;
+  if (!aligned16(m.p)) return kErrAlign;
+  if (m.ld < m.cols || m.ld < 1) return kErrLd;
+  if (align_ld && ((m.ld * m.esize) % 16) != 0) return kErrLd;
+  return kOk;
+}
+
+static void extent(const Mat& m, uintptr_t& lo, uintptr_t& hi) {
+  lo = (uintptr_t)m.p;
+  hi = lo + (uintptr_t)(((m.rows - 1) * m.ld + m.cols) * m.esize);
+}
+
+bool overlaps(const Mat& a, const Mat& b) {
+  if (a.rows <= 0 || a.cols <= 0 || b.rows <= 0 || b.cols <= 0) return false;
+  uintptr_t alo, ahi, blo, bhi;
+  extent(a, alo, ahi);
+  extent(b, blo, bhi);
+  return alo < bhi && blo < ahi;
+}
+
+// Common tail of the three quantizers: input X, codes Q, scales S (each a Mat), checked in order.
+static int check_quant(const Mat& x, const Mat& q, const Mat& s, bool s_align) {
+  int st;
+  if (x.p == nullptr || q.p == nullptr || s.p == nullptr) return kErrNull;
+  if ((st = check_mat(x, true)) != kOk) return st;
+  if ((st = check_mat(q, true)) != kOk) return st;
+  if ((st = check_mat(s, s_align)) != kOk) return st;
+  if (overlaps(q, x) || overlaps(s, x) || overlaps(q, s)) return kErrOverlap;
+  return kOk;
+}
+
+int validate_quant_1x128(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, const void* q,
+                         int64_t ldq, const void* s, int64_t lds, bool* empty) {
+  *empty = false;
+  if (in_esize(xt) == 0) return kErrDtype;
+  if (!fmt_ok(fmt)) return kErrFormat;
+  if (R < 0 || C < 0 || C % 128 != 0) return kErrShape;
+  if (R == 0 || C == 0) {
+    *empty = true;
+    return kOk;
+  }
+  return check_quant(Mat{x, R, C, ldx, in_esize(xt)}, Mat{q, R, C, ldq, 1}, Mat{s, C / 128, R, lds, 4}, true);
+}
+
+int validate_quant_128x1(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, const void* qt,
+                         int64_t ldqt, const void* st, int64_t ldst, bool* empty) {
+  *empty = false;
+  if (in_esize(xt) == 0) return kErrDtype;
+  if (!fmt_ok(fmt)) return kErrFormat;
+  if (R < 0 || C < 0 || R % 128 != 0 || C % 8 != 0) return kErrShape;
+  if (R == 0 || C == 0) {
+    *empty = true;
+    return kOk;
+  }
+  return check_quant(Mat{x, R, C, ldx, in_esize(xt)}, Mat{qt, C, R, ldqt, 1}, Mat{st, R / 128, C, ldst, 4}, true);
+}
+
+int validate_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, const void* q,
+                           int64_t ldq, const void* s, int64_t lds, bool* empty) {
+  *empty = false;
+  if (in_esize(wt) == 0) return kErrDtype;
+  if (!fmt_ok(fmt)) return kErrFormat;
+  if (N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return kErrShape;
+  if (N == 0 || K == 0) {
+    *empty = true;
+    return kOk;
+  }
+  return check_quant(Mat{w, N, K, ldw, in_esize(wt)}, Mat{q, N, K, ldq, 1}, Mat{s, N / 128, K / 128, lds, 4},
+                     false);
+}
+
+int validate_gemm(const GemmArgs& g, size_t ws_needed, bool* empty, bool* zero_fill) {
+  *empty = false;
+  *zero_fill = false;
+  if (g.op < 0 || g.op > 2) return kErrShape;
+  if (!fmt_ok(g.fa) || !fmt_ok(g.fb)) return kErrFormat;
+  if (g.out_t != 0 && g.out_t != 1) return kErrDtype;
+  const int64_t M = g.M, N = g.N, K = g.K;
+  if (M < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return kErrShape;
+  if (g.op == 2 && M % 128 != 0) return kErrShape;
+
+  // Operand geometry per op: (A codes, A scales, B codes, B scales, output) as matrices.
+  Mat qa, sa, qb, sb, out;
+  int64_t out_rows, out_cols, contraction;
+  const int oes = g.out_t == 0 ? 2 : 4;
+  if (g.op == 0) {  // fprop: X[M,K] (1x128), W[N,K] (128x128) -> Y[M,N]
+    qa = Mat{g.qa, M, K, g.ldqa, 1};
+    sa = Mat{g.sa, K / 128, M, g.ldsa, 4};
+    qb = Mat{g.qb, N, K, g.ldqb, 1};
+    sb = Mat{g.sb, N / 128, K / 128, g.ldsb, 4};
+    out_rows = M; out_cols = N; contraction = K;
+  } else if (g.op == 1) {  // dgrad: dY[M,N] (1x128), W[N,K] (128x128) -> dX[M,K]
+    qa = Mat{g.qa, M, N, g.ldqa, 1};
+    sa = Mat{g.sa, N / 128, M, g.ldsa, 4};
+    qb = Mat{g.qb, N, K, g.ldqb, 1};
+    sb = Mat{g.sb, N / 128, K / 128, g.ldsb, 4};
+    out_rows = M; out_cols = K; contraction = N;
+  } else {  // wgrad: dY^T[N,M] (128x1), X^T[K,M] (128x1) -> dW[N,K]
+    qa = Mat{g.qa, N, M, g.ldqa, 1};
+    sa = Mat{g.sa, M / 128, N, g.ldsa, 4};
+    qb = Mat{g.qb, K, M, g.ldqb, 1};
+    sb = Mat{g.sb, M / 128, K, g.ldsb, 4};
+    out_rows = N; out_cols = K; contraction = M;
+  }
+  out = Mat{g.out, out_rows, out_cols, g.ldout, oes};
+  if (out_rows == 0 || out_cols == 0) {
+    *empty = true;
+    return kOk;
+  }
+  int st;
+  if (g.out == nullptr) return kErrNull;
+  if ((st = check_mat(out, true)) != kOk) return st;
+  if (contraction == 0) {
+    *zero_fill = true;
+    return kOk;
+  }
+  if (g.qa == nullptr || g.sa == nullptr || g.qb == nullptr || g.sb == nullptr) return kErrNull;
+  if ((st = check_mat(qa, true)) != kOk) return st;
+  if ((st = check_mat(sa, true)) != kOk) return st;
+  if ((st = check_mat(qb, true)) != kOk) return st;
+  // weight scales are read one value at a time; the wgrad column scales as 16-byte vectors
+  if ((st = check_mat(sb, g.op == 2)) != kOk) return st;
+  if (overlaps(out, qa) || overlaps(out, sa) || overlaps(out, qb) || overlaps(out, sb)) return kErrOverlap;
+  if (ws_needed > 0) {
+    if (g.ws == nullptr || g.ws_bytes < ws_needed) return kErrWorkspace;
+    if (!aligned16(g.ws)) return kErrAlign;
+    Mat wsm{g.ws, 1, (int64_t)ws_needed, (int64_t)ws_needed, 1};
+    if (overlaps(wsm, out) || overlaps(wsm, qa) || overlaps(wsm, sa) || overlaps(wsm, qb) || overlaps(wsm, sb))
+      return kErrOverlap;
+  }
+  return kOk;
+}
+
+}  // namespace fp8bq

@@ -1,0 +1,58 @@
+// Argument validation for the C-ABI entry points (pure host C++, no HIP calls), so every error path
+// can be exercised on a machine without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8bq {
+
+// Status codes mirror fp8bq_status in include/fp8bq.h.
+enum Status : int {
+  kOk = 0,
+  kErrNull = 1,
+  kErrShape = 2,
+  kErrLd = 3,
+  kErrAlign = 4,
+  kErrDtype = 5,
+  kErrFormat = 6,
+  kErrWorkspace = 7,
+  kErrDevice = 8,
+  kErrLaunch = 9,
+  kErrOverlap = 10,
+};
+
+// A row-major matrix view for validation: base pointer, rows, columns, leading dimension (elements),
+// element size (bytes).
+struct Mat {
+  const void* p;
+  int64_t rows, cols, ld;
+  int esize;
+};
+
+// Checks pointer non-null, 16-byte alignment, ld >= cols and ld*esize % 16 == 0 (if align_ld).
+int check_mat(const Mat& m, bool align_ld);
+// Byte ranges of two non-empty matrices intersect.
+bool overlaps(const Mat& a, const Mat& b);
+
+int validate_quant_1x128(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, const void* q,
+                         int64_t ldq, const void* s, int64_t lds, bool* empty);
+int validate_quant_128x1(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, const void* qt,
+                         int64_t ldqt, const void* st, int64_t ldst, bool* empty);
+int validate_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, const void* q,
+                           int64_t ldq, const void* s, int64_t lds, bool* empty);
+
+// The three GEMMs share one validator: op selects the operand shapes.
+struct GemmArgs {
+  int op;
+  int64_t M, N, K;
+  const void* qa; int64_t ldqa; const void* sa; int64_t ldsa; int fa;
+  const void* qb; int64_t ldqb; const void* sb; int64_t ldsb; int fb;
+  const void* out; int out_t; int64_t ldout;
+  const void* ws; size_t ws_bytes;
+};
+// *empty: the output has no elements.  *zero_fill: the output is non-empty but the contraction is
+// empty, so the result is all zeros.  ws_needed: bytes the plan needs.
+int validate_gemm(const GemmArgs& g, size_t ws_needed, bool* empty, bool* zero_fill);
+
+}  // namespace fp8bq

@@ -1,0 +1,198 @@
+/*
+ * fp8bq.h -- FP8 blockwise-quantized linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of the Puro-2B FP8 recipe:
+ *   - "用 RTX 5090 花 $7000 训练 2B 大模型：Puro-2B 低成本预训练技术解析" (hankli.space),
+ *     section "Blackwell 的 FP8 Tensor Core" (the E4M3 / E5M2 formats, maxima 448 and 57344)
+ *     and section "核心挑战：Scale Factor 管理" (FP8Linear: scale = amax / fmt_max with a
+ *     1e-12 floor, divide, clamp to +-fmt_max, cast; dequantize = code value * scale);
+ *   - "小团队也能预训练！普罗2B：RTX5090训练成本不到5090美元" (66bd.net), paragraph
+ *     "FP8发挥RTX 5090的低精度效率优势" (DeepSeek-V3-style fine-grained blocks, linear GEMMs in
+ *     FP8, sensitive state in BF16/FP32);
+ *   - "Puro-2B: Poor Lab's Qwen2-1.5B Trained on RTX 5090 within $5090" (AI Papers Daily),
+ *     section "方法关键点", bullet "FP8 blockwise 混合精度" (E4M3 linear GEMMs, activations in
+ *     groups of 128, weights in 128x128 blocks).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller.  The library never frees,
+ *   retains or allocates caller memory; callers provide any workspace.
+ * - Matrices are row-major.  Sizes and leading dimensions (ld*) are in ELEMENTS.
+ * - Each call validates all arguments first; on any error it returns a nonzero fp8bq_status
+ *   and enqueues nothing.  On success it enqueues its kernels on `stream` (a hipStream_t;
+ *   NULL means the default stream) and returns FP8BQ_OK without synchronizing.  Faults on the
+ *   device surface at the caller's next synchronization, as usual for HIP.
+ * - Outputs are fully overwritten (no accumulation into existing contents).
+ * - Calls are thread-safe and re-entrant; there is no mutable global state besides a per-device
+ *   cache of the device's architecture check.  Calls that write overlapping outputs on the same
+ *   device must be ordered by the caller (same stream or events).
+ * - Alignment: every tensor pointer must be 16-byte aligned, and each leading dimension times
+ *   the element size must be a multiple of 16 bytes (bf16: ld % 8 == 0; fp32: ld % 4 == 0;
+ *   codes: ld % 16 == 0).  Scale arrays follow the same rule (ld % 4 == 0).
+ * - Inputs must be finite; NaN or Inf inputs give unspecified codes.
+ * - A dimension of size 0 makes the call a successful no-op.
+ *
+ * Quantization rule (per group of values, identical for all three quantizers):
+ *   amax = max |x|;  s = max(fp32(amax / fmt_max), fp32(1e-12));
+ *   q = round-to-nearest-even FP8 code of clamp(fp32(x / s), -fmt_max, fmt_max)
+ * where both divisions are IEEE fp32 divisions rounded to nearest even and the sign of a
+ * value that rounds to zero is kept.  Codes and scales are a deterministic function of the
+ * input: they are bit-identical from call to call.  Dequantized value = decode(q) * s.
+ */
+#ifndef FP8BQ_H_
+#define FP8BQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8BQ_OK = 0,
+  FP8BQ_ERR_NULL = 1,      /* a required pointer is NULL */
+  FP8BQ_ERR_SHAPE = 2,     /* negative size, or a grouped/contracted size not a multiple of 128 */
+  FP8BQ_ERR_LD = 3,        /* leading dimension smaller than the row length, or misaligned */
+  FP8BQ_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+  FP8BQ_ERR_DTYPE = 5,     /* unknown input or output element type */
+  FP8BQ_ERR_FORMAT = 6,    /* unknown FP8 format */
+  FP8BQ_ERR_WORKSPACE = 7, /* workspace NULL or smaller than fp8bq_gemm_workspace_size() */
+  FP8BQ_ERR_DEVICE = 8,    /* no current HIP device, or it is not gfx950 */
+  FP8BQ_ERR_LAUNCH = 9,    /* the kernel launch itself failed */
+  FP8BQ_ERR_OVERLAP = 10   /* an output overlaps an input the same call reads */
+} fp8bq_status;
+
+/* OCP FP8 formats: E4M3 = float8_e4m3fn (bias 7, no Inf, max 448);
+ * E5M2 = float8_e5m2 (bias 15, IEEE-like Inf/NaN, max 57344). */
+typedef enum { FP8BQ_E4M3 = 0, FP8BQ_E5M2 = 1 } fp8bq_fp8;
+
+/* Element type of a high-precision input. */
+typedef enum { FP8BQ_IN_BF16 = 0, FP8BQ_IN_F32 = 1 } fp8bq_in;
+
+/* Element type of a GEMM output: BF16 (round to nearest even from the FP32 accumulator), or
+ * FP32 (the accumulator itself). */
+typedef enum { FP8BQ_OUT_BF16 = 0, FP8BQ_OUT_F32 = 1 } fp8bq_out;
+
+/* GEMM selector for fp8bq_gemm_workspace_size. */
+typedef enum { FP8BQ_OP_FPROP = 0, FP8BQ_OP_DGRAD = 1, FP8BQ_OP_WGRAD = 2 } fp8bq_op;
+
+/*
+ * Activation quantization, one scale per 1x128 group (128 consecutive elements of a row).
+ * Defining passages: the quantize rule of FP8Linear (hankli.space, "核心挑战：Scale Factor 管理");
+ * the 1-D groups of 128 for activations (AI Papers Daily, "FP8 blockwise 混合精度").
+ *
+ *   x  [R, C]  input, element type xt, row stride ldx (>= C).  C % 128 == 0; R >= 0 is free.
+ *   q  [R, C]  output codes (uint8), row stride ldq (>= C).
+ *   s  [C/128][R] output scales (fp32), group-major: the scale of row r, group g is s[g*lds + r]
+ *              (lds >= R).  This layout makes the scales of one 128-wide contraction block
+ *              contiguous over rows, which is how the GEMMs read them.
+ * Used for X before fprop and for dY before dgrad.
+ */
+int fp8bq_quantize_act_1x128(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx,
+                             fp8bq_fp8 fmt, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             void* stream);
+
+/*
+ * Activation quantization along the token axis, one scale per 128x1 group (128 consecutive
+ * ROWS of one column), quantized from the original x (not from 1x128 codes), with transposed
+ * outputs so that the token axis is contiguous.  This is the same 1-D group of 128 laid along
+ * the axis wgrad contracts over (fine-grained blocks after DeepSeek-V3: 66bd.net,
+ * "FP8发挥RTX 5090的低精度效率优势"; rule as above).
+ *
+ *   x  [R, C]  input, element type xt, row stride ldx (>= C).  R % 128 == 0; C % 8 == 0.
+ *   qt [C, R]  output codes transposed: qt[c*ldqt + r] is the code of x[r, c] (ldqt >= R).
+ *   st [R/128][C] output scales: the scale of rows 128*rb .. 128*rb+127 of column c is
+ *              st[rb*ldst + c] (ldst >= C).
+ * Used for X and dY before wgrad.
+ */
+int fp8bq_quantize_act_128x1(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx,
+                             fp8bq_fp8 fmt, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst,
+                             void* stream);
+
+/*
+ * Weight quantization, one scale per aligned 128x128 tile.
+ * Defining passages: FP8Linear's rule (hankli.space, "核心挑战：Scale Factor 管理"); 2-D
+ * 128x128 blocks for weights (AI Papers Daily, "FP8 blockwise 混合精度").
+ *
+ *   w  [N, K]  input, element type wt, row stride ldw (>= K).  N % 128 == 0, K % 128 == 0.
+ *   q  [N, K]  output codes, row stride ldq (>= K).
+ *   s  [N/128][K/128] output scales: tile (nb, kb) has scale s[nb*lds + kb] (lds >= K/128).
+ * The same codes and scales serve fprop (W) and dgrad (W read along its rows).
+ */
+int fp8bq_quantize_weight_128x128(const void* w, fp8bq_in wt, int64_t N, int64_t K, int64_t ldw,
+                                  fp8bq_fp8 fmt, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                  void* stream);
+
+/*
+ * Forward GEMM  Y[M, N] = X[M, K] . W[N, K]^T  on FP8 operands with per-block scales,
+ * FP32 accumulation and BF16 (or FP32) output:
+ *   Y[m, n] = sum_kb sx(m, kb) * sw(n/128, kb) * sum_{k in kb} dec(qx[m, k]) * dec(qw[n, k]).
+ * Defining passages: linear-layer GEMMs in FP8 with high-precision accumulation and state
+ * (66bd.net, "FP8发挥RTX 5090的低精度效率优势"; AI Papers Daily, "FP8 blockwise 混合精度");
+ * dequantize-then-contract as in FP8Linear.forward (hankli.space).
+ *
+ *   qx/sx  from fp8bq_quantize_act_1x128(X): qx [M, K] (ldqx), sx [K/128][M] (ldsx >= M).
+ *   qw/sw  from fp8bq_quantize_weight_128x128(W): qw [N, K] (ldqw), sw [N/128][K/128] (ldsw).
+ *   fx/fw  the FP8 format of each operand (any combination of E4M3 / E5M2).
+ *   y      [M, N] output of type yt, row stride ldy (>= N).
+ *   M >= 0 is free; N % 128 == 0; K % 128 == 0.
+ *   ws/ws_bytes  device workspace of at least fp8bq_gemm_workspace_size(FP8BQ_OP_FPROP, M, N, K)
+ *          bytes (may be NULL when that size is 0).  Its contents are scratch.
+ */
+int fp8bq_gemm_fprop(int64_t M, int64_t N, int64_t K,
+                     const uint8_t* qx, int64_t ldqx, const float* sx, int64_t ldsx, fp8bq_fp8 fx,
+                     const uint8_t* qw, int64_t ldqw, const float* sw, int64_t ldsw, fp8bq_fp8 fw,
+                     void* y, fp8bq_out yt, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Data-gradient GEMM  dX[M, K] = dY[M, N] . W[N, K]  (contraction over the N output features):
+ *   dX[m, k] = sum_nb sdy(m, nb) * sw(nb, k/128) * sum_{n in nb} dec(qdy[m, n]) * dec(qw[n, k]).
+ * Defining passages: as fprop (all linear GEMMs of the layer run in FP8); gradients may use
+ * E5M2 (hankli.space, "Blackwell 的 FP8 Tensor Core").
+ *
+ *   qdy/sdy  from fp8bq_quantize_act_1x128(dY): qdy [M, N] (ldqdy), sdy [N/128][M] (ldsdy >= M).
+ *   qw/sw    the weight's codes and scales exactly as produced for fprop.
+ *   dx       [M, K] output of type dxt, row stride lddx (>= K).
+ *   M >= 0 is free; N % 128 == 0; K % 128 == 0.
+ *   ws       at least fp8bq_gemm_workspace_size(FP8BQ_OP_DGRAD, M, N, K) bytes (holds W's codes
+ *            transposed to [K, N] for the duration of the call).
+ */
+int fp8bq_gemm_dgrad(int64_t M, int64_t N, int64_t K,
+                     const uint8_t* qdy, int64_t ldqdy, const float* sdy, int64_t ldsdy, fp8bq_fp8 fdy,
+                     const uint8_t* qw, int64_t ldqw, const float* sw, int64_t ldsw, fp8bq_fp8 fw,
+                     void* dx, fp8bq_out dxt, int64_t lddx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weight-gradient GEMM  dW[N, K] = dY[M, N]^T . X[M, K]  (contraction over the M tokens):
+ *   dW[n, k] = sum_mb sdy(mb, n) * sx(mb, k) * sum_{m in mb} dec(qdy[m, n]) * dec(qx[m, k]).
+ * Defining passages: as fprop; both operands carry 128x1 (token-axis) scales, an outer product
+ * per 128-token block.
+ *
+ *   qdyt/sdyt  from fp8bq_quantize_act_128x1(dY): qdyt [N, M] (ldqdyt >= M), sdyt [M/128][N].
+ *   qxt/sxt    from fp8bq_quantize_act_128x1(X):  qxt [K, M] (ldqxt >= M),  sxt [M/128][K].
+ *   dw         [N, K] output of type dwt, row stride lddw (>= K).
+ *   M % 128 == 0; N % 128 == 0; K % 128 == 0.
+ *   ws         at least fp8bq_gemm_workspace_size(FP8BQ_OP_WGRAD, M, N, K) bytes (FP32 partial
+ *              sums when the contraction is split across workgroups).
+ */
+int fp8bq_gemm_wgrad(int64_t M, int64_t N, int64_t K,
+                     const uint8_t* qdyt, int64_t ldqdyt, const float* sdyt, int64_t ldsdyt, fp8bq_fp8 fdy,
+                     const uint8_t* qxt, int64_t ldqxt, const float* sxt, int64_t ldsxt, fp8bq_fp8 fx,
+                     void* dw, fp8bq_out dwt, int64_t lddw, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes the given GEMM needs at these sizes on the current device (0 if none).
+ * Returns 0 for invalid arguments too; the GEMM call itself reports those. */
+size_t fp8bq_gemm_workspace_size(fp8bq_op op, int64_t M, int64_t N, int64_t K);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fp8bq_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int fp8bq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BQ_H_ */

@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/fp8bq.h
+declares, and rejects bad arguments with the documented status before touching the device.
+
+Pointers passed here are fake (16-byte aligned integers); every call is expected to return during
+argument validation, or with FP8BQ_ERR_DEVICE on a machine without a gfx950 GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import fp8_blockwise_quantized_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bq.h")
+
+OK, NULL, SHAPE, LD, ALIGN, DTYPE, FORMAT, WORKSPACE, DEVICE, LAUNCH, OVERLAP = range(11)
+HAVE_GPU = torch.cuda.is_available()
+
+P = lambda i: ctypes.c_void_p(0x100000 * (i + 1))  # disjoint, 16-byte aligned fake buffers
+NUL = ctypes.c_void_p(0)
+S0 = ctypes.c_void_p(0)  # stream
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8bq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = fq.lib()
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert fq.lib().fp8bq_version() >= 100
+    for st in range(11):
+        s = fq.status_string(st)
+        assert s.startswith("FP8BQ_")
+    assert fq.status_string(4242) == "FP8BQ_ERR_UNKNOWN"
+
+
+def q1x128(x=P(0), xt=0, R=256, C=256, ldx=256, fmt=0, q=P(1), ldq=256, s=P(2), lds=256):
+    return fq.lib().fp8bq_quantize_act_1x128(x, xt, R, C, ldx, fmt, q, ldq, s, lds, S0)
+
+
+def q128x1(x=P(0), xt=0, R=256, C=64, ldx=64, fmt=0, qt=P(1), ldqt=256, st=P(2), ldst=64):
+    return fq.lib().fp8bq_quantize_act_128x1(x, xt, R, C, ldx, fmt, qt, ldqt, st, ldst, S0)
+
+
+def qw(w=P(0), wt=0, N=256, K=256, ldw=256, fmt=0, q=P(1), ldq=256, s=P(2), lds=2):
+    return fq.lib().fp8bq_quantize_weight_128x128(w, wt, N, K, ldw, fmt, q, ldq, s, lds, S0)
+
+
+def valid_status():
+    return DEVICE if not HAVE_GPU else OK
+
+
+@pytest.mark.skipif(HAVE_GPU, reason="checks the no-device path")
+def test_valid_arguments_reach_the_device_check():
+    assert q1x128() == DEVICE
+    assert q128x1() == DEVICE
+    assert qw() == DEVICE
+
+
+def test_quant_1x128_validation():
+    assert q1x128(xt=7) == DTYPE
+    assert q1x128(fmt=2) == FORMAT
+    assert q1x128(C=200, ldx=200, ldq=208) == SHAPE
+    assert q1x128(R=-1) == SHAPE
+    assert q1x128(R=0, x=NUL, q=NUL, s=NUL) == OK  # empty: no-op
+    assert q1x128(x=NUL) == NULL
+    assert q1x128(s=NUL) == NULL
+    assert q1x128(x=ctypes.c_void_p(0x100008)) == ALIGN
+    assert q1x128(ldx=128) == LD
+    assert q1x128(ldx=260) == LD  # 520 bytes, not a multiple of 16
+    assert q1x128(ldq=264) == LD
+    assert q1x128(lds=255) == LD
+    assert q1x128(lds=258) == LD  # scales: ld % 4
+    assert q1x128(q=P(0)) == OVERLAP
+
+
+def test_quant_128x1_validation():
+    assert q128x1(R=200) == SHAPE
+    assert q128x1(C=12, ldx=16, ldst=16) == SHAPE  # C % 8
+    assert q128x1(ldqt=128) == LD
+    assert q128x1(ldst=60) == LD
+    assert q128x1(C=0) == OK
+    assert q128x1(st=P(0)) == OVERLAP
+
+
+def test_quant_weight_validation():
+    assert qw(N=200) == SHAPE
+    assert qw(K=100, ldw=112, ldq=112) == SHAPE
+    assert qw(lds=1) == LD
+    assert qw(lds=3) in (DEVICE, OK)  # weight scales need no ld alignment
+    assert qw(wt=1, ldw=254) == LD
+
+
+def gemm(fn, M=256, N=256, K=256, qa=P(0), ldqa=256, sa=P(1), ldsa=256, fa=0, qb=P(2), ldqb=256, sb=P(3), ldsb=2,
+         fb=0, out=P(4), out_t=0, ldout=256, ws=P(5), ws_bytes=1 << 20):
+    return getattr(fq.lib(), fn)(M, N, K, qa, ldqa, sa, ldsa, fa, qb, ldqb, sb, ldsb, fb, out, out_t, ldout, ws,
+                                 ws_bytes, S0)
+
+
+def test_gemm_validation():
+    for fn in ("fp8bq_gemm_fprop", "fp8bq_gemm_dgrad"):
+        assert gemm(fn) == valid_status()
+        assert gemm(fn, K=200) == SHAPE
+        assert gemm(fn, N=200) == SHAPE
+        assert gemm(fn, M=100, ldsa=100) == valid_status()  # ragged token count is allowed
+        assert gemm(fn, fa=3) == FORMAT
+        assert gemm(fn, out_t=5) == DTYPE
+        assert gemm(fn, qa=NUL) == NULL
+        assert gemm(fn, out=NUL) == NULL
+        assert gemm(fn, ldout=100) == LD
+        assert gemm(fn, ldsa=250) == LD
+        assert gemm(fn, out=P(0)) == OVERLAP
+        assert gemm(fn, M=0, qa=NUL, out=NUL) == OK
+    w = "fp8bq_gemm_wgrad"
+    assert gemm(w, ldsb=256) == valid_status()
+    assert gemm(w, M=200, ldqa=208, ldqb=208, ldsb=256) == SHAPE  # contraction must be a multiple of 128
+    assert gemm(w, ldsb=2) == LD  # column scales are read as vectors
+    # dgrad needs a workspace for the transposed weight codes
+    need = fq.fp8bq_gemm_workspace_size(fq.OP_DGRAD, 256, 256, 256)
+    assert need >= 256 * 256
+    assert gemm("fp8bq_gemm_dgrad", ws=NUL, ws_bytes=0) == WORKSPACE
+    assert gemm("fp8bq_gemm_dgrad", ws_bytes=need - 1) == WORKSPACE
+    assert gemm("fp8bq_gemm_dgrad", ws=ctypes.c_void_p(0x600008)) == ALIGN
+
+
+def test_workspace_sizes():
+    assert fq.fp8bq_gemm_workspace_size(fq.OP_FPROP, 8192, 8192, 2048) >= 0
+    assert fq.fp8bq_gemm_workspace_size(fq.OP_DGRAD, 16384, 11264, 2048) >= 11264 * 2048
+    assert fq.fp8bq_gemm_workspace_size(7, 1, 1, 1) == 0
+    assert fq.fp8bq_gemm_workspace_size(fq.OP_WGRAD, -1, 1, 1) == 0
+
+
+def test_zero_contraction_is_valid():
+    # K == 0 makes Y all zeros: only the output must be valid
+    assert gemm("fp8bq_gemm_fprop", K=0, qa=NUL, sa=NUL, qb=NUL, sb=NUL) == valid_status()

@@ -1,0 +1,253 @@
+"""GPU parity of the three quantize kernels against the CPU oracle: codes and FP32 scales must be
+bit-identical, compared in logical (row, group) coordinates.
+
+Small cases span several tiles and ragged tails; the full-size workloads are compared in full where
+the oracle is quick (the 8192x2048 activation and weight), otherwise on sampled rows (1x128 groups
+are independent per row) or sampled columns (128x1 groups are independent per column).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_blockwise_quantized_amd as fq
+import oracle
+import synth
+from parity import FP, f32_bits, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+FMTS = [oracle.E4M3, oracle.E5M2]
+
+
+def gpu_1x128(x, fmt):
+    q, s = fq.quantize_act_1x128(x.to(DEV), FP[fmt])
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy().T  # s -> logical [R, C/128]
+
+
+def gpu_128x1(x, fmt):
+    qt, st = fq.quantize_act_128x1(x.to(DEV), FP[fmt])
+    torch.cuda.synchronize()
+    return qt.cpu().numpy().T, st.cpu().numpy()  # codes back in x's orientation
+
+
+def gpu_w(w, fmt):
+    q, s = fq.quantize_weight_128x128(w.to(DEV), FP[fmt])
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def same(got, exp, what):
+    qg, sg = got
+    qe, se = exp
+    assert qg.shape == qe.shape and sg.shape == se.shape, what
+    bad = np.argwhere(qg != qe)
+    assert bad.size == 0, f"{what}: {len(bad)} code mismatches, first at {bad[:3].tolist()}"
+    sb = np.argwhere(f32_bits(sg) != f32_bits(se))
+    assert sb.size == 0, f"{what}: {len(sb)} scale mismatches, first at {sb[:3].tolist()}"
+
+
+# ------------------------------------------------------------------------------------------
+# the hardware FP8 conversion, driven through the 1x128 quantizer with scale exactly 1
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encoder_every_decision_point(fmt):
+    """Each row holds fmt_max (so s = 1 and y = x exactly) and 127 probe values; probes cover every
+    fp32 exponent up to the maximum x every top-11 mantissa pattern x 4 low-bit patterns, both
+    signs, plus every midpoint between adjacent codes and its two neighbours."""
+    m = np.float32(oracle.fmt_max(fmt))
+    emax = 127 + int(np.floor(np.log2(float(m))))
+    exps = np.arange(0, emax + 1, dtype=np.uint32)
+    top = np.arange(1 << 11, dtype=np.uint32) << np.uint32(12)
+    low = np.array([0, 1, 0x7FF, 0x800], dtype=np.uint32)
+    bits = ((exps[:, None, None] << np.uint32(23)) | top[None, :, None] | low[None, None, :]).reshape(-1)
+    y = bits.view(np.float32)
+    y = y[np.abs(y) <= m]
+    tab = oracle.decode_table(fmt)
+    n = int(np.isfinite(tab[:128]).sum())
+    mids = np.array([0.5 * (tab[c] + tab[c + 1]) for c in range(n - 1)], np.float32)
+    extra = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf))])
+    y = np.concatenate([y, -y, extra, -extra, np.array([0.0, -0.0], np.float32)])
+    rows = (y.size + 126) // 127
+    pad = np.zeros(rows * 127, np.float32)
+    pad[:y.size] = y
+    x = np.empty((rows, 128), np.float32)
+    x[:, 0] = m
+    x[:, 1:] = pad.reshape(rows, 127)
+    say(f"encoder sweep {fmt}: {x.size} values")
+    qg, sg = gpu_1x128(torch.from_numpy(x), fmt)
+    assert np.all(sg == 1.0)
+    exp = oracle.encode(x, fmt)
+    bad = np.argwhere(qg != exp)
+    assert bad.size == 0, (bad[:3], x[tuple(bad[0])], qg[tuple(bad[0])], exp[tuple(bad[0])])
+
+
+# ------------------------------------------------------------------------------------------
+# tiny workload (FP32 inputs)
+# ------------------------------------------------------------------------------------------
+
+def test_tiny_workload_all_quantizers():
+    c = synth.config1()
+    A, W, dY = c["A"], c["W"], c["dY"]
+    same(gpu_1x128(A, oracle.E4M3), oracle.quant_act_1x128(A.numpy(), oracle.E4M3), "A 1x128")
+    same(gpu_w(W, oracle.E4M3), oracle.quant_weight_128x128(W.numpy(), oracle.E4M3), "W 128x128")
+    for fmt in FMTS:
+        same(gpu_1x128(dY, fmt), oracle.quant_act_1x128(dY.numpy(), fmt), f"dY 1x128 {fmt}")
+        same(gpu_128x1(dY, fmt), oracle.quant_act_128x1(dY.numpy(), fmt), f"dY 128x1 {fmt}")
+        same(gpu_128x1(A, fmt), oracle.quant_act_128x1(A.numpy(), fmt), f"A 128x1 {fmt}")
+
+
+# ------------------------------------------------------------------------------------------
+# ragged and strided shapes
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("R", [1, 5, 63, 64, 65, 200, 1000])
+def test_1x128_ragged_rows(fmt, R):
+    x = synth.random_bf16((R, 384), seed=100 + R, outliers=True)
+    same(gpu_1x128(x, fmt), oracle.quant_act_1x128(x.float().numpy(), fmt), f"1x128 R={R}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(128, 8), (256, 72), (384, 200), (128, 1000), (640, 64)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_128x1_shapes(fmt, shape, dt):
+    x = synth.random_bf16(shape, seed=200 + shape[1], outliers=True)
+    if dt == "f32":
+        x = synth.random_f32(shape, seed=300 + shape[1])
+    same(gpu_128x1(x, fmt), oracle.quant_act_128x1(x.float().numpy(), fmt), f"128x1 {shape} {dt}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(128, 128), (384, 256), (256, 640)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_weight_shapes(fmt, shape, dt):
+    w = synth.random_bf16(shape, seed=400 + shape[1], std=0.02)
+    if dt == "f32":
+        w = synth.random_f32(shape, seed=500 + shape[1], std=0.02)
+    same(gpu_w(w, fmt), oracle.quant_weight_128x128(w.float().numpy(), fmt), f"weight {shape} {dt}")
+
+
+def test_strided_views():
+    big = synth.random_bf16((300, 512), seed=7, outliers=True).to(DEV)
+    x = big[:, 64:448]  # R=300, C=384, ldx=512
+    q = torch.zeros((300, 400), dtype=torch.uint8, device=DEV)[:, :384]
+    s = torch.zeros((3, 304 + 8), dtype=torch.float32, device=DEV)[:, :300]
+    fq.fp8bq_quantize_act_1x128(x, fq.E4M3, q, s)
+    torch.cuda.synchronize()
+    same((q.cpu().numpy(), s.cpu().numpy().T), oracle.quant_act_1x128(x.float().cpu().numpy(), oracle.E4M3),
+         "strided 1x128")
+    x2 = big[:256, 8:200]  # R=256, C=192
+    qt = torch.zeros((192, 272), dtype=torch.uint8, device=DEV)[:, :256]
+    st = torch.zeros((2, 200), dtype=torch.float32, device=DEV)[:, :192]
+    fq.fp8bq_quantize_act_128x1(x2, fq.E5M2, qt, st)
+    torch.cuda.synchronize()
+    same((qt.cpu().numpy().T, st.cpu().numpy()), oracle.quant_act_128x1(x2.float().cpu().numpy(), oracle.E5M2),
+         "strided 128x1")
+    w = big[:256, 128:384]
+    qw = torch.zeros((256, 272), dtype=torch.uint8, device=DEV)[:, :256]
+    sw = torch.zeros((2, 3), dtype=torch.float32, device=DEV)[:, :2]
+    fq.fp8bq_quantize_weight_128x128(w, fq.E4M3, qw, sw)
+    torch.cuda.synchronize()
+    same((qw.cpu().numpy(), sw.cpu().numpy()), oracle.quant_weight_128x128(w.float().cpu().numpy(), oracle.E4M3),
+         "strided weight")
+
+
+def _edge_matrix():
+    """256x256 BF16 with degenerate groups: zeros, negative zeros, floor-scale groups, BF16
+    subnormals, the BF16 maximum, single spikes, exact powers of two and ties after scaling."""
+    x = synth.random_bf16((256, 256), seed=77).float().numpy()
+    x[0, :128] = 0.0
+    x[1, :128] = -0.0
+    x[2, :128] = np.float32(1e-13)
+    x[3, :128] = np.float32(2.0 ** -130)  # BF16 subnormal
+    x[4, :128] = np.float32(3.3895313892515355e38)  # BF16 max
+    x[4, 5] = -x[4, 5]
+    x[5, :128] = 0.0
+    x[5, 77] = -5.0
+    x[6, :128] = np.float32(448.0) * np.float32(2.0) ** np.arange(-64, 64, dtype=np.float32) / np.float32(2 ** 20)
+    x[7, :128] = np.float32(896.0)
+    x[7, 1:128] = np.float32(3 * 2 ** -9)  # 3*2^-10 after s = 2: E4M3 tie -> even
+    x[8:, 128:] *= np.float32(1e-30)
+    x[:128, 0] = 0.0  # a zero 128x1 group in column 0
+    x[128:, 1] = -0.0
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_edge_values(fmt):
+    x = _edge_matrix()
+    xf = x.float().numpy()
+    same(gpu_1x128(x, fmt), oracle.quant_act_1x128(xf, fmt), "edge 1x128")
+    same(gpu_128x1(x, fmt), oracle.quant_act_128x1(xf, fmt), "edge 128x1")
+    same(gpu_w(x, fmt), oracle.quant_weight_128x128(xf, fmt), "edge 128x128")
+
+
+def test_deterministic():
+    x = synth.random_bf16((1024, 2048), seed=9, outliers=True).to(DEV)
+    a = fq.quantize_act_1x128(x)
+    b = fq.quantize_act_1x128(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------------------------------
+# full-size workloads
+# ------------------------------------------------------------------------------------------
+
+def test_single_linear_full():
+    c = synth.config2()
+    say("8192x2048 activation and weight, full comparison")
+    same(gpu_1x128(c["X"], oracle.E4M3), oracle.quant_act_1x128(c["X"].float().numpy(), oracle.E4M3), "X 1x128")
+    same(gpu_w(c["W"], oracle.E4M3), oracle.quant_weight_128x128(c["W"].float().numpy(), oracle.E4M3), "W")
+
+
+def _sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.choice(n, size=min(k, n), replace=False))
+    idx[0], idx[-1] = 0, n - 1
+    return np.unique(idx)
+
+
+def _check_act_sampled(x, fmt, what, seed):
+    """1x128 on sampled rows, 128x1 on sampled columns, of the full GPU result."""
+    R, C = x.shape
+    rows = _sample(R, 256, seed)
+    cols = _sample(C, 64, seed + 1)
+    xd = x.to(DEV)
+    q, s = fq.quantize_act_1x128(xd, FP[fmt])
+    qt, st = fq.quantize_act_128x1(xd, FP[fmt])
+    torch.cuda.synchronize()
+    xs = x[rows].float().numpy()
+    same((q.cpu().numpy()[rows], s.cpu().numpy().T[rows]), oracle.quant_act_1x128(xs, fmt), what + " 1x128")
+    xc = np.ascontiguousarray(x[:, cols].float().numpy())
+    same((qt.cpu().numpy()[cols].T, st.cpu().numpy()[:, cols]), oracle.quant_act_128x1(xc, fmt), what + " 128x1")
+
+
+@pytest.mark.parametrize("name", [n for n, _, _ in synth.DECODER_LINEARS])
+def test_decoder_block_sampled(name):
+    say(f"decoder block linear {name}")
+    c = synth.config3_linear(name)
+    _check_act_sampled(c["X"], oracle.E4M3, f"{name} X", 1)
+    _check_act_sampled(c["dY"], oracle.E4M3, f"{name} dY", 2)
+    same(gpu_w(c["W"], oracle.E4M3), oracle.quant_weight_128x128(c["W"].float().numpy(), oracle.E4M3), f"{name} W")
+
+
+def test_sweep_activations_sampled():
+    for M in synth.SWEEP_M:
+        x = synth.config4_x(M)
+        rows = _sample(M, 128, M)
+        q, s = gpu_1x128(x, oracle.E4M3)
+        same((q[rows], s[rows]), oracle.quant_act_1x128(x[rows].float().numpy(), oracle.E4M3), f"sweep M={M}")
+    w = synth.config4_weight()
+    same(gpu_w(w, oracle.E4M3), oracle.quant_weight_128x128(w.float().numpy(), oracle.E4M3), "sweep W")
+
+
+def test_heavy_tailed_gradients_sampled():
+    c = synth.config5()
+    _check_act_sampled(c["dY"], oracle.E5M2, "dY E5M2", 3)
+    _check_act_sampled(c["dY"], oracle.E4M3, "dY E4M3", 4)
+    _check_act_sampled(c["X"], oracle.E4M3, "X", 5)
+    same(gpu_w(c["W"], oracle.E4M3), oracle.quant_weight_128x128(c["W"].float().numpy(), oracle.E4M3), "W")
