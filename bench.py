@@ -1,0 +1,414 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 blockwise-quantized linear layer's hot path on one MI355X.
+
+One step = the whole path for one synthetic 2B-class decoder block at M = 16384 tokens (hidden
+2048; QKV 2048->2560, O 2048->2048, gate+up 2048->11264, down 5632->2048).  Per linear:
+    quantize X 1x128, quantize W 128x128, fprop Y = X W^T,
+    quantize dY 1x128, dgrad dX = dY W,
+    quantize dY 128x1, quantize X 128x1, wgrad dW = dY^T X
+i.e. 20 quantize passes and 12 GEMMs, all E4M3, BF16 in and out, inputs resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--workload decoder|linear|sweep] [--no-cpu-baseline]
+
+Prints ONE JSON line on stdout.  `value` = GEMM FLOPs of the step / wall time of the step (the
+quantize passes are inside the timed step).  `breakdown` holds per-product TFLOP/s and per-pass GB/s
+from HIP events recorded on the launch stream; `roofline` is for the dominant GEMM kernel;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same path (first 2048 tokens).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, published
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+METRIC = "FP8 blockwise GEMM TFLOP/s (fprop/dgrad/wgrad) + % of MI355X FP8 peak; quant GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", choices=["decoder", "linear", "sweep"], default="decoder")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=2048)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the GEMMs would shard by tokens, with one all-reduce of dW per step).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_blockwise_quantized_amd as fq
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    fq.lib()  # fail loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.workload == "decoder":
+        ops, bufs, desc = build_decoder(torch, fq, synth, dev)
+    elif args.workload == "linear":
+        ops, bufs, desc = build_linear(torch, fq, synth, dev)
+    else:
+        return run_sweep(args, torch, fq, synth, dev)
+
+    step_flops = sum(o["flops"] for o in ops)
+    step_bytes = sum(o["bytes"] for o in ops)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(record=None):
+        for i, o in enumerate(ops):
+            if record is not None:
+                record[i][0].record(stream)
+            o["fn"]()
+            if record is not None:
+                record[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, wall clock, synchronized on both sides
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+
+    # per-launch durations with HIP events on the launch stream (separate pass over the same steps)
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ops]
+          for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    dur = np.zeros(len(ops))
+    for k in range(args.steps):
+        for i in range(len(ops)):
+            dur[i] += ev[k][i][0].elapsed_time(ev[k][i][1])
+    dur_ms = dur / args.steps  # mean per launch
+
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    breakdown = summarize(ops, dur_ms)
+    roof = roofline(ops, dur_ms)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded, shapes and distributions of the workload)",
+        "config": desc,
+        "step_gemm_flops": step_flops,
+        "step_quant_bytes": step_bytes,
+        "pct_fp8_peak_step": round(100 * value / FP8_PEAK_TFLOPS, 2),
+        "breakdown": breakdown,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    del bufs
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_tokens, desc)
+    print(json.dumps(out), flush=True)
+
+
+# -----------------------------------------------------------------------------------------------
+# workloads
+# -----------------------------------------------------------------------------------------------
+
+def _q1x128_bytes(R, C, in_bytes=2):
+    return R * C * in_bytes + R * C + R * (C // 128) * 4
+
+
+def _q128x1_bytes(R, C, in_bytes=2):
+    return R * C * in_bytes + R * C + (R // 128) * C * 4
+
+
+def _qw_bytes(N, K, in_bytes=2):
+    return N * K * in_bytes + N * K + (N // 128) * (K // 128) * 4
+
+
+def _alloc_1x128(torch, R, C, dev):
+    return (torch.empty((R, C), dtype=torch.uint8, device=dev),
+            torch.empty((C // 128, (R + 3) // 4 * 4), dtype=torch.float32, device=dev)[:, :R])
+
+
+def _alloc_128x1(torch, R, C, dev):
+    return (torch.empty((C, R), dtype=torch.uint8, device=dev),
+            torch.empty((R // 128, (C + 3) // 4 * 4), dtype=torch.float32, device=dev)[:, :C])
+
+
+def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True):
+    """Closures for one linear's hot path; every output buffer is preallocated."""
+    M, K = X.shape
+    N = W.shape[0]
+    E4 = fq.E4M3
+    qx, sx = _alloc_1x128(torch, M, K, dev)
+    qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws_f = fq._workspace(fq.OP_FPROP, M, N, K, dev)
+    ops = [
+        dict(name=f"{name}.quant_x_1x128", kind="quant_1x128", bytes=_q1x128_bytes(M, K), flops=0,
+             fn=lambda: fq.fp8bq_quantize_act_1x128(X, E4, qx, sx)),
+        dict(name=f"{name}.quant_w_128x128", kind="quant_128x128", bytes=_qw_bytes(N, K), flops=0,
+             fn=lambda: fq.fp8bq_quantize_weight_128x128(W, E4, qw, sw)),
+        dict(name=f"{name}.fprop", kind="fprop", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
+             fn=lambda: fq.fp8bq_gemm_fprop(qx, sx, E4, qw, sw, E4, y, ws_f)),
+    ]
+    bufs = [qx, sx, qw, sw, y, ws_f]
+    if with_backward:
+        qdy, sdy = _alloc_1x128(torch, M, N, dev)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        qdyt, sdyt = _alloc_128x1(torch, M, N, dev)
+        qxt, sxt = _alloc_128x1(torch, M, K, dev)
+        dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        ws_d = fq._workspace(fq.OP_DGRAD, M, N, K, dev)
+        ws_w = fq._workspace(fq.OP_WGRAD, M, N, K, dev)
+        ops += [
+            dict(name=f"{name}.quant_dy_1x128", kind="quant_1x128", bytes=_q1x128_bytes(M, N), flops=0,
+                 fn=lambda: fq.fp8bq_quantize_act_1x128(dY, E4, qdy, sdy)),
+            dict(name=f"{name}.dgrad", kind="dgrad", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
+                 fn=lambda: fq.fp8bq_gemm_dgrad(qdy, sdy, E4, qw, sw, E4, dx, ws_d)),
+            dict(name=f"{name}.quant_dy_128x1", kind="quant_128x1", bytes=_q128x1_bytes(M, N), flops=0,
+                 fn=lambda: fq.fp8bq_quantize_act_128x1(dY, E4, qdyt, sdyt)),
+            dict(name=f"{name}.quant_x_128x1", kind="quant_128x1", bytes=_q128x1_bytes(M, K), flops=0,
+                 fn=lambda: fq.fp8bq_quantize_act_128x1(X, E4, qxt, sxt)),
+            dict(name=f"{name}.wgrad", kind="wgrad", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
+                 fn=lambda: fq.fp8bq_gemm_wgrad(qdyt, sdyt, E4, qxt, sxt, E4, dw, ws_w)),
+        ]
+        bufs += [qdy, sdy, dx, qdyt, sdyt, qxt, sxt, dw, ws_d, ws_w]
+    return ops, bufs
+
+
+def build_decoder(torch, fq, synth, dev):
+    log("generating the decoder-block inputs ...")
+    ops, bufs = [], []
+    for name, K, N in synth.DECODER_LINEARS:
+        c = synth.config3_linear(name)
+        X, W, dY = c["X"].to(dev), c["W"].to(dev), c["dY"].to(dev)
+        o, b = linear_ops(torch, fq, name, X, W, dY, dev)
+        ops += o
+        bufs += b + [X, W, dY]
+    desc = {
+        "workload": "decoder block fprop+dgrad+wgrad, M=16384 tokens, hidden 2048, GQA 16q/2kv x128 "
+                    "(QKV 2048->2560, O 2048->2048), SwiGLU gate+up 2048->11264, down 5632->2048; "
+                    "E4M3 act 1x128 / weight 128x128 / wgrad 128x1; BF16 in/out",
+        "tokens": synth.DECODER_M,
+        "linears": [[n, k, nn] for n, k, nn in synth.DECODER_LINEARS],
+        "gemms_per_step": 12,
+        "quant_passes_per_step": 20,
+    }
+    return ops, bufs, desc
+
+
+def build_linear(torch, fq, synth, dev):
+    c = synth.config2()
+    X, W = c["X"].to(dev), c["W"].to(dev)
+    ops, bufs = linear_ops(torch, fq, "linear", X, W, None, dev, with_backward=False)
+    desc = {"workload": "single fprop linear X[8192,2048] W[8192,2048], E4M3 act 1x128 / weight 128x128",
+            "tokens": 8192}
+    return ops, bufs + [X, W], desc
+
+
+def run_sweep(args, torch, fq, synth, dev):
+    W = synth.config4_weight().to(dev)
+    res = []
+    for M in synth.SWEEP_M:
+        X = synth.config4_x(M).to(dev)
+        ops, bufs = linear_ops(torch, fq, f"M{M}", X, W, None, dev, with_backward=False)
+        g = ops[2]
+        for _ in range(args.warmup):
+            g["fn"]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            g["fn"]()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        tf = g["flops"] / (ms * 1e-3) / 1e12
+        res.append({"M": M, "ms": round(ms, 5), "tflops": round(tf, 1), "pct_peak": round(100 * tf / FP8_PEAK_TFLOPS, 1)})
+        log(res[-1])
+    print(json.dumps({"workload": "square-weight fprop sweep K=N=2048", "points": res}))
+
+
+# -----------------------------------------------------------------------------------------------
+# reporting
+# -----------------------------------------------------------------------------------------------
+
+def summarize(ops, dur_ms):
+    kinds = {}
+    for o, d in zip(ops, dur_ms):
+        k = kinds.setdefault(o["kind"], {"ms": 0.0, "flops": 0, "bytes": 0, "launches": 0})
+        k["ms"] += float(d)
+        k["flops"] += o["flops"]
+        k["bytes"] += o["bytes"]
+        k["launches"] += 1
+    out = {}
+    for name, k in kinds.items():
+        r = {"ms_per_step": round(k["ms"], 4), "launches": k["launches"]}
+        if k["flops"]:
+            tf = k["flops"] / (k["ms"] * 1e-3) / 1e12
+            r.update(tflops=round(tf, 1), pct_fp8_peak=round(100 * tf / FP8_PEAK_TFLOPS, 1))
+        if k["bytes"]:
+            gbs = k["bytes"] / (k["ms"] * 1e-3) / 1e9
+            r.update(gbs=round(gbs, 1), pct_hbm_peak=round(100 * gbs / HBM_PEAK_GBS, 1))
+        out[name] = r
+    out["per_launch"] = [{"op": o["name"], "ms": round(float(d), 5),
+                          **({"tflops": round(o["flops"] / (d * 1e-3) / 1e12, 1)} if o["flops"] else
+                             {"gbs": round(o["bytes"] / (d * 1e-3) / 1e9, 1)})}
+                         for o, d in zip(ops, dur_ms)]
+    return out
+
+
+# Kernel instance names per product (gemm_tn_kernel<OP, BM, BN, waves_m, waves_n, scale mode, fmtA,
+# fmtB, f32 out>); a product's events bracket only its GEMM kernel except dgrad, whose call also runs
+# the weight-code transpose.
+GEMM_KERNEL = {
+    "fprop": "gemm_tn_kernel<0, 128, 128, 2, 2, 0, 0, 0, 0>",
+    "dgrad": "gemm_tn_kernel<1, 128, 128, 2, 2, 0, 0, 0, 0>",
+    "wgrad": "gemm_tn_kernel<2, 128, 128, 2, 2, 1, 0, 0, 0>",
+}
+ISOLATED = ("fprop", "wgrad")
+
+
+def _traffic(kind):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}_decoder_block.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        t = json.load(open(path))
+        src = open(os.path.join(ROOT, "fp8_blockwise_quantized_amd", "csrc", "gemm.hip"), "rb").read()
+        if t.get("gemm_hip_sha256") != hashlib.sha256(src).hexdigest():
+            return None
+        return t.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def roofline(ops, dur_ms):
+    """Dominant GEMM kernel (largest total time among products whose events bracket only the GEMM
+    kernel): achieved = its algorithmic FLOPs per launch / its mean launch duration."""
+    best = None
+    for kind in ISOLATED:
+        sel = [(o, d) for o, d in zip(ops, dur_ms) if o["kind"] == kind]
+        if not sel:
+            continue
+        t = sum(d for _, d in sel)
+        if best is None or t > best[1]:
+            best = (kind, t, sel)
+    if best is None:
+        return None
+    kind, t, sel = best
+    flops_per_launch = sum(o["flops"] for o, _ in sel) / len(sel)
+    ms_per_launch = t / len(sel)
+    achieved = flops_per_launch / (ms_per_launch * 1e-3) / 1e12
+    return {
+        "bound": "mfma",
+        "kernel": GEMM_KERNEL[kind],
+        "achieved": round(achieved, 1),
+        "peak": FP8_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+        "traffic": _traffic(kind),
+        "launches_per_step": len(sel),
+        "flops_per_launch": flops_per_launch,
+        "mean_launch_ms": round(ms_per_launch, 5),
+    }
+
+
+# -----------------------------------------------------------------------------------------------
+# CPU oracle baseline
+# -----------------------------------------------------------------------------------------------
+
+def cpu_baseline(tokens, desc):
+    """The oracle (as it stands) on the same path for the first `tokens` tokens of every linear:
+    quantize X, W, dY (1x128, 128x128, 1x128, 128x1, 128x1), fprop, dgrad, wgrad, BF16 rounding."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    E4 = oracle.E4M3
+    flops = 0
+    t_total = 0.0
+    for name, K, N in synth.DECODER_LINEARS:
+        c = synth.config3_linear(name)
+        X = c["X"][:tokens].float().numpy()
+        dY = c["dY"][:tokens].float().numpy()
+        W = c["W"].float().numpy()
+        t0 = time.perf_counter()
+        qx, sx = oracle.quant_act_1x128(X, E4)
+        qw, sw = oracle.quant_weight_128x128(W, E4)
+        oracle.to_bf16_rne(oracle.gemm_fprop(qx, sx, E4, qw, sw, E4))
+        qdy, sdy = oracle.quant_act_1x128(dY, E4)
+        oracle.to_bf16_rne(oracle.gemm_dgrad(qdy, sdy, E4, qw, sw, E4))
+        qdyt, sdyt = oracle.quant_act_128x1(dY, E4)
+        qxt, sxt = oracle.quant_act_128x1(X, E4)
+        oracle.to_bf16_rne(oracle.gemm_wgrad(qdyt, sdyt, E4, qxt, sxt, E4))
+        t_total += time.perf_counter() - t0
+        flops += 3 * 2 * tokens * N * K
+        log(f"cpu oracle {name}: {t_total:.1f} s so far")
+    return {
+        "value": round(flops / t_total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"the same decoder-block path (4 linears x quantize 5 ways + fprop/dgrad/wgrad + BF16 "
+                  f"rounding) on the first {tokens} of {desc.get('tokens')} tokens, full weights; "
+                  f"NumPy quantizers on 1 core, float64 BLAS GEMMs on {threads} threads; "
+                  f"{t_total:.1f} s wall",
+        "seconds": round(t_total, 2),
+        "cpu_model": _cpu_model(),
+        "cpu_count": os.cpu_count(),
+        "affinity": len(os.sched_getaffinity(0)),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -107,7 +107,7 @@ static int run_gemm(const GemmArgs& g, void* stream) {
     d.sb_nstride = 0;
   }
   void* ws_gemm = plan.ws_gemm ? (uint8_t*)g.ws + plan.ws_transpose : nullptr;
-  return launched(launch_gemm(d, plan, ws_gemm, s));
+  return launched(launch_gemm(g.op, d, plan, ws_gemm, s));
 }
 
 }  // namespace fp8bq

@@ -70,7 +70,8 @@ __device__ __forceinline__ v8i lds_patch(const uint8_t* tile, int row, int lane)
   return r;
 }
 
-template <int BM, int BN, int WGM, int WGN, int SBM, int FA, int FB, int OUTF32>
+// OP (fprop / dgrad / wgrad) only names the instance, so profiles attribute time per product.
+template <int OP, int BM, int BN, int WGM, int WGN, int SBM, int FA, int FB, int OUTF32>
 __global__ __launch_bounds__(WGM* WGN * 64) void gemm_tn_kernel(GemmDesc d, int64_t tiles_m, int64_t tiles_n) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WTM = BM / WGM;
@@ -239,31 +240,36 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_tn_kernel(GemmDesc d, int6
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int SBM, int FA, int FB, int OUTF32>
+template <int OP, int BM, int BN, int WGM, int WGN, int SBM, int FA, int FB, int OUTF32>
 static hipError_t launch_variant(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_tn_kernel<BM, BN, WGM, WGN, SBM, FA, FB, OUTF32>), dim3((unsigned)p.grid),
+  hipLaunchKernelGGL((gemm_tn_kernel<OP, BM, BN, WGM, WGN, SBM, FA, FB, OUTF32>), dim3((unsigned)p.grid),
                      dim3(WGM * WGN * 64), 0, st, d, p.tiles_m, p.tiles_n);
   return hipGetLastError();
 }
 
-template <int SBM, int FA, int FB, int OUTF32>
+template <int OP, int SBM, int FA, int FB, int OUTF32>
 static hipError_t launch_fmt(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
-  return launch_variant<128, 128, 2, 2, SBM, FA, FB, OUTF32>(d, p, st);
+  return launch_variant<OP, 128, 128, 2, 2, SBM, FA, FB, OUTF32>(d, p, st);
 }
 
-template <int SBM, int OUTF32>
-static hipError_t launch_sbm(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
-  if (d.fa == kE4M3 && d.fb == kE4M3) return launch_fmt<SBM, kE4M3, kE4M3, OUTF32>(d, p, st);
-  if (d.fa == kE5M2 && d.fb == kE4M3) return launch_fmt<SBM, kE5M2, kE4M3, OUTF32>(d, p, st);
-  if (d.fa == kE4M3 && d.fb == kE5M2) return launch_fmt<SBM, kE4M3, kE5M2, OUTF32>(d, p, st);
-  return launch_fmt<SBM, kE5M2, kE5M2, OUTF32>(d, p, st);
+template <int OP, int SBM, int OUTF32>
+static hipError_t launch_formats(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
+  if (d.fa == kE4M3 && d.fb == kE4M3) return launch_fmt<OP, SBM, kE4M3, kE4M3, OUTF32>(d, p, st);
+  if (d.fa == kE5M2 && d.fb == kE4M3) return launch_fmt<OP, SBM, kE5M2, kE4M3, OUTF32>(d, p, st);
+  if (d.fa == kE4M3 && d.fb == kE5M2) return launch_fmt<OP, SBM, kE4M3, kE5M2, OUTF32>(d, p, st);
+  return launch_fmt<OP, SBM, kE5M2, kE5M2, OUTF32>(d, p, st);
 }
 
-hipError_t launch_gemm(const GemmDesc& d, const GemmPlan& p, void* ws, hipStream_t st) {
+template <int OP, int SBM>
+static hipError_t launch_out(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
+  return d.out_f32 ? launch_formats<OP, SBM, 1>(d, p, st) : launch_formats<OP, SBM, 0>(d, p, st);
+}
+
+hipError_t launch_gemm(int op, const GemmDesc& d, const GemmPlan& p, void* ws, hipStream_t st) {
   (void)ws;
-  if (d.sb_mode == kSbBlock128)
-    return d.out_f32 ? launch_sbm<kSbBlock128, 1>(d, p, st) : launch_sbm<kSbBlock128, 0>(d, p, st);
-  return d.out_f32 ? launch_sbm<kSbColumn, 1>(d, p, st) : launch_sbm<kSbColumn, 0>(d, p, st);
+  if (op == kOpFprop) return launch_out<kOpFprop, kSbBlock128>(d, p, st);
+  if (op == kOpDgrad) return launch_out<kOpDgrad, kSbBlock128>(d, p, st);
+  return launch_out<kOpWgrad, kSbColumn>(d, p, st);
 }
 
 // ---------------------------------------------------------------------------------------------

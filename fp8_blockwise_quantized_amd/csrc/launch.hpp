@@ -39,7 +39,7 @@ struct GemmDesc {
   int sb_mode;   // SbMode
 };
 
-hipError_t launch_gemm(const GemmDesc& d, const GemmPlan& plan, void* ws, hipStream_t st);
+hipError_t launch_gemm(int op, const GemmDesc& d, const GemmPlan& plan, void* ws, hipStream_t st);
 
 // Byte-matrix transpose: dst[c * ldd + r] = src[r * lds + c] for r < R, c < C (R, C multiples of 128).
 hipError_t launch_transpose_u8(const uint8_t* src, int64_t lds, uint8_t* dst, int64_t ldd, int64_t R, int64_t C,
