@@ -29,6 +29,8 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-disable-promote-alloca-to-lds",
+    # MFMA results in VGPRs: the per-block scale fold reads them directly (no AGPR copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-command-line-argument",
 ]

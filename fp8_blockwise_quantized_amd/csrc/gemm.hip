@@ -70,20 +70,43 @@ __device__ __forceinline__ v8i lds_patch(const uint8_t* tile, int row, int lane)
   return r;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte (or 4-byte) global load per lane written straight into LDS at lds_base + 16 * lane
+// (or 4 * lane): global_load_lds_dwordx4 / _dword.  lds_base must be the same for the whole wave.
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 4, 0, 0);
+}
+
 // OP (fprop / dgrad / wgrad) only names the instance, so profiles attribute time per product.
+//
+// LDS stage layout (two stages): [A tile BM x 128 B][B tile BN x 128 B][A scales BM x f32]
+// [B scales: BN x f32 (per-column mode) or one f32 per 128 columns (per-block mode), 64 slots min].
+// Tiles and scales arrive by direct global->LDS loads: wave w fills 1 KB chunks w, w+NW, ... (8 rows
+// each); lane l of a chunk fetches the 16 bytes that belong at LDS offset 16*l, i.e. row l/8 and
+// physical chunk l%8, whose logical chunk is (l%8) ^ swz(row).
 template <int OP, int BM, int BN, int WGM, int WGN, int SBM, int FA, int FB, int OUTF32>
-__global__ __launch_bounds__(WGM* WGN * 64) void gemm_tn_kernel(GemmDesc d, int64_t tiles_m, int64_t tiles_n) {
-  constexpr int NT = WGM * WGN * 64;
+__global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN == 4 ? 2 : 1)) void gemm_tn_kernel(GemmDesc d, int64_t tiles_m,
+                                                                                      int64_t tiles_n) {
+  constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM;
   constexpr int WTN = BN / WGN;
   constexpr int MI = WTM / 16;
   constexpr int NI = WTN / 16;
-  constexpr int ACH = BM * 8 / NT;  // 16-byte chunks per thread per stage
-  constexpr int BCH = BN * 8 / NT;
-  constexpr int STAGE = (BM + BN) * 128;
-  static_assert(ACH >= 1 && BCH >= 1, "tile too small for the workgroup");
+  constexpr int SA_OFF = (BM + BN) * 128;
+  constexpr int NSB = SBM == kSbColumn ? BN : (BN / kGroup);
+  constexpr int SB_OFF = SA_OFF + BM * 4;
+  constexpr int STAGE = SB_OFF + (NSB > 64 ? NSB : 64) * 4;
+  constexpr int ACHUNKS = BM / 8, BCHUNKS = BN / 8;       // 1 KB chunks per stage
+  constexpr int SAJOBS = BM / 64;                          // 64 scales per wave job
+  constexpr int SBJOBS = NSB > 64 ? NSB / 64 : 1;
+  static_assert(ACHUNKS % NW == 0 && BCHUNKS % NW == 0, "tile chunks must split evenly over waves");
+  static_assert(BM % 64 == 0 && (NSB <= 64 || NSB % 64 == 0), "scale jobs are 64 lanes wide");
   static_assert(SBM != kSbBlock128 || WTN <= 128, "a wave's columns must share one weight block");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   int64_t tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -95,70 +118,57 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_tn_kernel(GemmDesc d, int6
   const int64_t M = d.M, N = d.N;
   const int nkb = (int)(d.K / kGroup);
 
-  // global -> LDS assignments
-  const uint8_t* ga[ACH];
-  int la[ACH];
+  // per-lane global sources for this wave's chunks (block 0 of the contraction)
+  const uint8_t* ga[ACHUNKS / NW];
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int cid = t + NT * i, row = cid >> 3, ch = cid & 7;
+  for (int i = 0; i < ACHUNKS / NW; ++i) {
+    const int c = wid + NW * i, row = 8 * c + (lane >> 3), lc = (lane & 7) ^ swz(row);
     int64_t gr = m0 + row;
-    gr = gr < M ? gr : M - 1;
-    ga[i] = d.a + gr * d.lda + ch * 16;
-    la[i] = row * 128 + ((ch ^ swz(row)) << 4);
+    gr = gr < M ? gr : M - 1;  // rows past the end are clamped; their results are never stored
+    ga[i] = d.a + gr * d.lda + lc * 16;
   }
-  const uint8_t* gb[BCH];
-  int lb[BCH];
+  const uint8_t* gb[BCHUNKS / NW];
 #pragma unroll
-  for (int i = 0; i < BCH; ++i) {
-    const int cid = t + NT * i, row = cid >> 3, ch = cid & 7;
+  for (int i = 0; i < BCHUNKS / NW; ++i) {
+    const int c = wid + NW * i, row = 8 * c + (lane >> 3), lc = (lane & 7) ^ swz(row);
     int64_t gr = n0 + row;
     gr = gr < N ? gr : N - 1;
-    gb[i] = d.b + gr * d.ldb + ch * 16;
-    lb[i] = BM * 128 + row * 128 + ((ch ^ swz(row)) << 4);
+    gb[i] = d.b + gr * d.ldb + lc * 16;
   }
-  // per-lane scale addressing
-  int64_t sa_row[MI];
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    int64_t m = m0 + wm * WTM + 16 * i + (lane & 15);
-    sa_row[i] = m < M ? m : M - 1;
+  // scale sources: job j of the A scales covers rows 64j..64j+63; B scales likewise
+  const float* gsa = nullptr;
+  int sa_job = -1;
+  if (wid < SAJOBS) {
+    sa_job = wid;
+    int64_t m = m0 + 64 * wid + lane;
+    m = m < M ? m : M - 1;
+    gsa = d.sa + m;
   }
-  const int64_t ncol_wave = n0 + wn * WTN;
-  const int64_t sb_blk = (ncol_wave / kGroup) * d.sb_nstride;  // kSbBlock128
-  int64_t sb_col[NI];                                           // kSbColumn
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    int64_t n = ncol_wave + 16 * j + 4 * (lane >> 4);
-    sb_col[j] = n < N ? n : N - 4;
+  const float* gsb = nullptr;
+  int sb_job = -1;
+  if (wid >= NW - SBJOBS) {
+    sb_job = wid - (NW - SBJOBS);
+    if constexpr (SBM == kSbColumn) {
+      int64_t n = n0 + 64 * sb_job + lane;
+      n = n < N ? n : N - 1;
+      gsb = d.sb + n;
+    } else {
+      const int64_t nbl = N / kGroup;
+      int64_t nb = n0 / kGroup + (lane < NSB ? lane : NSB - 1);
+      nb = nb < nbl ? nb : nbl - 1;
+      gsb = d.sb + nb * d.sb_nstride;
+    }
   }
 
-  v4i ra[ACH], rb[BCH];
-  float sav[MI], nsav[MI];
-  float sbb = 0.0f, nsbb = 0.0f;
-  v4f sbc[SBM == kSbColumn ? NI : 1], nsbc[SBM == kSbColumn ? NI : 1];
-
-#define FP8BQ_LOAD_STAGE(KB)                                                                  \
-  do {                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < ACH; ++i) ra[i] =                                   \
-        *reinterpret_cast<const v4i*>(ga[i] + (int64_t)(KB) * kGroup);                        \
-    _Pragma("unroll") for (int i = 0; i < BCH; ++i) rb[i] =                                   \
-        *reinterpret_cast<const v4i*>(gb[i] + (int64_t)(KB) * kGroup);                        \
-  } while (0)
-#define FP8BQ_STORE_STAGE(STG)                                                                \
-  do {                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < ACH; ++i) *reinterpret_cast<v4i*>((STG) + la[i]) = ra[i]; \
-    _Pragma("unroll") for (int i = 0; i < BCH; ++i) *reinterpret_cast<v4i*>((STG) + lb[i]) = rb[i]; \
-  } while (0)
-#define FP8BQ_LOAD_SCALES(KB, SA, SBB, SBC)                                                   \
-  do {                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < MI; ++i) SA[i] = d.sa[(int64_t)(KB) * d.ldsa + sa_row[i]]; \
-    if constexpr (SBM == kSbBlock128) {                                                       \
-      SBB = d.sb[(int64_t)(KB) * d.sb_kstride + sb_blk];                                      \
-    } else {                                                                                  \
-      _Pragma("unroll") for (int j = 0; j < NI; ++j) SBC[j] =                                 \
-          *reinterpret_cast<const v4f*>(d.sb + (int64_t)(KB) * d.sb_kstride + sb_col[j]);     \
-    }                                                                                         \
-  } while (0)
+  auto load_stage = [&](int kb, uint8_t* stg) {
+#pragma unroll
+    for (int i = 0; i < ACHUNKS / NW; ++i) dma16(ga[i] + (int64_t)kb * kGroup, stg + (wid + NW * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < BCHUNKS / NW; ++i)
+      dma16(gb[i] + (int64_t)kb * kGroup, stg + BM * 128 + (wid + NW * i) * 1024);
+    if (sa_job >= 0) dma4(gsa + (int64_t)kb * d.ldsa, stg + SA_OFF + 256 * sa_job);
+    if (sb_job >= 0) dma4(gsb + (int64_t)kb * d.sb_kstride, stg + SB_OFF + 256 * sb_job);
+  };
 
   v4f acc[MI][NI];
 #pragma unroll
@@ -166,60 +176,82 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_tn_kernel(GemmDesc d, int6
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-  FP8BQ_LOAD_STAGE(0);
-  FP8BQ_LOAD_SCALES(0, sav, sbb, sbc);
-  FP8BQ_STORE_STAGE(smem);
+  load_stage(0, smem);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int kb = 0; kb < nkb; ++kb) {
     const uint8_t* stage = smem + (kb & 1) * STAGE;
-    const bool more = kb + 1 < nkb;
-    if (more) {
-      FP8BQ_LOAD_STAGE(kb + 1);
-      FP8BQ_LOAD_SCALES(kb + 1, nsav, nsbb, nsbc);
-    }
-    v8i ap[MI], bp[NI];
+    // the other stage was last read before the previous barrier: refill it while this one is used
+    if (kb + 1 < nkb) load_stage(kb + 1, smem + ((kb + 1) & 1) * STAGE);
+
+    const float* ssa = reinterpret_cast<const float*>(stage + SA_OFF);
+    const float* ssb = reinterpret_cast<const float*>(stage + SB_OFF);
+    float sa_[MI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) ap[i] = lds_patch(stage, wm * WTM + 16 * i + (lane & 15), lane);
+    for (int i = 0; i < MI; ++i) sa_[i] = ssa[wm * WTM + 16 * i + (lane & 15)];
+    v8i bp[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) bp[j] = lds_patch(stage + BM * 128, wn * WTN + 16 * j + (lane & 15), lane);
+
+    // MFMA u is issued while the fold of MFMA u-LAG runs on the VALU, so the matrix pipe and the
+    // vector pipe overlap within the wave.  A patches are read as they are needed.
+    constexpr int NTILE = MI * NI;
+    constexpr int LAG = 2;
+    v4f p[NTILE];
+    v8i ap[MI];
+    if constexpr (SBM == kSbBlock128) {
+      const float sbv = ssb[(wn * WTN) / kGroup];
+      float sc[MI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+      for (int i = 0; i < MI; ++i) sc[i] = sa_[i] * sbv;
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const v4f p = mfma_block<FA, FB>(bp[j], ap[i]);
-        if constexpr (SBM == kSbBlock128) {
-          const float sc = sav[i] * sbb;
-          acc[i][j][0] = __builtin_fmaf(p[0], sc, acc[i][j][0]);
-          acc[i][j][1] = __builtin_fmaf(p[1], sc, acc[i][j][1]);
-          acc[i][j][2] = __builtin_fmaf(p[2], sc, acc[i][j][2]);
-          acc[i][j][3] = __builtin_fmaf(p[3], sc, acc[i][j][3]);
-        } else {
-          acc[i][j][0] = __builtin_fmaf(p[0], sav[i] * sbc[j].x, acc[i][j][0]);
-          acc[i][j][1] = __builtin_fmaf(p[1], sav[i] * sbc[j].y, acc[i][j][1]);
-          acc[i][j][2] = __builtin_fmaf(p[2], sav[i] * sbc[j].z, acc[i][j][2]);
-          acc[i][j][3] = __builtin_fmaf(p[3], sav[i] * sbc[j].w, acc[i][j][3]);
+      for (int u = 0; u < NTILE + LAG; ++u) {
+        if (u < NTILE) {
+          if (u % NI == 0) ap[u / NI] = lds_patch(stage, wm * WTM + 16 * (u / NI) + (lane & 15), lane);
+          p[u] = mfma_block<FA, FB>(bp[u % NI], ap[u / NI]);
+        }
+        if (u >= LAG) {
+          const int v = u - LAG, i = v / NI, j = v % NI;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[v][r], sc[i], acc[i][j][r]);
         }
       }
-    }
-    if (more) {
-      FP8BQ_STORE_STAGE(smem + ((kb + 1) & 1) * STAGE);
 #pragma unroll
-      for (int i = 0; i < MI; ++i) sav[i] = nsav[i];
-      if constexpr (SBM == kSbBlock128) {
-        sbb = nsbb;
-      } else {
+      for (int u = 0; u < NTILE; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then up to five VALU ops
+      }
+    } else {
+      v4f sbc[NI];
 #pragma unroll
-        for (int j = 0; j < NI; ++j) sbc[j] = nsbc[j];
+      for (int j = 0; j < NI; ++j)
+        sbc[j] = *reinterpret_cast<const v4f*>(ssb + wn * WTN + 16 * j + 4 * (lane >> 4));
+#pragma unroll
+      for (int u = 0; u < NTILE + LAG; ++u) {
+        if (u < NTILE) {
+          if (u % NI == 0) ap[u / NI] = lds_patch(stage, wm * WTM + 16 * (u / NI) + (lane & 15), lane);
+          p[u] = mfma_block<FA, FB>(bp[u % NI], ap[u / NI]);
+        }
+        if (u >= LAG) {
+          const int v = u - LAG, i = v / NI, j = v % NI;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[v][r], sa_[i] * sbc[j][r], acc[i][j][r]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NTILE; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
       }
     }
+    // the refill of the other stage must land before anyone reads it after the barrier
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-#undef FP8BQ_LOAD_STAGE
-#undef FP8BQ_STORE_STAGE
-#undef FP8BQ_LOAD_SCALES
 
   // epilogue
+  const int64_t ncol_wave = n0 + wn * WTN;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int64_t m = m0 + wm * WTM + 16 * i + (lane & 15);
@@ -230,7 +262,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_tn_kernel(GemmDesc d, int6
       if (n >= N) continue;
       if constexpr (OUTF32) {
         float* c = reinterpret_cast<float*>(d.c) + m * d.ldc + n;
-        *reinterpret_cast<float4*>(c) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<v4f*>(c) = acc[i][j];
       } else {
         uint16_t* c = reinterpret_cast<uint16_t*>(d.c) + m * d.ldc + n;
         *reinterpret_cast<uint2*>(c) =
@@ -249,7 +281,10 @@ static hipError_t launch_variant(const GemmDesc& d, const GemmPlan& p, hipStream
 
 template <int OP, int SBM, int FA, int FB, int OUTF32>
 static hipError_t launch_fmt(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
-  return launch_variant<OP, 128, 128, 2, 2, SBM, FA, FB, OUTF32>(d, p, st);
+  switch (p.variant) {
+    case kVar256x256: return launch_variant<OP, 256, 256, 2, 4, SBM, FA, FB, OUTF32>(d, p, st);
+    default: return launch_variant<OP, 128, 128, 2, 2, SBM, FA, FB, OUTF32>(d, p, st);
+  }
 }
 
 template <int OP, int SBM, int OUTF32>

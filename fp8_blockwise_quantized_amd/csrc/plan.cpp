@@ -1,7 +1,18 @@
 // Tile / launch planner (pure host C++).
 #include "plan.hpp"
 
+#include <cstdlib>
+
 namespace fp8bq {
+
+// FP8BQ_GEMM_VARIANT=<n> forces a tile variant (tuning aid); read once.
+static int forced_variant() {
+  static const int v = [] {
+    const char* e = std::getenv("FP8BQ_GEMM_VARIANT");
+    return e ? std::atoi(e) : -1;
+  }();
+  return v;
+}
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -17,9 +28,10 @@ GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count) {
   } else {
     rows = N; cols = K;
   }
-  p.tile_m = 128;
-  p.tile_n = 128;
-  p.variant = 0;
+  p.variant = kVar128x128;
+  if (forced_variant() >= 0) p.variant = forced_variant();
+  p.tile_m = p.variant == kVar256x256 ? 256 : 128;
+  p.tile_n = p.variant == kVar256x256 ? 256 : 128;
   p.split_k = 1;
   p.tiles_m = cdiv(rows, p.tile_m);
   p.tiles_n = cdiv(cols, p.tile_n);

@@ -11,6 +11,11 @@
 namespace fp8bq {
 
 enum SbMode : int { kSbBlock128 = 0, kSbColumn = 1 };
+// Kernel tile variants: workgroup tile (rows x columns of the output) and wave layout.
+enum Variant : int {
+  kVar128x128 = 0,  // 4 waves (2x2) of 64x64, two workgroups per CU
+  kVar256x256 = 1,  // 8 waves (2x4) of 128x64, one workgroup per CU
+};
 enum Op : int { kOpFprop = 0, kOpDgrad = 1, kOpWgrad = 2 };
 
 struct GemmPlan {
