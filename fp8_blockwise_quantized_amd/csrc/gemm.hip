@@ -81,16 +81,54 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 4, 0, 0);
 }
 
+// One work unit: an output tile and the range of 128-long contraction blocks it sums.
+struct Unit {
+  int64_t m0, n0;
+  int kb0, kb1, split;
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ Unit unit_of(int64_t u, int64_t tiles_m, int64_t tiles_n, int nsplit, int nkb) {
+  const int64_t T = tiles_m * tiles_n;
+  const int64_t w = u % T;
+  const int s = (int)(u / T);
+  int64_t tm, tn;
+  tile_of(w, tiles_m, tiles_n, tm, tn);
+  Unit r;
+  r.m0 = tm * BM;
+  r.n0 = tn * BN;
+  r.kb0 = (int)((int64_t)s * nkb / nsplit);
+  r.kb1 = (int)((int64_t)(s + 1) * nkb / nsplit);
+  r.split = s;
+  return r;
+}
+
 // OP (fprop / dgrad / wgrad) only names the instance, so profiles attribute time per product.
 //
-// LDS stage layout (two stages): [A tile BM x 128 B][B tile BN x 128 B][A scales BM x f32]
-// [B scales: BN x f32 (per-column mode) or one f32 per 128 columns (per-block mode), 64 slots min].
-// Tiles and scales arrive by direct global->LDS loads: wave w fills 1 KB chunks w, w+NW, ... (8 rows
-// each); lane l of a chunk fetches the 16 bytes that belong at LDS offset 16*l, i.e. row l/8 and
-// physical chunk l%8, whose logical chunk is (l%8) ^ swz(row).
-template <int OP, int BM, int BN, int WGM, int WGN, int SBM, int FA, int FB, int OUTF32>
-__global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN == 4 ? 2 : 1)) void gemm_tn_kernel(GemmDesc d, int64_t tiles_m,
-                                                                                      int64_t tiles_n) {
+// Persistent workgroups: workgroup b processes work units b, b + G, b + 2G, ... (G = grid size, a
+// multiple of 8 when there is more than one round, so every unit of a workgroup maps to its XCD's
+// contiguous range in tile_of).  A unit is one BM x BN output tile and a range of contraction blocks
+// (all of them, or 1/nsplit when the contraction is split; split units write FP32 partial sums that
+// a separate pass adds in a fixed order).  The LDS ring runs continuously across units: the loads
+// for a unit's first block are issued while the previous unit's last block is multiplied and its
+// tile is written out.
+//
+// LDS stage layout (NSTAGE stages, a ring): [A tile BM x 128 B][B tile BN x 128 B][A scales BM x f32]
+// [B scales: BN x f32 (per-column mode) or one f32 per 128 columns (per-block mode), 64 slots min]
+// [256 B sink for padding loads].  Tiles and scales arrive by direct global->LDS loads: wave w fills
+// 1 KB chunks w, w+NW, ... (8 rows each); lane l of a chunk fetches the 16 bytes that belong at LDS
+// offset 16*l, i.e. row l/8 and physical chunk l%8, whose logical chunk is (l%8) ^ swz(row).  Every
+// wave issues the same number of loads per stage (scale jobs are padded with loads into the sink), so
+// one s_waitcnt vmcnt(loads per stage) leaves exactly the newest stage in flight.
+template <int BM, int BN, int NW, int NSTAGE>
+struct StageMinBlocks {
+  static constexpr int kStage = (BM + BN) * 128 + BM * 4 + 64 * 4 + 256;  // lower bound of STAGE
+  static constexpr int value = (NW == 4 && 2 * NSTAGE * kStage <= 160 * 1024) ? 2 : 1;
+};
+
+template <int OP, int BM, int BN, int WGM, int WGN, int NSTAGE, int SBM, int FA, int FB, int OUTF32>
+__global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, NSTAGE>::value)) void gemm_tn_kernel(
+    GemmDesc d, int64_t tiles_m, int64_t tiles_n, int nsplit, float* __restrict__ partial) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM;
   constexpr int WTN = BN / WGN;
@@ -99,75 +137,117 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN == 4 ? 2 : 1)) void gemm_
   constexpr int SA_OFF = (BM + BN) * 128;
   constexpr int NSB = SBM == kSbColumn ? BN : (BN / kGroup);
   constexpr int SB_OFF = SA_OFF + BM * 4;
-  constexpr int STAGE = SB_OFF + (NSB > 64 ? NSB : 64) * 4;
-  constexpr int ACHUNKS = BM / 8, BCHUNKS = BN / 8;       // 1 KB chunks per stage
-  constexpr int SAJOBS = BM / 64;                          // 64 scales per wave job
+  constexpr int SINK_OFF = SB_OFF + (NSB > 64 ? NSB : 64) * 4;
+  constexpr int STAGE = SINK_OFF + 256;
+  constexpr int ACHUNKS = BM / 8, BCHUNKS = BN / 8;  // 1 KB chunks per stage
+  constexpr int SAJOBS = BM / 64;                     // 64 scales per wave job
   constexpr int SBJOBS = NSB > 64 ? NSB / 64 : 1;
+  constexpr int SJOBS = SAJOBS + SBJOBS;
+  constexpr int JPW = (SJOBS + NW - 1) / NW;          // scale jobs per wave (padded)
+  constexpr int LOADS = ACHUNKS / NW + BCHUNKS / NW + JPW;  // loads per wave per stage
   static_assert(ACHUNKS % NW == 0 && BCHUNKS % NW == 0, "tile chunks must split evenly over waves");
   static_assert(BM % 64 == 0 && (NSB <= 64 || NSB % 64 == 0), "scale jobs are 64 lanes wide");
   static_assert(SBM != kSbBlock128 || WTN <= 128, "a wave's columns must share one weight block");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "LDS ring does not fit");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
 
-  int64_t tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wid / WGN, wn = wid % WGN;
   const int64_t M = d.M, N = d.N;
   const int nkb = (int)(d.K / kGroup);
+  const int64_t U = tiles_m * tiles_n * nsplit;
+  const int64_t G = gridDim.x;
 
-  // per-lane global sources for this wave's chunks (block 0 of the contraction)
-  const uint8_t* ga[ACHUNKS / NW];
+  // tile-independent parts of this lane's load addresses
+  int arow[ACHUNKS / NW], acol[ACHUNKS / NW];
 #pragma unroll
   for (int i = 0; i < ACHUNKS / NW; ++i) {
-    const int c = wid + NW * i, row = 8 * c + (lane >> 3), lc = (lane & 7) ^ swz(row);
-    int64_t gr = m0 + row;
-    gr = gr < M ? gr : M - 1;  // rows past the end are clamped; their results are never stored
-    ga[i] = d.a + gr * d.lda + lc * 16;
+    const int row = 8 * (wid + NW * i) + (lane >> 3);
+    arow[i] = row;
+    acol[i] = ((lane & 7) ^ swz(row)) * 16;
   }
-  const uint8_t* gb[BCHUNKS / NW];
+  int brow[BCHUNKS / NW], bcol[BCHUNKS / NW];
 #pragma unroll
   for (int i = 0; i < BCHUNKS / NW; ++i) {
-    const int c = wid + NW * i, row = 8 * c + (lane >> 3), lc = (lane & 7) ^ swz(row);
-    int64_t gr = n0 + row;
-    gr = gr < N ? gr : N - 1;
-    gb[i] = d.b + gr * d.ldb + lc * 16;
+    const int row = 8 * (wid + NW * i) + (lane >> 3);
+    brow[i] = row;
+    bcol[i] = ((lane & 7) ^ swz(row)) * 16;
   }
-  // scale sources: job j of the A scales covers rows 64j..64j+63; B scales likewise
-  const float* gsa = nullptr;
-  int sa_job = -1;
-  if (wid < SAJOBS) {
-    sa_job = wid;
-    int64_t m = m0 + 64 * wid + lane;
-    m = m < M ? m : M - 1;
-    gsa = d.sa + m;
-  }
-  const float* gsb = nullptr;
-  int sb_job = -1;
-  if (wid >= NW - SBJOBS) {
-    sb_job = wid - (NW - SBJOBS);
-    if constexpr (SBM == kSbColumn) {
-      int64_t n = n0 + 64 * sb_job + lane;
-      n = n < N ? n : N - 1;
-      gsb = d.sb + n;
-    } else {
-      const int64_t nbl = N / kGroup;
-      int64_t nb = n0 / kGroup + (lane < NSB ? lane : NSB - 1);
-      nb = nb < nbl ? nb : nbl - 1;
-      gsb = d.sb + nb * d.sb_nstride;
-    }
-  }
-
-  auto load_stage = [&](int kb, uint8_t* stg) {
+  // load-side cursor: unit lu, block lkb, and this lane's sources for that unit
+  int64_t lu = blockIdx.x;
+  Unit L = unit_of<BM, BN>(lu, tiles_m, tiles_n, nsplit, nkb);
+  int lkb = L.kb0;
+  bool lmore = true;
+  const uint8_t* ga[ACHUNKS / NW];
+  const uint8_t* gb[BCHUNKS / NW];
+  const float* gs[JPW];
+  int64_t gsk[JPW];
+  int lso[JPW];
+  auto set_sources = [&](const Unit& u) {
 #pragma unroll
-    for (int i = 0; i < ACHUNKS / NW; ++i) dma16(ga[i] + (int64_t)kb * kGroup, stg + (wid + NW * i) * 1024);
+    for (int i = 0; i < ACHUNKS / NW; ++i) {
+      int64_t r = u.m0 + arow[i];
+      r = r < M ? r : M - 1;  // rows past the end are clamped; their results are never stored
+      ga[i] = d.a + r * d.lda + acol[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BCHUNKS / NW; ++i) {
+      int64_t r = u.n0 + brow[i];
+      r = r < N ? r : N - 1;
+      gb[i] = d.b + r * d.ldb + bcol[i];
+    }
+    // scale jobs: job j < SAJOBS loads A scales of rows 64j..64j+63, the next SBJOBS the B scales;
+    // wave w runs jobs w, w+NW, ...; missing jobs load a valid scale into the sink
+#pragma unroll
+    for (int q = 0; q < JPW; ++q) {
+      const int j = wid + NW * q;
+      if (j < SAJOBS) {
+        int64_t m = u.m0 + 64 * j + lane;
+        m = m < M ? m : M - 1;
+        gs[q] = d.sa + m;
+        gsk[q] = d.ldsa;
+        lso[q] = SA_OFF + 256 * j;
+      } else if (j < SJOBS) {
+        const int v = j - SAJOBS;
+        if constexpr (SBM == kSbColumn) {
+          int64_t n = u.n0 + 64 * v + lane;
+          n = n < N ? n : N - 1;
+          gs[q] = d.sb + n;
+        } else {
+          const int64_t nbl = N / kGroup;
+          int64_t nb = u.n0 / kGroup + (lane < NSB ? lane : NSB - 1);
+          nb = nb < nbl ? nb : nbl - 1;
+          gs[q] = d.sb + nb * d.sb_nstride;
+        }
+        gsk[q] = d.sb_kstride;
+        lso[q] = SB_OFF + 256 * v;
+      } else {
+        gs[q] = d.sa;
+        gsk[q] = 0;
+        lso[q] = SINK_OFF;
+      }
+    }
+  };
+  auto load_next = [&](uint8_t* stg) {  // issue the loads of (lu, lkb) into stg, then advance
+#pragma unroll
+    for (int i = 0; i < ACHUNKS / NW; ++i) dma16(ga[i] + (int64_t)lkb * kGroup, stg + (wid + NW * i) * 1024);
 #pragma unroll
     for (int i = 0; i < BCHUNKS / NW; ++i)
-      dma16(gb[i] + (int64_t)kb * kGroup, stg + BM * 128 + (wid + NW * i) * 1024);
-    if (sa_job >= 0) dma4(gsa + (int64_t)kb * d.ldsa, stg + SA_OFF + 256 * sa_job);
-    if (sb_job >= 0) dma4(gsb + (int64_t)kb * d.sb_kstride, stg + SB_OFF + 256 * sb_job);
+      dma16(gb[i] + (int64_t)lkb * kGroup, stg + BM * 128 + (wid + NW * i) * 1024);
+#pragma unroll
+    for (int q = 0; q < JPW; ++q) dma4(gs[q] + (int64_t)lkb * gsk[q], stg + lso[q]);
+    if (++lkb == L.kb1) {
+      lu += G;
+      if (lu < U) {
+        L = unit_of<BM, BN>(lu, tiles_m, tiles_n, nsplit, nkb);
+        lkb = L.kb0;
+        set_sources(L);
+      } else {
+        lmore = false;
+      }
+    }
   };
 
   v4f acc[MI][NI];
@@ -176,14 +256,35 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN == 4 ? 2 : 1)) void gemm_
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-  load_stage(0, smem);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (lu >= U) return;  // (the grid never exceeds the unit count)
+  set_sources(L);
+  // compute-side cursor
+  int64_t cu = lu;
+  Unit C = L;
+  int ckb = C.kb0;
+
+  // prologue: up to NSTAGE-1 blocks in flight, the first landed
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) {
+    if (lmore) {
+      load_next(smem + s * STAGE);
+      ++issued;
+    }
+  }
+  if (issued == NSTAGE - 1) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * LOADS) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const uint8_t* stage = smem + (kb & 1) * STAGE;
-    // the other stage was last read before the previous barrier: refill it while this one is used
-    if (kb + 1 < nkb) load_stage(kb + 1, smem + ((kb + 1) & 1) * STAGE);
+  int rd = 0, wr = NSTAGE - 1;  // ring slots read / refilled this iteration
+  while (true) {
+    const uint8_t* stage = smem + rd * STAGE;
+    // slot wr was last read in the previous iteration, before its barrier: refill it now
+    const bool refill = lmore;
+    if (refill) load_next(smem + wr * STAGE);
 
     const float* ssa = reinterpret_cast<const float*>(stage + SA_OFF);
     const float* ssb = reinterpret_cast<const float*>(stage + SB_OFF);
@@ -245,66 +346,114 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN == 4 ? 2 : 1)) void gemm_
         __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
       }
     }
-    // the refill of the other stage must land before anyone reads it after the barrier
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the slot read next iteration must have landed before anyone reads it after the barrier; the
+    // loads issued this iteration (if any) may stay in flight
+    if (refill) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * LOADS) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
-  }
+    rd = rd + 1 == NSTAGE ? 0 : rd + 1;
+    wr = wr + 1 == NSTAGE ? 0 : wr + 1;
 
-  // epilogue
-  const int64_t ncol_wave = n0 + wn * WTN;
+    if (++ckb < C.kb1) continue;
+
+    // unit finished: write the tile (or its partial sum) and move on
+    const int64_t ncol_wave = C.n0 + wn * WTN;
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int64_t m = m0 + wm * WTM + 16 * i + (lane & 15);
-    if (m >= M) continue;
+    for (int i = 0; i < MI; ++i) {
+      const int64_t m = C.m0 + wm * WTM + 16 * i + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int64_t n = ncol_wave + 16 * j + 4 * (lane >> 4);
-      if (n >= N) continue;
-      if constexpr (OUTF32) {
-        float* c = reinterpret_cast<float*>(d.c) + m * d.ldc + n;
-        *reinterpret_cast<v4f*>(c) = acc[i][j];
-      } else {
-        uint16_t* c = reinterpret_cast<uint16_t*>(d.c) + m * d.ldc + n;
-        *reinterpret_cast<uint2*>(c) =
-            make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+      for (int j = 0; j < NI; ++j) {
+        const int64_t n = ncol_wave + 16 * j + 4 * (lane >> 4);
+        if (m < M && n < N) {
+          if (nsplit > 1) {
+            float* c = partial + ((int64_t)C.split * M + m) * N + n;
+            *reinterpret_cast<v4f*>(c) = acc[i][j];
+          } else if constexpr (OUTF32) {
+            float* c = reinterpret_cast<float*>(d.c) + m * d.ldc + n;
+            *reinterpret_cast<v4f*>(c) = acc[i][j];
+          } else {
+            uint16_t* c = reinterpret_cast<uint16_t*>(d.c) + m * d.ldc + n;
+            *reinterpret_cast<uint2*>(c) =
+                make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+          }
+        }
+        acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
       }
+    }
+    cu += G;
+    if (cu >= U) break;
+    C = unit_of<BM, BN>(cu, tiles_m, tiles_n, nsplit, nkb);
+    ckb = C.kb0;
+  }
+}
+
+// Sum of the split partial sums in split order, converted to the output type:
+// out[m, n] = sum_s partial[s][m][n].
+template <int OUTF32>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int nsplit, int64_t M,
+                                                            int64_t N, void* __restrict__ out, int64_t ldo) {
+  const int64_t total = M * (N / 4);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / (N / 4), n = 4 * (i - m * (N / 4));
+    v4f s = *reinterpret_cast<const v4f*>(partial + m * N + n);
+    for (int k = 1; k < nsplit; ++k) s += *reinterpret_cast<const v4f*>(partial + ((int64_t)k * M + m) * N + n);
+    if constexpr (OUTF32) {
+      *reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + m * ldo + n) = s;
+    } else {
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + m * ldo + n) =
+          make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
     }
   }
 }
 
-template <int OP, int BM, int BN, int WGM, int WGN, int SBM, int FA, int FB, int OUTF32>
-static hipError_t launch_variant(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_tn_kernel<OP, BM, BN, WGM, WGN, SBM, FA, FB, OUTF32>), dim3((unsigned)p.grid),
-                     dim3(WGM * WGN * 64), 0, st, d, p.tiles_m, p.tiles_n);
+template <int OP, int BM, int BN, int WGM, int WGN, int NSTAGE, int SBM, int FA, int FB, int OUTF32>
+static hipError_t launch_variant(const GemmDesc& d, const GemmPlan& p, float* partial, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_tn_kernel<OP, BM, BN, WGM, WGN, NSTAGE, SBM, FA, FB, OUTF32>), dim3((unsigned)p.grid),
+                     dim3(WGM * WGN * 64), 0, st, d, p.tiles_m, p.tiles_n, p.split_k, partial);
   return hipGetLastError();
 }
 
 template <int OP, int SBM, int FA, int FB, int OUTF32>
-static hipError_t launch_fmt(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
-  switch (p.variant) {
-    case kVar256x256: return launch_variant<OP, 256, 256, 2, 4, SBM, FA, FB, OUTF32>(d, p, st);
-    default: return launch_variant<OP, 128, 128, 2, 2, SBM, FA, FB, OUTF32>(d, p, st);
-  }
+static hipError_t launch_fmt(const GemmDesc& d, const GemmPlan& p, float* partial, hipStream_t st) {
+  return launch_variant<OP, 128, 128, 2, 2, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
 }
 
 template <int OP, int SBM, int OUTF32>
-static hipError_t launch_formats(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
-  if (d.fa == kE4M3 && d.fb == kE4M3) return launch_fmt<OP, SBM, kE4M3, kE4M3, OUTF32>(d, p, st);
-  if (d.fa == kE5M2 && d.fb == kE4M3) return launch_fmt<OP, SBM, kE5M2, kE4M3, OUTF32>(d, p, st);
-  if (d.fa == kE4M3 && d.fb == kE5M2) return launch_fmt<OP, SBM, kE4M3, kE5M2, OUTF32>(d, p, st);
-  return launch_fmt<OP, SBM, kE5M2, kE5M2, OUTF32>(d, p, st);
+static hipError_t launch_formats(const GemmDesc& d, const GemmPlan& p, float* partial, hipStream_t st) {
+  if (d.fa == kE4M3 && d.fb == kE4M3) return launch_fmt<OP, SBM, kE4M3, kE4M3, OUTF32>(d, p, partial, st);
+  if (d.fa == kE5M2 && d.fb == kE4M3) return launch_fmt<OP, SBM, kE5M2, kE4M3, OUTF32>(d, p, partial, st);
+  if (d.fa == kE4M3 && d.fb == kE5M2) return launch_fmt<OP, SBM, kE4M3, kE5M2, OUTF32>(d, p, partial, st);
+  return launch_fmt<OP, SBM, kE5M2, kE5M2, OUTF32>(d, p, partial, st);
 }
 
 template <int OP, int SBM>
-static hipError_t launch_out(const GemmDesc& d, const GemmPlan& p, hipStream_t st) {
-  return d.out_f32 ? launch_formats<OP, SBM, 1>(d, p, st) : launch_formats<OP, SBM, 0>(d, p, st);
+static hipError_t launch_out(const GemmDesc& d, const GemmPlan& p, float* partial, hipStream_t st) {
+  return d.out_f32 ? launch_formats<OP, SBM, 1>(d, p, partial, st) : launch_formats<OP, SBM, 0>(d, p, partial, st);
 }
 
 hipError_t launch_gemm(int op, const GemmDesc& d, const GemmPlan& p, void* ws, hipStream_t st) {
-  (void)ws;
-  if (op == kOpFprop) return launch_out<kOpFprop, kSbBlock128>(d, p, st);
-  if (op == kOpDgrad) return launch_out<kOpDgrad, kSbBlock128>(d, p, st);
-  return launch_out<kOpWgrad, kSbColumn>(d, p, st);
+  float* partial = p.split_k > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  hipError_t e;
+  if (op == kOpFprop)
+    e = launch_out<kOpFprop, kSbBlock128>(d, p, partial, st);
+  else if (op == kOpDgrad)
+    e = launch_out<kOpDgrad, kSbBlock128>(d, p, partial, st);
+  else
+    e = launch_out<kOpWgrad, kSbColumn>(d, p, partial, st);
+  if (e != hipSuccess || p.split_k <= 1) return e;
+  const int64_t total = d.M * (d.N / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (d.out_f32)
+    hipLaunchKernelGGL(splitk_reduce_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, partial, p.split_k, d.M,
+                       d.N, d.c, d.ldc);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, partial, p.split_k, d.M,
+                       d.N, d.c, d.ldc);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------

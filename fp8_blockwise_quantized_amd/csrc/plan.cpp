@@ -1,44 +1,56 @@
 // Tile / launch planner (pure host C++).
 #include "plan.hpp"
 
-#include <cstdlib>
-
 namespace fp8bq {
-
-// FP8BQ_GEMM_VARIANT=<n> forces a tile variant (tuning aid); read once.
-static int forced_variant() {
-  static const int v = [] {
-    const char* e = std::getenv("FP8BQ_GEMM_VARIANT");
-    return e ? std::atoi(e) : -1;
-  }();
-  return v;
-}
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Cost model in microseconds: a round of resident units takes about 1.2 us per contraction block
+// (measured: two 128x128 workgroups per CU), and a split adds a pass that writes and re-reads
+// split x rows x cols FP32 partials and writes the output (~5 TB/s effective).  Splitting pays off
+// only when the tiles alone leave workgroup slots idle.
+int choose_split(int64_t rows, int64_t cols, int64_t nkb, int64_t slots) {
+  const int64_t tiles = cdiv(rows, kTileM) * cdiv(cols, kTileN);
+  int best = 1;
+  double best_us = 0.0;
+  for (int s = 1; s <= kMaxSplit; ++s) {
+    if (s > 1 && nkb / s < 4) break;  // keep at least 4 blocks per unit
+    const double rounds = (double)cdiv(tiles * s, slots);
+    const double gemm_us = rounds * ((double)nkb / s) * 1.2;
+    const double red_us = s > 1 ? (8.0 * s + 4.0) * (double)rows * (double)cols / 5.0e6 : 0.0;
+    const double us = gemm_us + red_us;
+    if (s == 1 || us < best_us * 0.97) {
+      best = s;
+      best_us = us;
+    }
+  }
+  return best;
+}
+
 GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count) {
-  (void)cu_count;
   GemmPlan p;
   // Output shape and contraction length in the kernel's TN frame.
-  int64_t rows, cols;
+  int64_t rows, cols, contraction;
   if (op == kOpFprop) {
-    rows = M; cols = N;
+    rows = M; cols = N; contraction = K;
   } else if (op == kOpDgrad) {
-    rows = M; cols = K;
+    rows = M; cols = K; contraction = N;
   } else {
-    rows = N; cols = K;
+    rows = N; cols = K; contraction = M;
   }
-  p.variant = kVar128x128;
-  if (forced_variant() >= 0) p.variant = forced_variant();
-  p.tile_m = p.variant == kVar256x256 ? 256 : 128;
-  p.tile_n = p.variant == kVar256x256 ? 256 : 128;
-  p.split_k = 1;
+  const int64_t slots = (int64_t)(cu_count > 0 ? cu_count : 256) * kBlocksPerCu;
+  const int64_t nkb = contraction / 128;
   p.tiles_m = cdiv(rows, p.tile_m);
   p.tiles_n = cdiv(cols, p.tile_n);
-  p.grid = p.tiles_m * p.tiles_n * p.split_k;
-  p.ws_gemm = 0;
+  p.split_k = (rows > 0 && cols > 0 && nkb > 0) ? choose_split(rows, cols, nkb, slots) : 1;
+  p.units = p.tiles_m * p.tiles_n * p.split_k;
+  // persistent grid: one workgroup per slot (a multiple of 8, so each workgroup stays on one XCD's
+  // range of tiles), or one per unit when there are fewer units
+  int64_t g = slots - slots % 8;
+  p.grid = p.units < g ? p.units : g;
+  p.ws_gemm = p.split_k > 1 ? (size_t)p.split_k * (size_t)rows * (size_t)cols * 4 : 0;
   p.ws_transpose = (op == kOpDgrad) ? (size_t)N * (size_t)K : 0;
-  // round the transpose buffer up so the split-K area that may follow it stays 256-byte aligned
+  // round the transpose buffer up so the partial sums that follow it stay 256-byte aligned
   p.ws_transpose = (p.ws_transpose + 255) & ~(size_t)255;
   return p;
 }

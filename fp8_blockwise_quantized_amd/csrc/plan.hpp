@@ -1,8 +1,8 @@
 // Tile / launch planner for the scaled FP8 GEMMs (pure host C++, no HIP calls).
 //
 // Given the product (fprop, dgrad, wgrad), its sizes and the device's compute-unit count, picks the
-// workgroup tile, the split of the contraction across workgroups, the workspace it needs, and the
-// grid.  Deterministic for equal inputs.
+// split of the contraction across workgroups, the persistent grid, and the workspace it needs.
+// Deterministic for equal inputs.
 #pragma once
 
 #include <stddef.h>
@@ -11,21 +11,21 @@
 namespace fp8bq {
 
 enum SbMode : int { kSbBlock128 = 0, kSbColumn = 1 };
-// Kernel tile variants: workgroup tile (rows x columns of the output) and wave layout.
-enum Variant : int {
-  kVar128x128 = 0,  // 4 waves (2x2) of 64x64, two workgroups per CU
-  kVar256x256 = 1,  // 8 waves (2x4) of 128x64, one workgroup per CU
-};
 enum Op : int { kOpFprop = 0, kOpDgrad = 1, kOpWgrad = 2 };
 
+constexpr int kTileM = 128;         // output rows per work unit
+constexpr int kTileN = 128;         // output columns per work unit
+constexpr int kBlocksPerCu = 2;     // resident workgroups per CU (LDS and VGPR budget of the kernel)
+constexpr int kMaxSplit = 8;
+
 struct GemmPlan {
-  int tile_m = 128;   // output rows per workgroup
-  int tile_n = 128;   // output columns per workgroup
-  int variant = 0;    // kernel instance (tile shape / wave layout)
-  int split_k = 1;    // contraction split across workgroups (partials reduced in the workspace)
+  int tile_m = kTileM;
+  int tile_n = kTileN;
+  int split_k = 1;    // contraction split across work units (FP32 partials reduced afterwards)
   int64_t tiles_m = 0, tiles_n = 0;
-  int64_t grid = 0;   // workgroups launched
-  size_t ws_gemm = 0;       // workspace for split-K partial sums
+  int64_t units = 0;  // tiles x split
+  int64_t grid = 0;   // persistent workgroups launched
+  size_t ws_gemm = 0;       // workspace for split partial sums
   size_t ws_transpose = 0;  // workspace for dgrad's transposed weight codes
   size_t ws_total() const { return ws_transpose + ws_gemm; }
 };
@@ -33,5 +33,8 @@ struct GemmPlan {
 // M, N, K follow the C-ABI meaning for each op (fprop: Y[M,N] = X[M,K] W[N,K]^T; dgrad: dX[M,K] =
 // dY[M,N] W[N,K]; wgrad: dW[N,K] = dY[M,N]^T X[M,K]).
 GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count);
+
+// The split the cost model picks for an output of rows x cols with nkb contraction blocks.
+int choose_split(int64_t rows, int64_t cols, int64_t nkb, int64_t slots);
 
 }  // namespace fp8bq

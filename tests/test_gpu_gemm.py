@@ -254,3 +254,35 @@ def test_heavy_tailed_gradients_full_size():
     ncols, kcols = _sample(5632, 48, 6), _sample(2048, 48, 7)
     checked(run_wgrad(c["dY"], c["X"], E5, E4, ncols=ncols, kcols=kcols), "heavy-tail wgrad e5m2 x e4m3")
     checked(run_wgrad(c["dY"], c["X"], E4, E4, ncols=ncols, kcols=kcols), "heavy-tail wgrad e4m3 x e4m3")
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 1280), (200, 256, 1664), (128, 128, 4096)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_split_contraction(shape, out_dtype):
+    """Few output tiles and a long contraction: the planner splits the contraction across work
+    units (uneven splits included) and adds the FP32 partial sums in a fixed order."""
+    M, N, K = shape
+    X = synth.random_bf16((M, K), seed=81 + K, outliers=True)
+    W = synth.random_bf16((N, K), seed=82 + K, std=0.02)
+    split = fq.fp8bq_gemm_workspace_size(fq.OP_FPROP, M, N, K)
+    assert split > 0  # this shape takes the split path
+    checked(run_fprop(X, W, out_dtype=out_dtype), f"split fprop {shape}", out_dtype == torch.float32)
+    if M % 128 == 0:  # wgrad's output dimensions are feature counts (multiples of 128)
+        dY = synth.random_bf16((K, N), seed=83 + K, std=1e-3)
+        Xw = synth.random_bf16((K, M), seed=84 + K, outliers=True)
+        checked(run_wgrad(dY, Xw, out_dtype=out_dtype), f"split wgrad {shape}", out_dtype == torch.float32)
+    dYd = synth.random_bf16((M, K), seed=85 + K, std=1e-3)
+    Wd = synth.random_bf16((K, N), seed=86 + K, std=0.02)
+    checked(run_dgrad(dYd, Wd, out_dtype=out_dtype), f"split dgrad {shape}", out_dtype == torch.float32)
+
+
+def test_split_is_deterministic():
+    dY = synth.random_bf16((4096, 256), seed=91, std=1e-3).to(DEV)
+    X = synth.random_bf16((4096, 256), seed=92).to(DEV)
+    qdyt, sdyt = fq.quantize_act_128x1(dY)
+    qxt, sxt = fq.quantize_act_128x1(X)
+    a = fq.gemm_wgrad(qdyt, sdyt, qxt, sxt)
+    b = fq.gemm_wgrad(qdyt, sdyt, qxt, sxt)
+    torch.cuda.synchronize()
+    assert fq.fp8bq_gemm_workspace_size(fq.OP_WGRAD, 4096, 256, 256) > 0
+    assert torch.equal(a, b)
