@@ -30,26 +30,32 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// 16-byte chunk swizzle inside a 128-byte LDS row (conflict-free for 8- and 16-lane phases).
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// 16-byte chunk swizzle inside a 128-byte LDS row.  It depends on row % 16 only, so every 16-row
+// patch has the same per-lane read pattern (one pair of lane offsets serves all patches; the patch
+// position goes into the instruction's immediate offset).  Conflict-free for 8-lane phases (rows
+// 0-7 and 8-15 each get 8 distinct chunks) and for 16-lane phases over 64 banks (rows of equal
+// parity get distinct chunks).
+__device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
 
 constexpr int kGroupRows = 8;  // output tile rows per L2 group
 constexpr int kXcds = 8;
 
 // Bijective remap of the hardware workgroup id (dispatched round-robin over the XCDs) to a logical
 // tile id so each XCD processes a contiguous range of logical ids, then row-grouped tile ordering.
-__device__ __forceinline__ void tile_of(int64_t w, int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
-  const int64_t nblk = tiles_m * tiles_n;
-  const int64_t q8 = nblk / kXcds, r8 = nblk % kXcds;
-  const int64_t x = w % kXcds;
-  const int64_t L = x * q8 + (x < r8 ? x : r8) + w / kXcds;
-  const int64_t group = (int64_t)kGroupRows * tiles_n;
-  const int64_t gid = L / group;
-  const int64_t first = gid * kGroupRows;
-  const int64_t gsz = (tiles_m - first) < kGroupRows ? (tiles_m - first) : kGroupRows;
-  const int64_t rem = L - gid * group;
-  tm = first + rem % gsz;
-  tn = rem / gsz;
+// 32-bit arithmetic (the planner keeps tile and unit counts below 2^31); the results are wave-uniform
+// and kept in scalar registers.
+__device__ __forceinline__ void tile_of(uint32_t w, uint32_t tiles_m, uint32_t tiles_n, uint32_t& tm, uint32_t& tn) {
+  const uint32_t nblk = tiles_m * tiles_n;
+  const uint32_t q8 = nblk / kXcds, r8 = nblk % kXcds;
+  const uint32_t x = w % kXcds;
+  const uint32_t L = x * q8 + (x < r8 ? x : r8) + w / kXcds;
+  const uint32_t group = (uint32_t)kGroupRows * tiles_n;
+  const uint32_t gid = L / group;
+  const uint32_t first = gid * kGroupRows;
+  const uint32_t gsz = (tiles_m - first) < (uint32_t)kGroupRows ? (tiles_m - first) : (uint32_t)kGroupRows;
+  const uint32_t rem = L - gid * group;
+  tm = __builtin_amdgcn_readfirstlane(first + rem % gsz);
+  tn = __builtin_amdgcn_readfirstlane(rem / gsz);
 }
 
 template <int FA, int FB>
@@ -60,12 +66,19 @@ __device__ __forceinline__ v4f mfma_block(const v8i& bpatch, const v8i& apatch) 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bpatch, apatch, zero, FB, FA, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ v8i lds_patch(const uint8_t* tile, int row, int lane) {
-  const uint8_t* base = tile + row * 128;
-  const int c0 = 2 * (lane >> 4);
-  const int s = swz(row);
-  const v4i lo = *reinterpret_cast<const v4i*>(base + ((c0 ^ s) << 4));
-  const v4i hi = *reinterpret_cast<const v4i*>(base + (((c0 + 1) ^ s) << 4));
+// Byte offsets, within a 16-row patch, of the two 16-byte chunks lane reads: row lane % 16, logical
+// chunks 2*(lane/16) and 2*(lane/16)+1 (32 consecutive contraction bytes).
+struct PatchLane {
+  int lo, hi;
+};
+__device__ __forceinline__ PatchLane patch_lane(int lane) {
+  const int r = lane & 15, s = swz(r), c0 = 2 * (lane >> 4);
+  return PatchLane{r * 128 + ((c0 ^ s) << 4), r * 128 + (((c0 + 1) ^ s) << 4)};
+}
+// The MFMA operand of the 16-row patch starting at patch_base (a multiple of 16 rows into a tile).
+__device__ __forceinline__ v8i lds_patch(const uint8_t* patch_base, PatchLane pl) {
+  const v4i lo = *reinterpret_cast<const v4i*>(patch_base + pl.lo);
+  const v4i hi = *reinterpret_cast<const v4i*>(patch_base + pl.hi);
   v8i r = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   return r;
 }
@@ -83,23 +96,23 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* lds_base) {
 
 // One work unit: an output tile and the range of 128-long contraction blocks it sums.
 struct Unit {
-  int64_t m0, n0;
+  int m0, n0;
   int kb0, kb1, split;
 };
 
 template <int BM, int BN>
-__device__ __forceinline__ Unit unit_of(int64_t u, int64_t tiles_m, int64_t tiles_n, int nsplit, int nkb) {
-  const int64_t T = tiles_m * tiles_n;
-  const int64_t w = u % T;
+__device__ __forceinline__ Unit unit_of(uint32_t u, uint32_t tiles_m, uint32_t tiles_n, int nsplit, int nkb) {
+  const uint32_t T = tiles_m * tiles_n;
+  const uint32_t w = u % T;
   const int s = (int)(u / T);
-  int64_t tm, tn;
+  uint32_t tm, tn;
   tile_of(w, tiles_m, tiles_n, tm, tn);
   Unit r;
-  r.m0 = tm * BM;
-  r.n0 = tn * BN;
-  r.kb0 = (int)((int64_t)s * nkb / nsplit);
-  r.kb1 = (int)((int64_t)(s + 1) * nkb / nsplit);
-  r.split = s;
+  r.m0 = (int)tm * BM;
+  r.n0 = (int)tn * BN;
+  r.kb0 = __builtin_amdgcn_readfirstlane(s * nkb / nsplit);
+  r.kb1 = __builtin_amdgcn_readfirstlane((s + 1) * nkb / nsplit);
+  r.split = __builtin_amdgcn_readfirstlane(s);
   return r;
 }
 
@@ -128,7 +141,7 @@ struct StageMinBlocks {
 
 template <int OP, int BM, int BN, int WGM, int WGN, int NSTAGE, int SBM, int FA, int FB, int OUTF32>
 __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, NSTAGE>::value)) void gemm_tn_kernel(
-    GemmDesc d, int64_t tiles_m, int64_t tiles_n, int nsplit, float* __restrict__ partial) {
+    GemmDesc d, uint32_t tiles_m, uint32_t tiles_n, int nsplit, float* __restrict__ partial) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM;
   constexpr int WTN = BN / WGN;
@@ -157,46 +170,36 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   const int wm = wid / WGN, wn = wid % WGN;
   const int64_t M = d.M, N = d.N;
   const int nkb = (int)(d.K / kGroup);
-  const int64_t U = tiles_m * tiles_n * nsplit;
-  const int64_t G = gridDim.x;
+  const uint32_t U = tiles_m * tiles_n * (uint32_t)nsplit;
+  const uint32_t G = gridDim.x;
 
-  // tile-independent parts of this lane's load addresses
-  int arow[ACHUNKS / NW], acol[ACHUNKS / NW];
-#pragma unroll
-  for (int i = 0; i < ACHUNKS / NW; ++i) {
-    const int row = 8 * (wid + NW * i) + (lane >> 3);
-    arow[i] = row;
-    acol[i] = ((lane & 7) ^ swz(row)) * 16;
-  }
-  int brow[BCHUNKS / NW], bcol[BCHUNKS / NW];
-#pragma unroll
-  for (int i = 0; i < BCHUNKS / NW; ++i) {
-    const int row = 8 * (wid + NW * i) + (lane >> 3);
-    brow[i] = row;
-    bcol[i] = ((lane & 7) ^ swz(row)) * 16;
-  }
-  // load-side cursor: unit lu, block lkb, and this lane's sources for that unit
-  int64_t lu = blockIdx.x;
+  // load-side cursor: unit lu, block lkb, and this lane's sources for that unit as 32-bit offsets
+  // from workgroup-uniform bases (rows past the end are clamped; their results are never stored)
+  uint32_t lu = blockIdx.x;
   Unit L = unit_of<BM, BN>(lu, tiles_m, tiles_n, nsplit, nkb);
   int lkb = L.kb0;
   bool lmore = true;
-  const uint8_t* ga[ACHUNKS / NW];
-  const uint8_t* gb[BCHUNKS / NW];
+  const uint8_t* abase = d.a;
+  const uint8_t* bbase = d.b;
+  uint32_t aoff[ACHUNKS / NW], boff[BCHUNKS / NW];
   const float* gs[JPW];
   int64_t gsk[JPW];
   int lso[JPW];
   auto set_sources = [&](const Unit& u) {
+    abase = d.a + (int64_t)u.m0 * d.lda;
+    bbase = d.b + (int64_t)u.n0 * d.ldb;
+    const int64_t mleft = M - 1 - u.m0, nleft = N - 1 - u.n0;
 #pragma unroll
     for (int i = 0; i < ACHUNKS / NW; ++i) {
-      int64_t r = u.m0 + arow[i];
-      r = r < M ? r : M - 1;  // rows past the end are clamped; their results are never stored
-      ga[i] = d.a + r * d.lda + acol[i];
+      const int row = 8 * (wid + NW * i) + (lane >> 3);
+      const int64_t r = row < mleft ? row : mleft;
+      aoff[i] = (uint32_t)(r * d.lda) + (uint32_t)(((lane & 7) ^ swz(row)) * 16);
     }
 #pragma unroll
     for (int i = 0; i < BCHUNKS / NW; ++i) {
-      int64_t r = u.n0 + brow[i];
-      r = r < N ? r : N - 1;
-      gb[i] = d.b + r * d.ldb + bcol[i];
+      const int row = 8 * (wid + NW * i) + (lane >> 3);
+      const int64_t r = row < nleft ? row : nleft;
+      boff[i] = (uint32_t)(r * d.ldb) + (uint32_t)(((lane & 7) ^ swz(row)) * 16);
     }
     // scale jobs: job j < SAJOBS loads A scales of rows 64j..64j+63, the next SBJOBS the B scales;
     // wave w runs jobs w, w+NW, ...; missing jobs load a valid scale into the sink
@@ -232,10 +235,10 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   };
   auto load_next = [&](uint8_t* stg) {  // issue the loads of (lu, lkb) into stg, then advance
 #pragma unroll
-    for (int i = 0; i < ACHUNKS / NW; ++i) dma16(ga[i] + (int64_t)lkb * kGroup, stg + (wid + NW * i) * 1024);
+    for (int i = 0; i < ACHUNKS / NW; ++i) dma16(abase + aoff[i] + lkb * kGroup, stg + (wid + NW * i) * 1024);
 #pragma unroll
     for (int i = 0; i < BCHUNKS / NW; ++i)
-      dma16(gb[i] + (int64_t)lkb * kGroup, stg + BM * 128 + (wid + NW * i) * 1024);
+      dma16(bbase + boff[i] + lkb * kGroup, stg + BM * 128 + (wid + NW * i) * 1024);
 #pragma unroll
     for (int q = 0; q < JPW; ++q) dma4(gs[q] + (int64_t)lkb * gsk[q], stg + lso[q]);
     if (++lkb == L.kb1) {
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   if (lu >= U) return;  // (the grid never exceeds the unit count)
   set_sources(L);
   // compute-side cursor
-  int64_t cu = lu;
+  uint32_t cu = lu;
   Unit C = L;
   int ckb = C.kb0;
 
@@ -279,6 +282,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   }
   __syncthreads();
 
+  const PatchLane pl = patch_lane(lane);
   int rd = 0, wr = NSTAGE - 1;  // ring slots read / refilled this iteration
   while (true) {
     const uint8_t* stage = smem + rd * STAGE;
@@ -291,60 +295,60 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
     float sa_[MI];
 #pragma unroll
     for (int i = 0; i < MI; ++i) sa_[i] = ssa[wm * WTM + 16 * i + (lane & 15)];
-    v8i bp[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) bp[j] = lds_patch(stage + BM * 128, wn * WTN + 16 * j + (lane & 15), lane);
 
-    // MFMA u is issued while the fold of MFMA u-LAG runs on the VALU, so the matrix pipe and the
-    // vector pipe overlap within the wave.  A patches are read as they are needed.
+    // The side with fewer 16-row patches stays in registers for the whole block; the other side is
+    // streamed one patch at a time (MFMA order: streamed patch outer).  MFMA u is issued while the
+    // fold of MFMA u-LAG runs on the VALU, so the matrix pipe and the vector pipe overlap.
+    constexpr bool STREAM_B = NI > MI;
+    constexpr int NOUT = STREAM_B ? NI : MI;  // streamed patches
+    constexpr int NIN = STREAM_B ? MI : NI;   // resident patches
     constexpr int NTILE = MI * NI;
     constexpr int LAG = 2;
+    const uint8_t* atile = stage + wm * WTM * 128;
+    const uint8_t* btile = stage + BM * 128 + wn * WTN * 128;
+    v8i res[NIN], str[NOUT];
+#pragma unroll
+    for (int k = 0; k < NIN; ++k)
+      res[k] = STREAM_B ? lds_patch(atile + 16 * k * 128, pl) : lds_patch(btile + 16 * k * 128, pl);
     v4f p[NTILE];
-    v8i ap[MI];
+    float sbv = 0.0f;
+    v4f sbc[NI];
     if constexpr (SBM == kSbBlock128) {
-      const float sbv = ssb[(wn * WTN) / kGroup];
-      float sc[MI];
-#pragma unroll
-      for (int i = 0; i < MI; ++i) sc[i] = sa_[i] * sbv;
-#pragma unroll
-      for (int u = 0; u < NTILE + LAG; ++u) {
-        if (u < NTILE) {
-          if (u % NI == 0) ap[u / NI] = lds_patch(stage, wm * WTM + 16 * (u / NI) + (lane & 15), lane);
-          p[u] = mfma_block<FA, FB>(bp[u % NI], ap[u / NI]);
-        }
-        if (u >= LAG) {
-          const int v = u - LAG, i = v / NI, j = v % NI;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[v][r], sc[i], acc[i][j][r]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NTILE; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then up to five VALU ops
-      }
+      sbv = ssb[(wn * WTN) / kGroup];
     } else {
-      v4f sbc[NI];
 #pragma unroll
       for (int j = 0; j < NI; ++j)
         sbc[j] = *reinterpret_cast<const v4f*>(ssb + wn * WTN + 16 * j + 4 * (lane >> 4));
+    }
 #pragma unroll
-      for (int u = 0; u < NTILE + LAG; ++u) {
-        if (u < NTILE) {
-          if (u % NI == 0) ap[u / NI] = lds_patch(stage, wm * WTM + 16 * (u / NI) + (lane & 15), lane);
-          p[u] = mfma_block<FA, FB>(bp[u % NI], ap[u / NI]);
-        }
-        if (u >= LAG) {
-          const int v = u - LAG, i = v / NI, j = v % NI;
+    for (int u = 0; u < NTILE + LAG; ++u) {
+      if (u < NTILE) {
+        const int o = u / NIN, k = u % NIN;
+        if (k == 0) str[o] = STREAM_B ? lds_patch(btile + 16 * o * 128, pl) : lds_patch(atile + 16 * o * 128, pl);
+        p[u] = STREAM_B ? mfma_block<FA, FB>(str[o], res[k]) : mfma_block<FA, FB>(res[k], str[o]);
+      }
+      if (u >= LAG) {
+        const int v = u - LAG, o = v / NIN, k = v % NIN;
+        const int i = STREAM_B ? k : o, j = STREAM_B ? o : k;
+        if constexpr (SBM == kSbBlock128) {
+          const float sc = sa_[i] * sbv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[v][r], sc, acc[i][j][r]);
+        } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[v][r], sa_[i] * sbc[j][r], acc[i][j][r]);
         }
       }
+    }
+    // schedule: the resident patches and the first streamed patch are read first; then each MFMA is
+    // followed by its fold, and the two reads of the next streamed patch ride on the first two
+    // MFMAs of the current one (one patch of read-ahead bounds the live registers)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NIN + 2, 0);
 #pragma unroll
-      for (int u = 0; u < NTILE; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
-      }
+    for (int u = 0; u < NTILE; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                               // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, SBM == kSbBlock128 ? 5 : 9, 0);    // then a fold
+      if (u % NIN < 2 && u / NIN + 1 < NOUT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     // the slot read next iteration must have landed before anyone reads it after the barrier; the
     // loads issued this iteration (if any) may stay in flight
@@ -360,10 +364,10 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
     if (++ckb < C.kb1) continue;
 
     // unit finished: write the tile (or its partial sum) and move on
-    const int64_t ncol_wave = C.n0 + wn * WTN;
+    const int64_t ncol_wave = (int64_t)C.n0 + wn * WTN;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int64_t m = C.m0 + wm * WTM + 16 * i + (lane & 15);
+      const int64_t m = (int64_t)C.m0 + wm * WTM + 16 * i + (lane & 15);
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int64_t n = ncol_wave + 16 * j + 4 * (lane >> 4);
@@ -412,12 +416,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 template <int OP, int BM, int BN, int WGM, int WGN, int NSTAGE, int SBM, int FA, int FB, int OUTF32>
 static hipError_t launch_variant(const GemmDesc& d, const GemmPlan& p, float* partial, hipStream_t st) {
   hipLaunchKernelGGL((gemm_tn_kernel<OP, BM, BN, WGM, WGN, NSTAGE, SBM, FA, FB, OUTF32>), dim3((unsigned)p.grid),
-                     dim3(WGM * WGN * 64), 0, st, d, p.tiles_m, p.tiles_n, p.split_k, partial);
+                     dim3(WGM * WGN * 64), 0, st, d, (uint32_t)p.tiles_m, (uint32_t)p.tiles_n, p.split_k, partial);
   return hipGetLastError();
 }
 
 template <int OP, int SBM, int FA, int FB, int OUTF32>
 static hipError_t launch_fmt(const GemmDesc& d, const GemmPlan& p, float* partial, hipStream_t st) {
+  if (p.tile_m == 256) return launch_variant<OP, 256, 256, 2, 4, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
   return launch_variant<OP, 128, 128, 2, 2, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
 }
 
