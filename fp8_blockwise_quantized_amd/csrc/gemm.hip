@@ -422,8 +422,11 @@ static hipError_t launch_variant(const GemmDesc& d, const GemmPlan& p, float* pa
 
 template <int OP, int SBM, int FA, int FB, int OUTF32>
 static hipError_t launch_fmt(const GemmDesc& d, const GemmPlan& p, float* partial, hipStream_t st) {
-  if (p.tile_m == 256) return launch_variant<OP, 256, 256, 2, 4, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
-  return launch_variant<OP, 128, 128, 2, 2, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
+  switch (p.shape) {
+    case k128x256: return launch_variant<OP, 128, 256, 2, 4, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
+    case k256x128: return launch_variant<OP, 256, 128, 4, 2, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
+    default: return launch_variant<OP, 128, 128, 2, 2, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
+  }
 }
 
 template <int OP, int SBM, int OUTF32>

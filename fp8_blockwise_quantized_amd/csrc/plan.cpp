@@ -1,7 +1,19 @@
 // Tile / launch planner (pure host C++).
 #include "plan.hpp"
 
+#include <cstdlib>
+
 namespace fp8bq {
+
+// FP8BQ_GEMM_TILE=<0|1|2> forces a tile shape (tuning aid); read once.
+static int forced_shape() {
+  static const int v = [] {
+    const char* e = std::getenv("FP8BQ_GEMM_TILE");
+    const int x = e ? std::atoi(e) : -1;
+    return (x >= 0 && x <= 2) ? x : -1;
+  }();
+  return v;
+}
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -9,8 +21,8 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // (measured: two 128x128 workgroups per CU), and a split adds a pass that writes and re-reads
 // split x rows x cols FP32 partials and writes the output (~5 TB/s effective).  Splitting pays off
 // only when the tiles alone leave workgroup slots idle.
-int choose_split(int64_t rows, int64_t cols, int64_t nkb, int64_t slots) {
-  const int64_t tiles = cdiv(rows, kTileM) * cdiv(cols, kTileN);
+int choose_split(int64_t rows, int64_t cols, int64_t nkb, int64_t slots, int tile_m, int tile_n) {
+  const int64_t tiles = cdiv(rows, tile_m) * cdiv(cols, tile_n);
   int best = 1;
   double best_us = 0.0;
   for (int s = 1; s <= kMaxSplit; ++s) {
@@ -38,11 +50,14 @@ GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count) {
   } else {
     rows = N; cols = K; contraction = M;
   }
-  const int64_t slots = (int64_t)(cu_count > 0 ? cu_count : 256) * kBlocksPerCu;
+  p.shape = forced_shape() >= 0 ? forced_shape() : k128x128;
+  p.tile_m = tile_rows(p.shape);
+  p.tile_n = tile_cols(p.shape);
+  const int64_t slots = (int64_t)(cu_count > 0 ? cu_count : 256) * blocks_per_cu(p.shape);
   const int64_t nkb = contraction / 128;
   p.tiles_m = cdiv(rows, p.tile_m);
   p.tiles_n = cdiv(cols, p.tile_n);
-  p.split_k = (rows > 0 && cols > 0 && nkb > 0) ? choose_split(rows, cols, nkb, slots) : 1;
+  p.split_k = (rows > 0 && cols > 0 && nkb > 0) ? choose_split(rows, cols, nkb, slots, p.tile_m, p.tile_n) : 1;
   p.units = p.tiles_m * p.tiles_n * p.split_k;
   // persistent grid: one workgroup per slot (a multiple of 8, so each workgroup stays on one XCD's
   // range of tiles), or one per unit when there are fewer units

@@ -13,14 +13,18 @@ namespace fp8bq {
 enum SbMode : int { kSbBlock128 = 0, kSbColumn = 1 };
 enum Op : int { kOpFprop = 0, kOpDgrad = 1, kOpWgrad = 2 };
 
-constexpr int kTileM = 128;         // output rows per work unit
-constexpr int kTileN = 128;         // output columns per work unit
-constexpr int kBlocksPerCu = 2;     // resident workgroups per CU (LDS and VGPR budget of the kernel)
+// Workgroup tile shapes (output rows x columns of one work unit).  All use 64x64 wave tiles:
+//   k128x128: 4 waves, two workgroups per CU;  k128x256 / k256x128: 8 waves, one workgroup per CU.
+enum TileShape : int { k128x128 = 0, k128x256 = 1, k256x128 = 2 };
+inline int tile_rows(int shape) { return shape == k256x128 ? 256 : 128; }
+inline int tile_cols(int shape) { return shape == k128x256 ? 256 : 128; }
+inline int blocks_per_cu(int shape) { return shape == k128x128 ? 2 : 1; }
 constexpr int kMaxSplit = 8;
 
 struct GemmPlan {
-  int tile_m = kTileM;
-  int tile_n = kTileN;
+  int shape = k128x128;
+  int tile_m = 128;
+  int tile_n = 128;
   int split_k = 1;    // contraction split across work units (FP32 partials reduced afterwards)
   int64_t tiles_m = 0, tiles_n = 0;
   int64_t units = 0;  // tiles x split
@@ -35,6 +39,6 @@ struct GemmPlan {
 GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count);
 
 // The split the cost model picks for an output of rows x cols with nkb contraction blocks.
-int choose_split(int64_t rows, int64_t cols, int64_t nkb, int64_t slots);
+int choose_split(int64_t rows, int64_t cols, int64_t nkb, int64_t slots, int tile_m, int tile_n);
 
 }  // namespace fp8bq

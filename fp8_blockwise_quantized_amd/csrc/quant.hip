@@ -19,13 +19,27 @@
 
 namespace fp8bq {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Plain (temporal) global accesses: inputs are often read again (an activation feeds both the 1x128
+// and the 128x1 pass) and codes are read next by the GEMM, so letting them stay in the 256 MB
+// Infinity Cache pays; non-temporal hints measured faster only on tensors larger than that cache.
+__device__ __forceinline__ void store_codes8(uint8_t* p, uint2 w) {
+  *reinterpret_cast<u32x2*>(p) = (u32x2){w.x, w.y};
+}
+__device__ __forceinline__ void store_codes16(uint8_t* p, uint4 w) {
+  *reinterpret_cast<u32x4*>(p) = (u32x4){w.x, w.y, w.z, w.w};
+}
+
 // Load 8 consecutive input elements (16 bytes of BF16 or 32 bytes of FP32) as fp32.
 template <typename TIn>
 struct Load8;
 template <>
 struct Load8<uint16_t> {
   static __device__ __forceinline__ void run(const uint16_t* p, float (&v)[8]) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
     v[0] = bf16lo(w.x); v[1] = bf16hi(w.x);
     v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
     v[4] = bf16lo(w.z); v[5] = bf16hi(w.z);
@@ -35,8 +49,8 @@ struct Load8<uint16_t> {
 template <>
 struct Load8<float> {
   static __device__ __forceinline__ void run(const float* p, float (&v)[8]) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *(reinterpret_cast<const float4*>(p) + 1);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *(reinterpret_cast<const f32x4*>(p) + 1);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
@@ -89,43 +103,43 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const TIn* __restrict_
     const float sc = group_scale<FMT>(amax);
     const float rc = 1.0f / sc;
     if (r < R) {
-      const uint2 w = quant8<FMT>(v[p], sc, rc);
-      *reinterpret_cast<uint2*>(q + r * ldq + col) = w;
+      store_codes8(q + r * ldq + col, quant8<FMT>(v[p], sc, rc));
       if (l16 == 0) s[g * lds + r] = sc;
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// 128x1: grid (ceil(C/64), R/128).  A block owns rows 128*rb .. +127 and 64 columns.  Thread t
-// holds a 4-row x 8-column patch (rows 4*(t>>3)+0..3, columns 8*(t&7)+0..7).  Column amax goes
-// through LDS; codes are packed 4 rows to a dword, staged transposed in LDS, and written as 16-byte
-// runs along the token axis.
+// 128x1: grid (ceil(C/128), R/128).  A block owns rows 128*rb .. +127 and 128 columns (256-byte row
+// segments of BF16).  Thread t holds an 8-row x 8-column patch (rows 8*(t>>4)+0..7, columns
+// 8*(t&15)+0..7), i.e. 8 independent 16-byte loads.  Column amax goes through LDS; each column's
+// 8 codes are packed into two dwords, staged transposed in LDS, and written as 16-byte runs along
+// the token axis (128 contiguous bytes per column).
 // ---------------------------------------------------------------------------------------------
-constexpr int kQtCols = 64;
-constexpr int kQtStride = 33;  // dwords per staged column (32 + 1 pad against bank conflicts)
+constexpr int kQtCols = 128;
+constexpr int kQtStride = 34;  // dwords per staged column (32 + 2 pad; even for 8-byte stores)
 
 template <typename TIn, int FMT>
 __global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict__ x, int64_t C, int64_t ldx,
                                                           uint8_t* __restrict__ qt, int64_t ldqt,
                                                           float* __restrict__ st, int64_t ldst) {
-  __shared__ float red[32][kQtCols + 1];
+  __shared__ float red[16][kQtCols + 1];
   __shared__ float ssc[kQtCols];
   __shared__ float src[kQtCols];
-  __shared__ uint32_t tileT[kQtCols * kQtStride];
+  __shared__ __attribute__((aligned(8))) uint32_t tileT[kQtCols * kQtStride];
 
   const int t = threadIdx.x;
-  const int cc = t & 7;
-  const int rg = t >> 3;
+  const int cc = t & 15;
+  const int rg = t >> 4;
   const int64_t rb = blockIdx.y;
   const int64_t c0 = (int64_t)blockIdx.x * kQtCols;
   const int64_t col = c0 + 8 * cc;
   const bool cvalid = col < C;  // C % 8 == 0, so a chunk is all in or all out
 
-  float v[4][8];
+  float v[8][8];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int64_t r = rb * kGroup + 4 * rg + p;
+  for (int p = 0; p < 8; ++p) {
+    const int64_t r = rb * kGroup + 8 * rg + p;
     if (cvalid) {
       Load8<TIn>::run(x + r * ldx + col, v[p]);
     } else {
@@ -136,16 +150,15 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict_
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float m = __builtin_fabsf(v[0][i]);
-    m = __builtin_fmaxf(m, __builtin_fabsf(v[1][i]));
-    m = __builtin_fmaxf(m, __builtin_fabsf(v[2][i]));
-    m = __builtin_fmaxf(m, __builtin_fabsf(v[3][i]));
+#pragma unroll
+    for (int p = 1; p < 8; ++p) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
     red[rg][8 * cc + i] = m;
   }
   __syncthreads();
   if (t < kQtCols) {
     float m = 0.0f;
-#pragma unroll 8
-    for (int k = 0; k < 32; ++k) m = __builtin_fmaxf(m, red[k][t]);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = __builtin_fmaxf(m, red[k][t]);
     const float sc = group_scale<FMT>(m);
     ssc[t] = sc;
     src[t] = 1.0f / sc;
@@ -156,21 +169,20 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict_
   for (int i = 0; i < 8; ++i) {
     const int c = 8 * cc + i;
     const float sc = ssc[c], rc = src[c];
-    const float y0 = clamp_fmt<FMT>(div_by_scale(v[0][i], sc, rc));
-    const float y1 = clamp_fmt<FMT>(div_by_scale(v[1][i], sc, rc));
-    const float y2 = clamp_fmt<FMT>(div_by_scale(v[2][i], sc, rc));
-    const float y3 = clamp_fmt<FMT>(div_by_scale(v[3][i], sc, rc));
-    tileT[c * kQtStride + rg] = pack4<FMT>(y0, y1, y2, y3);
+    float y[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) y[p] = clamp_fmt<FMT>(div_by_scale(v[p][i], sc, rc));
+    const uint2 w = make_uint2(pack4<FMT>(y[0], y[1], y[2], y[3]), pack4<FMT>(y[4], y[5], y[6], y[7]));
+    *reinterpret_cast<uint2*>(tileT + c * kQtStride + 2 * rg) = w;
   }
   __syncthreads();
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < 4; ++pass) {
     const int c = (t >> 3) + 32 * pass;
     const int ch = t & 7;
     if (c0 + c < C) {
       const uint32_t* src4 = tileT + c * kQtStride + 4 * ch;
-      const uint4 w = make_uint4(src4[0], src4[1], src4[2], src4[3]);
-      *reinterpret_cast<uint4*>(qt + (c0 + c) * ldqt + rb * kGroup + 16 * ch) = w;
+      store_codes16(qt + (c0 + c) * ldqt + rb * kGroup + 16 * ch, make_uint4(src4[0], src4[1], src4[2], src4[3]));
     }
   }
 }
@@ -207,8 +219,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const TIn* __restric
   const float rc = 1.0f / sc;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    const uint2 c = quant8<FMT>(v[p], sc, rc);
-    *reinterpret_cast<uint2*>(q + (nb * kGroup + rsub + 16 * p) * ldq + col) = c;
+    store_codes8(q + (nb * kGroup + rsub + 16 * p) * ldq + col, quant8<FMT>(v[p], sc, rc));
   }
   if (t == 0) s[nb * lds + kb] = sc;
 }
