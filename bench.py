@@ -13,7 +13,7 @@ i.e. 20 quantize passes and 12 GEMMs, all E4M3, BF16 in and out, inputs resident
 Prints ONE JSON line on stdout.  `value` = GEMM FLOPs of the step / wall time of the step (the
 quantize passes are inside the timed step).  `breakdown` holds per-product TFLOP/s and per-pass GB/s
 from HIP events recorded on the launch stream; `roofline` is for the dominant GEMM kernel;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same path (first 2048 tokens).
+`cpu_baseline` times the CPU oracle on a bounded sample of the same path (first 4096 tokens).
 """
 
 import argparse
@@ -42,14 +42,17 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", choices=["decoder", "linear", "sweep"], default="decoder")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-tokens", type=int, default=2048)
+    p.add_argument("--cpu-tokens", type=int, default=4096)
+    p.add_argument("--calibrate", action="store_true",
+                   help="first run one plain elementwise kernel over 256 MiB in / 256 MiB out, so a "
+                        "rocprofv3 counter run can scale FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
 
 
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the GEMMs would shard by tokens, with one all-reduce of dW per step).", file=sys.stderr)
         sys.exit(2)
 
@@ -65,6 +68,13 @@ def main():
     fq.lib()  # fail loudly if the HIP library is not built
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.calibrate:
+        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.neg(a, out=b)  # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        del a, b
 
     if args.workload == "decoder":
         ops, bufs, desc = build_decoder(torch, fq, synth, dev)
@@ -290,15 +300,15 @@ def summarize(ops, dur_ms):
     return out
 
 
-# Kernel instance names per product (gemm_tn_kernel<OP, BM, BN, waves_m, waves_n, scale mode, fmtA,
-# fmtB, f32 out>); a product's events bracket only its GEMM kernel except dgrad, whose call also runs
-# the weight-code transpose.
+# Kernel instance names per product as profilers print them (gemm_tn_kernel<OP, BM, BN, waves_m,
+# waves_n, LDS stages, scale mode, fmtA, fmtB, f32 out>).  Only fprop's call launches exactly one
+# kernel on the decoder workload (dgrad's also transposes the weight codes, and the split wgrads add
+# a reduction pass), so its events bracket the kernel alone: the roofline is taken on it.
 GEMM_KERNEL = {
-    "fprop": "gemm_tn_kernel<0, 128, 128, 2, 2, 0, 0, 0, 0>",
-    "dgrad": "gemm_tn_kernel<1, 128, 128, 2, 2, 0, 0, 0, 0>",
-    "wgrad": "gemm_tn_kernel<2, 128, 128, 2, 2, 1, 0, 0, 0>",
+    "fprop": "void fp8bq::gemm_tn_kernel<0, 128, 128, 2, 2, 2, 0, 0, 0, 0>(fp8bq::GemmDesc, unsigned int, "
+             "unsigned int, int, float*)",
 }
-ISOLATED = ("fprop", "wgrad")
+ISOLATED = ("fprop",)
 
 
 def _traffic(kind):
@@ -318,8 +328,9 @@ def _traffic(kind):
 
 
 def roofline(ops, dur_ms):
-    """Dominant GEMM kernel (largest total time among products whose events bracket only the GEMM
-    kernel): achieved = its algorithmic FLOPs per launch / its mean launch duration."""
+    """The fprop GEMM kernel (the GEMMs are the dominant cost; fprop's calls launch that one kernel):
+    achieved = its algorithmic FLOPs per launch / its mean launch duration (HIP events on the launch
+    stream), averaged over the step's launches."""
     best = None
     for kind in ISOLATED:
         sel = [(o, d) for o, d in zip(ops, dur_ms) if o["kind"] == kind]
