@@ -95,11 +95,12 @@ __device__ __forceinline__ float wave_max(float v) {
   return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
 }
 
-// Round-to-nearest-even fp32 -> bf16 pair (lowers to v_cvt_pk_bf16_f32 on gfx950).
+// Round-to-nearest-even fp32 -> bf16 pair, lo in the low half: one v_cvt_pk_bf16_f32 on gfx950.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 }  // namespace fp8bq

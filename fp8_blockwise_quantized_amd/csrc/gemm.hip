@@ -21,6 +21,8 @@
 // kb+1 (and its scales) are issued before the MFMAs of block kb.  Workgroup ids are remapped so that
 // each XCD (its own L2) works on a contiguous, row-grouped region of output tiles.
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -233,24 +235,46 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
       }
     }
   };
-  auto load_next = [&](uint8_t* stg) {  // issue the loads of (lu, lkb) into stg, then advance
-#pragma unroll
-    for (int i = 0; i < ACHUNKS / NW; ++i) dma16(abase + aoff[i] + lkb * kGroup, stg + (wid + NW * i) * 1024);
-#pragma unroll
-    for (int i = 0; i < BCHUNKS / NW; ++i)
-      dma16(bbase + boff[i] + lkb * kGroup, stg + BM * 128 + (wid + NW * i) * 1024);
-#pragma unroll
-    for (int q = 0; q < JPW; ++q) dma4(gs[q] + (int64_t)lkb * gsk[q], stg + lso[q]);
-    if (++lkb == L.kb1) {
-      lu += G;
-      if (lu < U) {
+  // Issue the loads of (lu, lkb) into stg, then advance the cursor.  Once every block has been
+  // issued the cursor stays on the last one and further calls load it again into the free slot:
+  // every call issues exactly LOADS loads, so one constant s_waitcnt serves every iteration and no
+  // branch separates the MFMAs from their folds.  (A slot refilled that way is never read: it would
+  // hold a block past the end.)
+  // load number i (0 <= i < LOADS) of this wave for the current cursor position
+  auto issue_load = [&](int i, uint8_t* stg) {
+    if (i < ACHUNKS / NW) {
+      dma16(abase + aoff[i] + lkb * kGroup, stg + (wid + NW * i) * 1024);
+    } else if (i < ACHUNKS / NW + BCHUNKS / NW) {
+      const int b = i - ACHUNKS / NW;
+      dma16(bbase + boff[b] + lkb * kGroup, stg + BM * 128 + (wid + NW * b) * 1024);
+    } else {
+      const int q = i - ACHUNKS / NW - BCHUNKS / NW;
+      dma4(gs[q] + (int64_t)lkb * gsk[q], stg + lso[q]);
+    }
+  };
+  auto advance = [&]() {
+    if (lmore && ++lkb == L.kb1) {
+      if (lu + G < U) {
+        lu += G;
         L = unit_of<BM, BN>(lu, tiles_m, tiles_n, nsplit, nkb);
         lkb = L.kb0;
         set_sources(L);
       } else {
+        lkb = L.kb1 - 1;
         lmore = false;
       }
     }
+  };
+  auto load_next = [&](uint8_t* stg) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) issue_load(i, stg);
+    advance();
+  };
+  // Every wave waits for its own loads of the slot read next, then the barrier makes them (and the
+  // end of all reads of the slot refilled next) visible workgroup-wide.  No memory fence: loads of
+  // the newer stages stay in flight across the barrier.
+  auto stage_barrier = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NSTAGE - 2) * LOADS) : "memory");
   };
 
   v4f acc[MI][NI];
@@ -266,51 +290,46 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   Unit C = L;
   int ckb = C.kb0;
 
-  // prologue: up to NSTAGE-1 blocks in flight, the first landed
-  int issued = 0;
+  // prologue: NSTAGE-1 blocks in flight, the first landed
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s) {
-    if (lmore) {
-      load_next(smem + s * STAGE);
-      ++issued;
-    }
-  }
-  if (issued == NSTAGE - 1) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * LOADS) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();
+  for (int s = 0; s < NSTAGE - 1; ++s) load_next(smem + s * STAGE);
+  stage_barrier();
 
   const PatchLane pl = patch_lane(lane);
   int rd = 0, wr = NSTAGE - 1;  // ring slots read / refilled this iteration
   while (true) {
     const uint8_t* stage = smem + rd * STAGE;
-    // slot wr was last read in the previous iteration, before its barrier: refill it now
-    const bool refill = lmore;
-    if (refill) load_next(smem + wr * STAGE);
-
-    const float* ssa = reinterpret_cast<const float*>(stage + SA_OFF);
-    const float* ssb = reinterpret_cast<const float*>(stage + SB_OFF);
-    float sa_[MI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i) sa_[i] = ssa[wm * WTM + 16 * i + (lane & 15)];
+    uint8_t* refill = smem + wr * STAGE;  // last read in the previous iteration, before its barrier
 
     // The side with fewer 16-row patches stays in registers for the whole block; the other side is
-    // streamed one patch at a time (MFMA order: streamed patch outer).  MFMA u is issued while the
-    // fold of MFMA u-LAG runs on the VALU, so the matrix pipe and the vector pipe overlap.
+    // streamed one patch at a time (MFMA order: streamed patch outer), the next patch read while the
+    // current one's MFMAs run.  Step u issues MFMA u and the fold of MFMA u-LAG, whose result is then
+    // complete, plus one of this wave's loads of the refilled slot while there are any left; a
+    // scheduling fence closes every step, so the matrix pipe never waits on a fold and at most LAG+1
+    // MFMA results are live.  The block's first reads are ordered by first use, so the first MFMA
+    // waits only for its own two patches.
     constexpr bool STREAM_B = NI > MI;
     constexpr int NOUT = STREAM_B ? NI : MI;  // streamed patches
     constexpr int NIN = STREAM_B ? MI : NI;   // resident patches
     constexpr int NTILE = MI * NI;
     constexpr int LAG = 2;
+    static_assert(LOADS <= NTILE + LAG, "every load needs a step");
     const uint8_t* atile = stage + wm * WTM * 128;
     const uint8_t* btile = stage + BM * 128 + wn * WTN * 128;
+    auto streamed = [&](int o) {
+      return STREAM_B ? lds_patch(btile + 16 * o * 128, pl) : lds_patch(atile + 16 * o * 128, pl);
+    };
+    auto resident = [&](int k) {
+      return STREAM_B ? lds_patch(atile + 16 * k * 128, pl) : lds_patch(btile + 16 * k * 128, pl);
+    };
+    const float* ssa = reinterpret_cast<const float*>(stage + SA_OFF);
+    const float* ssb = reinterpret_cast<const float*>(stage + SB_OFF);
     v8i res[NIN], str[NOUT];
+    str[0] = streamed(0);
+    res[0] = resident(0);
+    float sa_[MI];
 #pragma unroll
-    for (int k = 0; k < NIN; ++k)
-      res[k] = STREAM_B ? lds_patch(atile + 16 * k * 128, pl) : lds_patch(btile + 16 * k * 128, pl);
-    v4f p[NTILE];
+    for (int i = 0; i < MI; ++i) sa_[i] = ssa[wm * WTM + 16 * i + (lane & 15)];
     float sbv = 0.0f;
     v4f sbc[NI];
     if constexpr (SBM == kSbBlock128) {
@@ -321,12 +340,17 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
         sbc[j] = *reinterpret_cast<const v4f*>(ssb + wn * WTN + 16 * j + 4 * (lane >> 4));
     }
 #pragma unroll
+    for (int k = 1; k < NIN; ++k) res[k] = resident(k);
+    v4f p[NTILE];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
     for (int u = 0; u < NTILE + LAG; ++u) {
       if (u < NTILE) {
         const int o = u / NIN, k = u % NIN;
-        if (k == 0) str[o] = STREAM_B ? lds_patch(btile + 16 * o * 128, pl) : lds_patch(atile + 16 * o * 128, pl);
+        if (k == 0 && o + 1 < NOUT) str[o + 1] = streamed(o + 1);
         p[u] = STREAM_B ? mfma_block<FA, FB>(str[o], res[k]) : mfma_block<FA, FB>(res[k], str[o]);
       }
+      if (u < LOADS) issue_load(u, refill);
       if (u >= LAG) {
         const int v = u - LAG, o = v / NIN, k = v % NIN;
         const int i = STREAM_B ? k : o, j = STREAM_B ? o : k;
@@ -339,59 +363,73 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
           for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[v][r], sa_[i] * sbc[j][r], acc[i][j][r]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // schedule: the resident patches and the first streamed patch are read first; then each MFMA is
-    // followed by its fold, and the two reads of the next streamed patch ride on the first two
-    // MFMAs of the current one (one patch of read-ahead bounds the live registers)
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NIN + 2, 0);
+    // keep the folds in the step sequence (not sunk past the cursor update's branches)
 #pragma unroll
-    for (int u = 0; u < NTILE; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                               // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, SBM == kSbBlock128 ? 5 : 9, 0);    // then a fold
-      if (u % NIN < 2 && u / NIN + 1 < NOUT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) asm volatile("" : "+v"(acc[i][j]));
+    advance();
     // the slot read next iteration must have landed before anyone reads it after the barrier; the
-    // loads issued this iteration (if any) may stay in flight
-    if (refill) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSTAGE - 2) * LOADS) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();
+    // loads issued this iteration may stay in flight
+    stage_barrier();
     rd = rd + 1 == NSTAGE ? 0 : rd + 1;
     wr = wr + 1 == NSTAGE ? 0 : wr + 1;
 
     if (++ckb < C.kb1) continue;
 
-    // unit finished: write the tile (or its partial sum) and move on
-    const int64_t ncol_wave = (int64_t)C.n0 + wn * WTN;
+    // unit finished: write the tile (or its partial sum) and move on.  Lane l holds row l % 16 and
+    // columns 4 * (l / 16) .. +3 of each 16x16 patch; only tiles that reach past M or N check bounds.
+    {
+      const int64_t mrow = (int64_t)C.m0 + wm * WTM + (lane & 15);
+      const int64_t ncol = (int64_t)C.n0 + wn * WTN + 4 * (lane >> 4);
+      const bool full = (int64_t)C.m0 + BM <= M && (int64_t)C.n0 + BN <= N;
+      auto write = [&](auto checked) {
+        constexpr bool CHK = decltype(checked)::value;
+        if (nsplit > 1 || OUTF32) {
+          const int64_t ldc = nsplit > 1 ? N : d.ldc;
+          float* c0 = (nsplit > 1 ? partial + (int64_t)C.split * M * N : reinterpret_cast<float*>(d.c)) + mrow * ldc + ncol;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int64_t m = (int64_t)C.m0 + wm * WTM + 16 * i + (lane & 15);
+          for (int i = 0; i < MI; ++i) {
+            float* ci = c0 + 16 * i * ldc;
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int64_t n = ncol_wave + 16 * j + 4 * (lane >> 4);
-        if (m < M && n < N) {
-          if (nsplit > 1) {
-            float* c = partial + ((int64_t)C.split * M + m) * N + n;
-            *reinterpret_cast<v4f*>(c) = acc[i][j];
-          } else if constexpr (OUTF32) {
-            float* c = reinterpret_cast<float*>(d.c) + m * d.ldc + n;
-            *reinterpret_cast<v4f*>(c) = acc[i][j];
-          } else {
-            uint16_t* c = reinterpret_cast<uint16_t*>(d.c) + m * d.ldc + n;
-            *reinterpret_cast<uint2*>(c) =
-                make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+            for (int j = 0; j < NI; ++j) {
+              if (CHK && !(mrow + 16 * i < M && ncol + 16 * j < N)) continue;
+              *reinterpret_cast<v4f*>(ci + 16 * j) = acc[i][j];
+            }
+          }
+        } else {
+          uint16_t* c0 = reinterpret_cast<uint16_t*>(d.c) + mrow * d.ldc + ncol;
+#pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            uint16_t* ci = c0 + 16 * i * d.ldc;
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+              if (CHK && !(mrow + 16 * i < M && ncol + 16 * j < N)) continue;
+              *reinterpret_cast<uint2*>(ci + 16 * j) =
+                  make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+            }
           }
         }
-        acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+      };
+      if (full) {
+        write(std::false_type{});
+      } else {
+        write(std::true_type{});
       }
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
     }
     cu += G;
-    if (cu >= U) break;
+    if (cu >= U) break;  // (the loads issued after the last block are drained below)
     C = unit_of<BM, BN>(cu, tiles_m, tiles_n, nsplit, nkb);
     ckb = C.kb0;
   }
+  // no direct-to-LDS load may still be writing when the workgroup's LDS is handed to the next one
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Sum of the split partial sums in split order, converted to the output type:
@@ -425,6 +463,7 @@ static hipError_t launch_fmt(const GemmDesc& d, const GemmPlan& p, float* partia
   switch (p.shape) {
     case k128x256: return launch_variant<OP, 128, 256, 2, 4, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
     case k256x128: return launch_variant<OP, 256, 128, 4, 2, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
+    case k256x256: return launch_variant<OP, 256, 256, 2, 4, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
     default: return launch_variant<OP, 128, 128, 2, 2, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
   }
 }

@@ -5,12 +5,12 @@
 
 namespace fp8bq {
 
-// FP8BQ_GEMM_TILE=<0|1|2> forces a tile shape (tuning aid); read once.
+// FP8BQ_GEMM_TILE=<0|1|2|3> forces a tile shape (tuning aid); read once.
 static int forced_shape() {
   static const int v = [] {
     const char* e = std::getenv("FP8BQ_GEMM_TILE");
     const int x = e ? std::atoi(e) : -1;
-    return (x >= 0 && x <= 2) ? x : -1;
+    return (x >= 0 && x <= 3) ? x : -1;
   }();
   return v;
 }

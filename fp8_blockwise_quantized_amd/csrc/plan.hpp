@@ -14,10 +14,11 @@ enum SbMode : int { kSbBlock128 = 0, kSbColumn = 1 };
 enum Op : int { kOpFprop = 0, kOpDgrad = 1, kOpWgrad = 2 };
 
 // Workgroup tile shapes (output rows x columns of one work unit).  All use 64x64 wave tiles:
-//   k128x128: 4 waves, two workgroups per CU;  k128x256 / k256x128: 8 waves, one workgroup per CU.
-enum TileShape : int { k128x128 = 0, k128x256 = 1, k256x128 = 2 };
-inline int tile_rows(int shape) { return shape == k256x128 ? 256 : 128; }
-inline int tile_cols(int shape) { return shape == k128x256 ? 256 : 128; }
+//   k128x128: 4 waves, two workgroups per CU;  k128x256 / k256x128 / k256x256: 8 waves, one
+//   workgroup per CU (k256x256 with 128x64 wave tiles).
+enum TileShape : int { k128x128 = 0, k128x256 = 1, k256x128 = 2, k256x256 = 3 };
+inline int tile_rows(int shape) { return (shape == k256x128 || shape == k256x256) ? 256 : 128; }
+inline int tile_cols(int shape) { return (shape == k128x256 || shape == k256x256) ? 256 : 128; }
 inline int blocks_per_cu(int shape) { return shape == k128x128 ? 2 : 1; }
 constexpr int kMaxSplit = 8;
 
