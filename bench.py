@@ -121,7 +121,7 @@ def main():
 
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     breakdown = summarize(ops, dur_ms)
-    roof = roofline(ops, dur_ms)
+    roof = roofline(fq, ops, dur_ms)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -300,21 +300,26 @@ def summarize(ops, dur_ms):
     return out
 
 
-# Kernel instance names per product as profilers print them (gemm_tn_kernel<OP, BM, BN, waves_m,
-# waves_n, LDS stages, scale mode, fmtA, fmtB, f32 out>).  Only fprop's call launches exactly one
-# kernel on the decoder workload (dgrad's also transposes the weight codes, and the split wgrads add
-# a reduction pass), so its events bracket the kernel alone: the roofline is taken on it.
-GEMM_KERNEL = {
-    "fprop": "void fp8bq::gemm_tn_kernel<0, 128, 128, 2, 2, 2, 0, 0, 0, 0>(fp8bq::GemmDesc, unsigned int, "
-             "unsigned int, int, float*)",
-}
-ISOLATED = ("fprop",)
+# Kernel instance names as profilers print them: gemm_tn_kernel<OP, BM, BN, waves_m, waves_n, LDS
+# stages, scale mode, fmtA, fmtB, f32 out>; the tile shape comes from the library's plan query.
+_TILE_ARGS = {(128, 128): "128, 128, 2, 2, 2", (128, 256): "128, 256, 2, 4, 2", (256, 128): "256, 128, 4, 2, 2",
+              (256, 256): "256, 256, 2, 4, 2"}
+_OP_ID = {"fprop": 0, "dgrad": 1, "wgrad": 2}
 
 
-def _traffic(kind):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kind}_decoder_block.json")
+def gemm_kernel(fq, kind, M, N, K):
+    """(kernel name, isolated): isolated when the call launches that one kernel (dgrad's calls also
+    transpose the weight codes; a split contraction adds a reduction pass)."""
+    tm, tn, split = fq.fp8bq_gemm_plan(_OP_ID[kind], M, N, K)
+    name = (f"void fp8bq::gemm_tn_kernel<{_OP_ID[kind]}, {_TILE_ARGS[(tm, tn)]}, {1 if kind == 'wgrad' else 0}, "
+            f"0, 0, 0>(fp8bq::GemmDesc, unsigned int, unsigned int, int, float*)")
+    return name, kind != "dgrad" and split == 1
+
+
+def _traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic_decoder_block.json")
     if not os.path.exists(path):
         return None
     try:
@@ -322,38 +327,41 @@ def _traffic(kind):
         src = open(os.path.join(ROOT, "fp8_blockwise_quantized_amd", "csrc", "gemm.hip"), "rb").read()
         if t.get("gemm_hip_sha256") != hashlib.sha256(src).hexdigest():
             return None
-        return t.get("bytes_per_launch")
+        k = t.get("kernels", {}).get(kernel)
+        return k.get("bytes_per_launch") if k else None
     except (OSError, ValueError):
         return None
 
 
-def roofline(ops, dur_ms):
-    """The fprop GEMM kernel (the GEMMs are the dominant cost; fprop's calls launch that one kernel):
+def roofline(fq, ops, dur_ms):
+    """The dominant GEMM kernel among those whose every launch in the step is that kernel alone:
     achieved = its algorithmic FLOPs per launch / its mean launch duration (HIP events on the launch
-    stream), averaged over the step's launches."""
-    best = None
-    for kind in ISOLATED:
-        sel = [(o, d) for o, d in zip(ops, dur_ms) if o["kind"] == kind]
-        if not sel:
+    stream, one pair per call), over all of its launches in the step."""
+    groups = {}
+    for o, d in zip(ops, dur_ms):
+        if not o["flops"]:
             continue
-        t = sum(d for _, d in sel)
-        if best is None or t > best[1]:
-            best = (kind, t, sel)
-    if best is None:
+        name, isolated = gemm_kernel(fq, o["kind"], *o["shape"])
+        g = groups.setdefault(name, {"ok": True, "sel": []})
+        g["ok"] &= isolated
+        g["sel"].append((o, float(d)))
+    eligible = [(sum(d for _, d in g["sel"]), name, g["sel"]) for name, g in groups.items() if g["ok"]]
+    if not eligible:
         return None
-    kind, t, sel = best
+    t, name, sel = max(eligible)
     flops_per_launch = sum(o["flops"] for o, _ in sel) / len(sel)
     ms_per_launch = t / len(sel)
     achieved = flops_per_launch / (ms_per_launch * 1e-3) / 1e12
     return {
         "bound": "mfma",
-        "kernel": GEMM_KERNEL[kind],
+        "kernel": name,
         "achieved": round(achieved, 1),
         "peak": FP8_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-        "traffic": _traffic(kind),
+        "traffic": _traffic(name),
         "launches_per_step": len(sel),
+        "launches": [o["name"] for o, _ in sel],
         "flops_per_launch": flops_per_launch,
         "mean_launch_ms": round(ms_per_launch, 5),
     }

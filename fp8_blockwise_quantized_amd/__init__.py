@@ -14,6 +14,7 @@ Raw entry points (same names and argument order as the C ABI, tensors in place o
     fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws=None)
     fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None)
     fp8bq_gemm_workspace_size(op, M, N, K)
+    fp8bq_gemm_plan(op, M, N, K) -> (tile_m, tile_n, split_k)
 
 Allocating helpers (outputs created with torch on the input's device):
 
@@ -59,6 +60,7 @@ _SIGS = {
     "fp8bq_gemm_wgrad": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
                          _c_int, _c_vp, _c_int, _c_i64, _c_vp, _c_sz, _c_vp],
     "fp8bq_gemm_workspace_size": [_c_int, _c_i64, _c_i64, _c_i64],
+    "fp8bq_gemm_plan": [_c_int, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
     "fp8bq_status_string": [_c_int],
     "fp8bq_version": [],
 }
@@ -152,6 +154,14 @@ def fp8bq_quantize_weight_128x128(w, fmt, q, s):
 
 def fp8bq_gemm_workspace_size(op, M, N, K):
     return int(lib().fp8bq_gemm_workspace_size(int(op), int(M), int(N), int(K)))
+
+
+def fp8bq_gemm_plan(op, M, N, K):
+    tm, tn, sk = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = lib().fp8bq_gemm_plan(int(op), int(M), int(N), int(K), ctypes.cast(ctypes.byref(tm), _c_vp),
+                               ctypes.cast(ctypes.byref(tn), _c_vp), ctypes.cast(ctypes.byref(sk), _c_vp))
+    _check(st, "fp8bq_gemm_plan")
+    return tm.value, tn.value, sk.value
 
 
 def _ws_args(ws):

@@ -173,6 +173,17 @@ size_t fp8bq_gemm_workspace_size(fp8bq_op op, int64_t M, int64_t N, int64_t K) {
   return plan_gemm((int)op, M, N, K, cu_count_or_default()).ws_total();
 }
 
+int fp8bq_gemm_plan(fp8bq_op op, int64_t M, int64_t N, int64_t K, int32_t* tile_m, int32_t* tile_n,
+                    int32_t* split_k) {
+  if (!tile_m || !tile_n || !split_k) return kErrNull;
+  if ((int)op < 0 || (int)op > 2 || M < 0 || N < 0 || K < 0) return kErrShape;
+  const GemmPlan p = plan_gemm((int)op, M, N, K, cu_count_or_default());
+  *tile_m = p.tile_m;
+  *tile_n = p.tile_n;
+  *split_k = p.split_k;
+  return kOk;
+}
+
 const char* fp8bq_status_string(int status) {
   switch (status) {
     case kOk: return "FP8BQ_OK";

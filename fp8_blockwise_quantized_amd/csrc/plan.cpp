@@ -17,25 +17,34 @@ static int forced_shape() {
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Cost model in microseconds: a round of resident units takes about 1.2 us per contraction block
-// (measured: two 128x128 workgroups per CU), and a split adds a pass that writes and re-reads
-// split x rows x cols FP32 partials and writes the output (~5 TB/s effective).  Splitting pays off
-// only when the tiles alone leave workgroup slots idle.
-int choose_split(int64_t rows, int64_t cols, int64_t nkb, int64_t slots, int tile_m, int tile_n) {
-  const int64_t tiles = cdiv(rows, tile_m) * cdiv(cols, tile_n);
+// Time of one contraction block for one round of resident work units, in microseconds, measured
+// on MI355X: two 128x128 workgroups per CU take ~1.2 us per block, one 256x256 workgroup ~2.05 us
+// (4x the work for 1.7x the time: half the operand traffic per flop).
+static double block_us(int shape) { return shape == k256x256 ? 2.05 : 1.2; }
+
+// Cost model in microseconds: rounds of resident units x blocks per unit x block time, plus, for a
+// split, a pass that writes and re-reads split x rows x cols FP32 partials and writes the output
+// (~5 TB/s effective).  Splitting pays off only when the tiles alone leave workgroup slots idle.
+static double split_cost(int64_t rows, int64_t cols, int64_t nkb, int64_t slots, int shape, int s) {
+  const int64_t tiles = cdiv(rows, tile_rows(shape)) * cdiv(cols, tile_cols(shape));
+  const double rounds = (double)cdiv(tiles * s, slots);
+  const double gemm_us = rounds * ((double)nkb / s) * block_us(shape);
+  const double red_us = s > 1 ? (8.0 * s + 4.0) * (double)rows * (double)cols / 5.0e6 : 0.0;
+  return gemm_us + red_us;
+}
+
+static int best_split(int64_t rows, int64_t cols, int64_t nkb, int64_t slots, int shape, double* cost) {
   int best = 1;
   double best_us = 0.0;
   for (int s = 1; s <= kMaxSplit; ++s) {
     if (s > 1 && nkb / s < 4) break;  // keep at least 4 blocks per unit
-    const double rounds = (double)cdiv(tiles * s, slots);
-    const double gemm_us = rounds * ((double)nkb / s) * 1.2;
-    const double red_us = s > 1 ? (8.0 * s + 4.0) * (double)rows * (double)cols / 5.0e6 : 0.0;
-    const double us = gemm_us + red_us;
+    const double us = split_cost(rows, cols, nkb, slots, shape, s);
     if (s == 1 || us < best_us * 0.97) {
       best = s;
       best_us = us;
     }
   }
+  if (cost) *cost = best_us;
   return best;
 }
 
@@ -50,14 +59,26 @@ GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count) {
   } else {
     rows = N; cols = K; contraction = M;
   }
-  p.shape = forced_shape() >= 0 ? forced_shape() : k128x128;
+  const int64_t cus = cu_count > 0 ? cu_count : 256;
+  const int64_t nkb = contraction / 128;
+  const bool work = rows > 0 && cols > 0 && nkb > 0;
+  if (forced_shape() >= 0) {
+    p.shape = forced_shape();
+  } else if (work) {
+    // the faster of the two tile shapes under the cost model (ties go to the larger tile)
+    double c128 = 0.0, c256 = 0.0;
+    best_split(rows, cols, nkb, cus * blocks_per_cu(k128x128), k128x128, &c128);
+    best_split(rows, cols, nkb, cus * blocks_per_cu(k256x256), k256x256, &c256);
+    p.shape = c256 <= c128 ? k256x256 : k128x128;
+  } else {
+    p.shape = k128x128;
+  }
   p.tile_m = tile_rows(p.shape);
   p.tile_n = tile_cols(p.shape);
-  const int64_t slots = (int64_t)(cu_count > 0 ? cu_count : 256) * blocks_per_cu(p.shape);
-  const int64_t nkb = contraction / 128;
+  const int64_t slots = cus * blocks_per_cu(p.shape);
   p.tiles_m = cdiv(rows, p.tile_m);
   p.tiles_n = cdiv(cols, p.tile_n);
-  p.split_k = (rows > 0 && cols > 0 && nkb > 0) ? choose_split(rows, cols, nkb, slots, p.tile_m, p.tile_n) : 1;
+  p.split_k = work ? best_split(rows, cols, nkb, slots, p.shape, nullptr) : 1;
   p.units = p.tiles_m * p.tiles_n * p.split_k;
   // persistent grid: one workgroup per slot (a multiple of 8, so each workgroup stays on one XCD's
   // range of tiles), or one per unit when there are fewer units

@@ -39,7 +39,4 @@ struct GemmPlan {
 // dY[M,N] W[N,K]; wgrad: dW[N,K] = dY[M,N]^T X[M,K]).
 GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count);
 
-// The split the cost model picks for an output of rows x cols with nkb contraction blocks.
-int choose_split(int64_t rows, int64_t cols, int64_t nkb, int64_t slots, int tile_m, int tile_n);
-
 }  // namespace fp8bq

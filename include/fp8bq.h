@@ -74,7 +74,7 @@ typedef enum { FP8BQ_IN_BF16 = 0, FP8BQ_IN_F32 = 1 } fp8bq_in;
  * FP32 (the accumulator itself). */
 typedef enum { FP8BQ_OUT_BF16 = 0, FP8BQ_OUT_F32 = 1 } fp8bq_out;
 
-/* GEMM selector for fp8bq_gemm_workspace_size. */
+/* GEMM selector for fp8bq_gemm_workspace_size and fp8bq_gemm_plan. */
 typedef enum { FP8BQ_OP_FPROP = 0, FP8BQ_OP_DGRAD = 1, FP8BQ_OP_WGRAD = 2 } fp8bq_op;
 
 /*
@@ -184,6 +184,16 @@ int fp8bq_gemm_wgrad(int64_t M, int64_t N, int64_t K,
 /* Workspace bytes the given GEMM needs at these sizes on the current device (0 if none).
  * Returns 0 for invalid arguments too; the GEMM call itself reports those. */
 size_t fp8bq_gemm_workspace_size(fp8bq_op op, int64_t M, int64_t N, int64_t K);
+
+/* The launch plan the given GEMM uses at these sizes on the current device: the output tile of
+ * one work unit (*tile_m x *tile_n output rows x columns in the kernel's frame: fprop [M, N],
+ * dgrad [M, K], wgrad [N, K]) and the number of parts the contraction is split into (*split_k;
+ * 1 = no split, > 1 = FP32 partial sums in the workspace followed by a reduction pass).  The
+ * plan is a deterministic function of (op, M, N, K) and the device's compute-unit count.
+ * Returns FP8BQ_ERR_NULL if an output pointer is NULL, FP8BQ_ERR_SHAPE for an unknown op or a
+ * negative size; writes nothing then. */
+int fp8bq_gemm_plan(fp8bq_op op, int64_t M, int64_t N, int64_t K, int32_t* tile_m, int32_t* tile_n,
+                    int32_t* split_k);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fp8bq_status_string(int status);

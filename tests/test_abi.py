@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fq.lib()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -146,3 +146,26 @@ def test_workspace_sizes():
 def test_zero_contraction_is_valid():
     # K == 0 makes Y all zeros: only the output must be valid
     assert gemm("fp8bq_gemm_fprop", K=0, qa=NUL, sa=NUL, qb=NUL, sb=NUL) == valid_status()
+
+
+def test_gemm_plan_query():
+    """The plan query validates its arguments and reports one of the built tile shapes; the
+    workspace size agrees with the split it reports (FP32 partials of split x rows x cols)."""
+    lib = fq.lib()
+    i32 = ctypes.c_int32
+    a, b, c = i32(-1), i32(-1), i32(-1)
+    ref = lambda v: ctypes.cast(ctypes.byref(v), ctypes.c_void_p)
+    assert lib.fp8bq_gemm_plan(0, 256, 256, 256, NUL, ref(b), ref(c)) == NULL
+    assert lib.fp8bq_gemm_plan(3, 256, 256, 256, ref(a), ref(b), ref(c)) == SHAPE
+    assert lib.fp8bq_gemm_plan(0, -1, 256, 256, ref(a), ref(b), ref(c)) == SHAPE
+    assert a.value == -1 and b.value == -1 and c.value == -1
+    for op in (fq.OP_FPROP, fq.OP_DGRAD, fq.OP_WGRAD):
+        for (M, N, K) in [(256, 256, 256), (512, 2048, 2048), (16384, 2560, 2048), (16384, 11264, 2048),
+                          (16384, 2048, 5632)]:
+            tm, tn, sk = fq.fp8bq_gemm_plan(op, M, N, K)
+            assert (tm, tn) in [(128, 128), (128, 256), (256, 128), (256, 256)]
+            assert 1 <= sk <= 8
+            rows, cols = {fq.OP_FPROP: (M, N), fq.OP_DGRAD: (M, K), fq.OP_WGRAD: (N, K)}[op]
+            ws = fq.fp8bq_gemm_workspace_size(op, M, N, K)
+            transpose = ((N * K + 255) // 256) * 256 if op == fq.OP_DGRAD else 0
+            assert ws == transpose + (sk * rows * cols * 4 if sk > 1 else 0)
