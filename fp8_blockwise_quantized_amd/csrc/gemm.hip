@@ -87,13 +87,25 @@ __device__ __forceinline__ v8i lds_patch(const uint8_t* patch_base, PatchLane pl
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One 16-byte (or 4-byte) global load per lane written straight into LDS at lds_base + 16 * lane
-// (or 4 * lane): global_load_lds_dwordx4 / _dword.  lds_base must be the same for the whole wave.
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+// Raw buffer descriptor over [base, base + bytes): loads past the end read zeros instead of
+// faulting.  Word 3 is the gfx9 raw-buffer format word.
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ uint32_t sat32(int64_t bytes) {
+  return bytes < 0 ? 0u : (bytes < (int64_t)0xFFFFFFFF ? (uint32_t)bytes : 0xFFFFFFFFu);
 }
-__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 4, 0, 0);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+// One 16-byte (or 4-byte) load per lane from byte offset voff of the buffer, written straight into
+// LDS at lds_base + 16 * lane (or 4 * lane): buffer_load_dwordx4 / _dword with the lds flag.
+// lds_base must be the same for the whole wave.  (Buffer loads rather than global_load_lds: the
+// compiler then keeps exact counts for the waits on LDS reads.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, voff, 0, 0, 0);
 }
 
 // One work unit: an output tile and the range of 128-long contraction blocks it sums.
@@ -183,14 +195,19 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   bool lmore = true;
   const uint8_t* abase = d.a;
   const uint8_t* bbase = d.b;
+  uint32_t abytes = 0, bbytes = 0;  // from abase / bbase to the end of the tile's last valid row
   uint32_t aoff[ACHUNKS / NW], boff[BCHUNKS / NW];
-  const float* gs[JPW];
+  const float* gs[JPW];  // scale job q: array base (wave-uniform), per-lane byte offset, kb stride
   int64_t gsk[JPW];
+  uint32_t gsbytes[JPW];
+  uint32_t gvo[JPW];
   int lso[JPW];
   auto set_sources = [&](const Unit& u) {
     abase = d.a + (int64_t)u.m0 * d.lda;
     bbase = d.b + (int64_t)u.n0 * d.ldb;
     const int64_t mleft = M - 1 - u.m0, nleft = N - 1 - u.n0;
+    abytes = sat32((mleft < BM - 1 ? mleft : BM - 1) * d.lda + d.K);
+    bbytes = sat32((nleft < BN - 1 ? nleft : BN - 1) * d.ldb + d.K);
 #pragma unroll
     for (int i = 0; i < ACHUNKS / NW; ++i) {
       const int row = 8 * (wid + NW * i) + (lane >> 3);
@@ -211,26 +228,33 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
       if (j < SAJOBS) {
         int64_t m = u.m0 + 64 * j + lane;
         m = m < M ? m : M - 1;
-        gs[q] = d.sa + m;
+        gs[q] = d.sa;
+        gvo[q] = (uint32_t)(m * 4);
         gsk[q] = d.ldsa;
+        gsbytes[q] = sat32(M * 4);
         lso[q] = SA_OFF + 256 * j;
       } else if (j < SJOBS) {
         const int v = j - SAJOBS;
+        gs[q] = d.sb;
         if constexpr (SBM == kSbColumn) {
           int64_t n = u.n0 + 64 * v + lane;
           n = n < N ? n : N - 1;
-          gs[q] = d.sb + n;
+          gvo[q] = (uint32_t)(n * 4);
+          gsbytes[q] = sat32(N * 4);
         } else {
           const int64_t nbl = N / kGroup;
           int64_t nb = u.n0 / kGroup + (lane < NSB ? lane : NSB - 1);
           nb = nb < nbl ? nb : nbl - 1;
-          gs[q] = d.sb + nb * d.sb_nstride;
+          gvo[q] = (uint32_t)(nb * d.sb_nstride * 4);
+          gsbytes[q] = sat32(((nbl - 1) * d.sb_nstride + 1) * 4);
         }
         gsk[q] = d.sb_kstride;
         lso[q] = SB_OFF + 256 * v;
       } else {
         gs[q] = d.sa;
+        gvo[q] = 0;
         gsk[q] = 0;
+        gsbytes[q] = 4;
         lso[q] = SINK_OFF;
       }
     }
@@ -243,13 +267,14 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   // load number i (0 <= i < LOADS) of this wave for the current cursor position
   auto issue_load = [&](int i, uint8_t* stg) {
     if (i < ACHUNKS / NW) {
-      dma16(abase + aoff[i] + lkb * kGroup, stg + (wid + NW * i) * 1024);
+      dma16(rsrc_of(abase + lkb * kGroup, abytes - (uint32_t)(lkb * kGroup)), aoff[i], stg + (wid + NW * i) * 1024);
     } else if (i < ACHUNKS / NW + BCHUNKS / NW) {
       const int b = i - ACHUNKS / NW;
-      dma16(bbase + boff[b] + lkb * kGroup, stg + BM * 128 + (wid + NW * b) * 1024);
+      dma16(rsrc_of(bbase + lkb * kGroup, bbytes - (uint32_t)(lkb * kGroup)), boff[b],
+            stg + BM * 128 + (wid + NW * b) * 1024);
     } else {
       const int q = i - ACHUNKS / NW - BCHUNKS / NW;
-      dma4(gs[q] + (int64_t)lkb * gsk[q], stg + lso[q]);
+      dma4(rsrc_of(gs[q] + (int64_t)lkb * gsk[q], gsbytes[q]), gvo[q], stg + lso[q]);
     }
   };
   auto advance = [&]() {
@@ -270,9 +295,9 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
     for (int i = 0; i < LOADS; ++i) issue_load(i, stg);
     advance();
   };
-  // Every wave waits for its own loads of the slot read next, then the barrier makes them (and the
-  // end of all reads of the slot refilled next) visible workgroup-wide.  No memory fence: loads of
-  // the newer stages stay in flight across the barrier.
+  // Every wave waits for its own loads of the next block, then the barrier makes them (and the end
+  // of all reads of the current block's slot) visible workgroup-wide.  No memory fence: loads of
+  // the blocks after the next stay in flight across the barrier.
   auto stage_barrier = [&]() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NSTAGE - 2) * LOADS) : "memory");
   };
@@ -290,43 +315,68 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   Unit C = L;
   int ckb = C.kb0;
 
-  // prologue: NSTAGE-1 blocks in flight, the first landed
-#pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s) load_next(smem + s * STAGE);
-  stage_barrier();
-
+  // The side with fewer 16-row patches stays in registers for the whole block ("resident"); the
+  // other side is streamed one patch at a time.  MFMA order: streamed patch outer, except for the
+  // last two streamed patches, which alternate (resident patch outer) so that resident patch k is
+  // free after MFMA 2k+1 of that tail.
+  constexpr bool STREAM_B = NI > MI;
+  constexpr int NOUT = STREAM_B ? NI : MI;  // streamed patches
+  constexpr int NIN = STREAM_B ? MI : NI;   // resident patches
+  constexpr int NTILE = MI * NI;
+  constexpr int LAG = 2;
+  constexpr int TAIL0 = (NOUT - 2) * NIN;  // first MFMA of the two-patch tail
+  constexpr int UB = TAIL0 + 1;            // step that ends with the stage barrier
+  constexpr int NPOST = NTILE + LAG - UB - 1;  // steps after it
+  static_assert(NOUT >= 2 && NPOST >= 1, "tile too small for the pipelined order");
+  auto order = [&](int u, int& o, int& k) {
+    if (u < TAIL0) {
+      o = u / NIN;
+      k = u % NIN;
+    } else {
+      o = NOUT - 2 + (u - TAIL0) % 2;
+      k = (u - TAIL0) / 2;
+    }
+  };
   const PatchLane pl = patch_lane(lane);
-  int rd = 0, wr = NSTAGE - 1;  // ring slots read / refilled this iteration
-  while (true) {
-    const uint8_t* stage = smem + rd * STAGE;
-    uint8_t* refill = smem + wr * STAGE;  // last read in the previous iteration, before its barrier
+  auto streamed = [&](const uint8_t* stg, int o) {
+    return STREAM_B ? lds_patch(stg + BM * 128 + wn * WTN * 128 + 16 * o * 128, pl)
+                    : lds_patch(stg + wm * WTM * 128 + 16 * o * 128, pl);
+  };
+  auto resident = [&](const uint8_t* stg, int k) {
+    return STREAM_B ? lds_patch(stg + wm * WTM * 128 + 16 * k * 128, pl)
+                    : lds_patch(stg + BM * 128 + wn * WTN * 128 + 16 * k * 128, pl);
+  };
+  // The next block's first reads (its resident patches and first streamed patch), in the order the
+  // current block's tail frees their registers: read h goes out at tail step 2 + 2h.
+  constexpr int NHEAD = NIN + 1;
+  auto head_read = [&](const uint8_t* stg, int h, v8i* res, v8i* str) {
+    if (h == 0) res[0] = resident(stg, 0);
+    else if (h == 1) str[0] = streamed(stg, 0);
+    else res[h - 1] = resident(stg, h - 1);
+  };
 
-    // The side with fewer 16-row patches stays in registers for the whole block; the other side is
-    // streamed one patch at a time (MFMA order: streamed patch outer), the next patch read while the
-    // current one's MFMAs run.  Step u issues MFMA u and the fold of MFMA u-LAG, whose result is then
-    // complete, plus one of this wave's loads of the refilled slot while there are any left; a
-    // scheduling fence closes every step, so the matrix pipe never waits on a fold and at most LAG+1
-    // MFMA results are live.  The block's first reads are ordered by first use, so the first MFMA
-    // waits only for its own two patches.
-    constexpr bool STREAM_B = NI > MI;
-    constexpr int NOUT = STREAM_B ? NI : MI;  // streamed patches
-    constexpr int NIN = STREAM_B ? MI : NI;   // resident patches
-    constexpr int NTILE = MI * NI;
-    constexpr int LAG = 2;
-    static_assert(LOADS <= NTILE + LAG, "every load needs a step");
-    const uint8_t* atile = stage + wm * WTM * 128;
-    const uint8_t* btile = stage + BM * 128 + wn * WTN * 128;
-    auto streamed = [&](int o) {
-      return STREAM_B ? lds_patch(btile + 16 * o * 128, pl) : lds_patch(atile + 16 * o * 128, pl);
-    };
-    auto resident = [&](int k) {
-      return STREAM_B ? lds_patch(atile + 16 * k * 128, pl) : lds_patch(btile + 16 * k * 128, pl);
-    };
+  // prologue: every ring slot's block in flight, the first landed, its first reads issued
+  v8i res[NIN], str[NOUT];
+#pragma unroll
+  for (int s = 0; s < NSTAGE; ++s) load_next(smem + s * STAGE);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSTAGE - 1) * LOADS) : "memory");
+#pragma unroll
+  for (int h = 0; h < NHEAD; ++h) head_read(smem, h, res, str);
+
+  int rd = 0;  // ring slot of the block multiplied this iteration
+  while (true) {
+    const int nx = rd + 1 == NSTAGE ? 0 : rd + 1;
+    const uint8_t* stage = smem + rd * STAGE;
+    const uint8_t* nstage = smem + nx * STAGE;
+
+    // Step u issues MFMA u (and the read-ahead of the next streamed patch) and the fold of MFMA
+    // u-LAG, whose result is then complete; a scheduling fence closes every step, so the matrix pipe
+    // never waits on a fold and at most LAG+1 MFMA results are live.  Step UB ends with the stage
+    // barrier: every wave has read all it needs of this block (the tail's operands are in registers)
+    // and the next block has landed.  The steps after it refill this block's slot with the block
+    // NSTAGE ahead and read the next block's first patches while the tail's MFMAs run.
     const float* ssa = reinterpret_cast<const float*>(stage + SA_OFF);
     const float* ssb = reinterpret_cast<const float*>(stage + SB_OFF);
-    v8i res[NIN], str[NOUT];
-    str[0] = streamed(0);
-    res[0] = resident(0);
     float sa_[MI];
 #pragma unroll
     for (int i = 0; i < MI; ++i) sa_[i] = ssa[wm * WTM + 16 * i + (lane & 15)];
@@ -339,20 +389,27 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
       for (int j = 0; j < NI; ++j)
         sbc[j] = *reinterpret_cast<const v4f*>(ssb + wn * WTN + 16 * j + 4 * (lane >> 4));
     }
-#pragma unroll
-    for (int k = 1; k < NIN; ++k) res[k] = resident(k);
     v4f p[NTILE];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NTILE + LAG; ++u) {
       if (u < NTILE) {
-        const int o = u / NIN, k = u % NIN;
-        if (k == 0 && o + 1 < NOUT) str[o + 1] = streamed(o + 1);
+        int o, k;
+        order(u, o, k);
+        if (k == 0 && o + 1 < NOUT) str[o + 1] = streamed(stage, o + 1);
         p[u] = STREAM_B ? mfma_block<FA, FB>(str[o], res[k]) : mfma_block<FA, FB>(res[k], str[o]);
       }
-      if (u < LOADS) issue_load(u, refill);
+      if (u == UB) stage_barrier();
+      if (u > UB) {
+        const int t = u - UB - 1;  // post-barrier step 0 .. NPOST-1
+#pragma unroll
+        for (int i = t * LOADS / NPOST; i < (t + 1) * LOADS / NPOST; ++i) issue_load(i, smem + rd * STAGE);
+      }
+      if (u >= UB && (u - UB) % 2 == 1 && (u - UB) / 2 < NHEAD) head_read(nstage, (u - UB) / 2, res, str);
       if (u >= LAG) {
-        const int v = u - LAG, o = v / NIN, k = v % NIN;
+        int o, k;
+        order(u - LAG, o, k);
+        const int v = u - LAG;
         const int i = STREAM_B ? k : o, j = STREAM_B ? o : k;
         if constexpr (SBM == kSbBlock128) {
           const float sc = sa_[i] * sbv;
@@ -365,17 +422,17 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // head reads that did not fit into the steps
+#pragma unroll
+    for (int h = 0; h < NHEAD; ++h)
+      if (UB + 1 + 2 * h >= NTILE + LAG) head_read(nstage, h, res, str);
     // keep the folds in the step sequence (not sunk past the cursor update's branches)
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NI; ++j) asm volatile("" : "+v"(acc[i][j]));
     advance();
-    // the slot read next iteration must have landed before anyone reads it after the barrier; the
-    // loads issued this iteration may stay in flight
-    stage_barrier();
-    rd = rd + 1 == NSTAGE ? 0 : rd + 1;
-    wr = wr + 1 == NSTAGE ? 0 : wr + 1;
+    rd = nx;
 
     if (++ckb < C.kb1) continue;
 
