@@ -11,9 +11,10 @@
 // instruction's per-operand format fields.
 //
 // Operand roles: the MFMA's first operand is the B patch (16 output columns) and its second the A
-// patch (16 output rows).  A lane then holds output row (lane % 16) and four consecutive output
-// columns 4*(lane / 16) + 0..3, so the A-side scale is one value per lane and patch, and the epilogue
-// writes four adjacent BF16 values (8 bytes) per lane.
+// patch (16 output rows).  A lane then holds output row (lane % 16) and four output columns of the B
+// patch, so the A-side scale is one value per lane and patch.  For fprop and dgrad the B patches'
+// rows are permuted so that a lane's columns over all of its wave's B patches are consecutive: the
+// epilogue writes 16-byte runs (eight BF16 values) per lane.
 //
 // Data movement: per 128-long contraction block the workgroup stages a BM x 128 A tile and a
 // BN x 128 B tile in LDS (double-buffered, one barrier per block), with 16-byte chunks XOR-swizzled
@@ -75,6 +76,17 @@ struct PatchLane {
 };
 __device__ __forceinline__ PatchLane patch_lane(int lane) {
   const int r = lane & 15, s = swz(r), c0 = 2 * (lane >> 4);
+  return PatchLane{r * 128 + ((c0 ^ s) << 4), r * 128 + (((c0 + 1) ^ s) << 4)};
+}
+// B-side patches are permuted: row rho of B patch j (a wave's four patches of 16 output columns)
+// is output column 16*(rho/4) + 4*j + rho%4 of the wave's 64 columns.  Lane l then holds, over
+// the four patches, the 16 consecutive columns 16*(l/16) .. +15 of its output row, so the epilogue
+// writes 16-byte runs.  B tile rows get their own chunk swizzle, which for these row sets is
+// conflict-free and the same for all four patches (their offsets differ by 512 bytes):
+// swzb(row) = 2 * ((row / 16) % 4) + (row / 2) % 2.
+__device__ __forceinline__ int swzb(int row) { return (((row >> 4) & 3) << 1) | ((row >> 1) & 1); }
+__device__ __forceinline__ PatchLane b_patch_lane(int lane) {
+  const int rho = lane & 15, r = 16 * (rho >> 2) + (rho & 3), s = swzb(r), c0 = 2 * (lane >> 4);
   return PatchLane{r * 128 + ((c0 ^ s) << 4), r * 128 + (((c0 + 1) ^ s) << 4)};
 }
 // The MFMA operand of the 16-row patch starting at patch_base (a multiple of 16 rows into a tile).
@@ -171,6 +183,10 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   constexpr int SBJOBS = NSB > 64 ? NSB / 64 : 1;
   constexpr int SJOBS = SAJOBS + SBJOBS;
   constexpr int JPW = (SJOBS + NW - 1) / NW;          // scale jobs per wave (padded)
+  // B patch rows permuted for 16-byte BF16 stores (fprop / dgrad); the per-column-scale product
+  // (wgrad), mostly written as FP32 partial sums, keeps natural order (64-byte FP32 runs per row)
+  constexpr bool PERM = SBM == kSbBlock128;
+  static_assert(!PERM || NI == 4, "the B-side permutation is laid out for 64-column wave tiles");
   constexpr int LOADS = ACHUNKS / NW + BCHUNKS / NW + JPW;  // loads per wave per stage
   static_assert(ACHUNKS % NW == 0 && BCHUNKS % NW == 0, "tile chunks must split evenly over waves");
   static_assert(BM % 64 == 0 && (NSB <= 64 || NSB % 64 == 0), "scale jobs are 64 lanes wide");
@@ -218,7 +234,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
     for (int i = 0; i < BCHUNKS / NW; ++i) {
       const int row = 8 * (wid + NW * i) + (lane >> 3);
       const int64_t r = row < nleft ? row : nleft;
-      boff[i] = (uint32_t)(r * d.ldb) + (uint32_t)(((lane & 7) ^ swz(row)) * 16);
+      boff[i] = (uint32_t)(r * d.ldb) + (uint32_t)(((lane & 7) ^ (PERM ? swzb(row) : swz(row))) * 16);
     }
     // scale jobs: job j < SAJOBS loads A scales of rows 64j..64j+63, the next SBJOBS the B scales;
     // wave w runs jobs w, w+NW, ...; missing jobs load a valid scale into the sink
@@ -338,14 +354,13 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
     }
   };
   const PatchLane pl = patch_lane(lane);
-  auto streamed = [&](const uint8_t* stg, int o) {
-    return STREAM_B ? lds_patch(stg + BM * 128 + wn * WTN * 128 + 16 * o * 128, pl)
-                    : lds_patch(stg + wm * WTM * 128 + 16 * o * 128, pl);
+  const PatchLane plb = PERM ? b_patch_lane(lane) : pl;
+  auto apatch = [&](const uint8_t* stg, int i) { return lds_patch(stg + wm * WTM * 128 + 16 * i * 128, pl); };
+  auto bpatch = [&](const uint8_t* stg, int j) {
+    return lds_patch(stg + BM * 128 + wn * WTN * 128 + (PERM ? 512 : 2048) * j, plb);
   };
-  auto resident = [&](const uint8_t* stg, int k) {
-    return STREAM_B ? lds_patch(stg + wm * WTM * 128 + 16 * k * 128, pl)
-                    : lds_patch(stg + BM * 128 + wn * WTN * 128 + 16 * k * 128, pl);
-  };
+  auto streamed = [&](const uint8_t* stg, int o) { return STREAM_B ? bpatch(stg, o) : apatch(stg, o); };
+  auto resident = [&](const uint8_t* stg, int k) { return STREAM_B ? apatch(stg, k) : bpatch(stg, k); };
   // The next block's first reads (its resident patches and first streamed patch), in the order the
   // current block's tail frees their registers: read h goes out at tail step 2 + 2h.
   constexpr int NHEAD = NIN + 1;
@@ -436,11 +451,14 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
 
     if (++ckb < C.kb1) continue;
 
-    // unit finished: write the tile (or its partial sum) and move on.  Lane l holds row l % 16 and
-    // columns 4 * (l / 16) .. +3 of each 16x16 patch; only tiles that reach past M or N check bounds.
+    // unit finished: write the tile (or its partial sum) and move on.  Lane l holds row l % 16 of
+    // each 16-row A patch and, of the wave's 64 columns, 16*(l/16) .. +15 (permuted B rows: patch j
+    // gives +4j .. +4j+3) or 4*(l/16) .. +3 of each 16-column patch (natural order); only tiles that
+    // reach past M or N check bounds.
     {
       const int64_t mrow = (int64_t)C.m0 + wm * WTM + (lane & 15);
-      const int64_t ncol = (int64_t)C.n0 + wn * WTN + 4 * (lane >> 4);
+      const int64_t ncol = (int64_t)C.n0 + wn * WTN + (PERM ? 16 : 4) * (lane >> 4);
+      constexpr int JSTEP = PERM ? 4 : 16;  // column offset of patch j from ncol
       const bool full = (int64_t)C.m0 + BM <= M && (int64_t)C.n0 + BN <= N;
       auto write = [&](auto checked) {
         constexpr bool CHK = decltype(checked)::value;
@@ -452,8 +470,22 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
             float* ci = c0 + 16 * i * ldc;
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
-              if (CHK && !(mrow + 16 * i < M && ncol + 16 * j < N)) continue;
-              *reinterpret_cast<v4f*>(ci + 16 * j) = acc[i][j];
+              if (CHK && !(mrow + 16 * i < M && ncol + JSTEP * j < N)) continue;
+              *reinterpret_cast<v4f*>(ci + JSTEP * j) = acc[i][j];
+            }
+          }
+        } else if constexpr (PERM) {
+          uint16_t* c0 = reinterpret_cast<uint16_t*>(d.c) + mrow * d.ldc + ncol;
+#pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            uint16_t* ci = c0 + 16 * i * d.ldc;
+#pragma unroll
+            for (int t = 0; t < NI / 2; ++t) {
+              if (CHK && !(mrow + 16 * i < M && ncol + 8 * t < N)) continue;
+              const v4f& a = acc[i][2 * t];
+              const v4f& b = acc[i][2 * t + 1];
+              *reinterpret_cast<uint4*>(ci + 8 * t) = make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                                  pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
             }
           }
         } else {
