@@ -3,10 +3,10 @@
 
 One step = the whole path for one synthetic 2B-class decoder block at M = 16384 tokens (hidden
 2048; QKV 2048->2560, O 2048->2048, gate+up 2048->11264, down 5632->2048).  Per linear:
-    quantize X 1x128, quantize W 128x128, fprop Y = X W^T,
-    quantize dY 1x128, dgrad dX = dY W,
-    quantize dY 128x1, quantize X 128x1, wgrad dW = dY^T X
-i.e. 20 quantize passes and 12 GEMMs, all E4M3, BF16 in and out, inputs resident in HBM.
+    quantize X both ways (1x128 for fprop, 128x1 for wgrad) in one pass, quantize W 128x128,
+    fprop Y = X W^T,
+    quantize dY both ways in one pass, dgrad dX = dY W, wgrad dW = dY^T X
+i.e. 12 quantize passes and 12 GEMMs, all E4M3, BF16 in and out, inputs resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--workload decoder|linear|sweep] [--no-cpu-baseline]
 
@@ -175,8 +175,13 @@ def _alloc_128x1(torch, R, C, dev):
             torch.empty((R // 128, (C + 3) // 4 * 4), dtype=torch.float32, device=dev)[:, :C])
 
 
+def _qdual_bytes(R, C, in_bytes=2):
+    return R * C * in_bytes + 2 * R * C + R * (C // 128) * 4 + (R // 128) * C * 4
+
+
 def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True):
-    """Closures for one linear's hot path; every output buffer is preallocated."""
+    """Closures for one linear's hot path; every output buffer is preallocated.  With the backward
+    pass, X and dY are each quantized both ways (1x128 and 128x1) in one pass."""
     M, K = X.shape
     N = W.shape[0]
     E4 = fq.E4M3
@@ -185,36 +190,38 @@ def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True):
     sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ws_f = fq._workspace(fq.OP_FPROP, M, N, K, dev)
+    bufs = [qx, sx, qw, sw, y, ws_f]
+    if with_backward:
+        qxt, sxt = _alloc_128x1(torch, M, K, dev)
+        bufs += [qxt, sxt]
+        quant_x = dict(name=f"{name}.quant_x_dual", kind="quant_dual", bytes=_qdual_bytes(M, K), flops=0,
+                       fn=lambda: fq.fp8bq_quantize_act_dual(X, E4, qx, sx, E4, qxt, sxt))
+    else:
+        quant_x = dict(name=f"{name}.quant_x_1x128", kind="quant_1x128", bytes=_q1x128_bytes(M, K), flops=0,
+                       fn=lambda: fq.fp8bq_quantize_act_1x128(X, E4, qx, sx))
     ops = [
-        dict(name=f"{name}.quant_x_1x128", kind="quant_1x128", bytes=_q1x128_bytes(M, K), flops=0,
-             fn=lambda: fq.fp8bq_quantize_act_1x128(X, E4, qx, sx)),
+        quant_x,
         dict(name=f"{name}.quant_w_128x128", kind="quant_128x128", bytes=_qw_bytes(N, K), flops=0,
              fn=lambda: fq.fp8bq_quantize_weight_128x128(W, E4, qw, sw)),
         dict(name=f"{name}.fprop", kind="fprop", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
              fn=lambda: fq.fp8bq_gemm_fprop(qx, sx, E4, qw, sw, E4, y, ws_f)),
     ]
-    bufs = [qx, sx, qw, sw, y, ws_f]
     if with_backward:
         qdy, sdy = _alloc_1x128(torch, M, N, dev)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         qdyt, sdyt = _alloc_128x1(torch, M, N, dev)
-        qxt, sxt = _alloc_128x1(torch, M, K, dev)
         dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
         ws_d = fq._workspace(fq.OP_DGRAD, M, N, K, dev)
         ws_w = fq._workspace(fq.OP_WGRAD, M, N, K, dev)
         ops += [
-            dict(name=f"{name}.quant_dy_1x128", kind="quant_1x128", bytes=_q1x128_bytes(M, N), flops=0,
-                 fn=lambda: fq.fp8bq_quantize_act_1x128(dY, E4, qdy, sdy)),
+            dict(name=f"{name}.quant_dy_dual", kind="quant_dual", bytes=_qdual_bytes(M, N), flops=0,
+                 fn=lambda: fq.fp8bq_quantize_act_dual(dY, E4, qdy, sdy, E4, qdyt, sdyt)),
             dict(name=f"{name}.dgrad", kind="dgrad", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
                  fn=lambda: fq.fp8bq_gemm_dgrad(qdy, sdy, E4, qw, sw, E4, dx, ws_d)),
-            dict(name=f"{name}.quant_dy_128x1", kind="quant_128x1", bytes=_q128x1_bytes(M, N), flops=0,
-                 fn=lambda: fq.fp8bq_quantize_act_128x1(dY, E4, qdyt, sdyt)),
-            dict(name=f"{name}.quant_x_128x1", kind="quant_128x1", bytes=_q128x1_bytes(M, K), flops=0,
-                 fn=lambda: fq.fp8bq_quantize_act_128x1(X, E4, qxt, sxt)),
             dict(name=f"{name}.wgrad", kind="wgrad", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
                  fn=lambda: fq.fp8bq_gemm_wgrad(qdyt, sdyt, E4, qxt, sxt, E4, dw, ws_w)),
         ]
-        bufs += [qdy, sdy, dx, qdyt, sdyt, qxt, sxt, dw, ws_d, ws_w]
+        bufs += [qdy, sdy, dx, qdyt, sdyt, dw, ws_d, ws_w]
     return ops, bufs
 
 
@@ -230,11 +237,12 @@ def build_decoder(torch, fq, synth, dev):
     desc = {
         "workload": "decoder block fprop+dgrad+wgrad, M=16384 tokens, hidden 2048, GQA 16q/2kv x128 "
                     "(QKV 2048->2560, O 2048->2048), SwiGLU gate+up 2048->11264, down 5632->2048; "
-                    "E4M3 act 1x128 / weight 128x128 / wgrad 128x1; BF16 in/out",
+                    "E4M3 act 1x128 / weight 128x128 / wgrad 128x1 (X and dY quantized both ways in one pass "
+                    "each); BF16 in/out",
         "tokens": synth.DECODER_M,
         "linears": [[n, k, nn] for n, k, nn in synth.DECODER_LINEARS],
         "gemms_per_step": 12,
-        "quant_passes_per_step": 20,
+        "quant_passes_per_step": 12,
     }
     return ops, bufs, desc
 

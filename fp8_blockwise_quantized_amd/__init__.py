@@ -9,6 +9,7 @@ Raw entry points (same names and argument order as the C ABI, tensors in place o
 
     fp8bq_quantize_act_1x128(x, fmt, q, s)
     fp8bq_quantize_act_128x1(x, fmt, qt, st)
+    fp8bq_quantize_act_dual(x, fmt_rows, q, s, fmt_cols, qt, st)
     fp8bq_quantize_weight_128x128(w, fmt, q, s)
     fp8bq_gemm_fprop(qx, sx, fx, qw, sw, fw, y, ws=None)
     fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws=None)
@@ -20,6 +21,7 @@ Allocating helpers (outputs created with torch on the input's device):
 
     quantize_act_1x128(x, fmt) -> (q [R, C] uint8, s [C/128, R] float32)
     quantize_act_128x1(x, fmt) -> (qt [C, R] uint8, st [R/128, C] float32)
+    quantize_act_dual(x, fmt_rows, fmt_cols) -> (q, s, qt, st) of the two above, one pass over x
     quantize_weight_128x128(w, fmt) -> (q [N, K] uint8, s [N/128, K/128] float32)
     gemm_fprop(qx, sx, qw, sw, fx=E4M3, fw=E4M3, out_dtype=bf16) -> y [M, N]
     gemm_dgrad(qdy, sdy, qw, sw, fdy=E4M3, fw=E4M3, out_dtype=bf16) -> dx [M, K]
@@ -51,6 +53,8 @@ _c_sz = ctypes.c_size_t
 _SIGS = {
     "fp8bq_quantize_act_1x128": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
     "fp8bq_quantize_act_128x1": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
+    "fp8bq_quantize_act_dual": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_int,
+                                _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
     "fp8bq_quantize_weight_128x128": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
                                       _c_vp],
     "fp8bq_gemm_fprop": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
@@ -146,6 +150,13 @@ def fp8bq_quantize_act_128x1(x, fmt, qt, st):
                                           _ld(st), _stream(x)), "fp8bq_quantize_act_128x1")
 
 
+def fp8bq_quantize_act_dual(x, fmt_rows, q, s, fmt_cols, qt, st):
+    R, C = x.shape
+    _check(lib().fp8bq_quantize_act_dual(_ptr(x), _in_type(x), R, C, _ld(x), fmt_rows, _ptr(q), _ld(q), _ptr(s),
+                                         _ld(s), fmt_cols, _ptr(qt), _ld(qt), _ptr(st), _ld(st), _stream(x)),
+           "fp8bq_quantize_act_dual")
+
+
 def fp8bq_quantize_weight_128x128(w, fmt, q, s):
     N, K = w.shape
     _check(lib().fp8bq_quantize_weight_128x128(_ptr(w), _in_type(w), N, K, _ld(w), fmt, _ptr(q), _ld(q), _ptr(s),
@@ -219,6 +230,18 @@ def quantize_act_128x1(x, fmt=E4M3):
     st = torch.empty((R // 128, _pad4(C)), dtype=torch.float32, device=x.device)[:, :C]
     fp8bq_quantize_act_128x1(x, fmt, qt, st)
     return qt, st
+
+
+def quantize_act_dual(x, fmt_rows=E4M3, fmt_cols=E4M3):
+    """(q, s) of quantize_act_1x128(x, fmt_rows) and (qt, st) of quantize_act_128x1(x, fmt_cols) from one
+    pass over x (R and C multiples of 128)."""
+    R, C = x.shape
+    q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    s = torch.empty((C // 128, _pad4(R)), dtype=torch.float32, device=x.device)[:, :R]
+    qt = torch.empty((C, R), dtype=torch.uint8, device=x.device)
+    st = torch.empty((R // 128, _pad4(C)), dtype=torch.float32, device=x.device)[:, :C]
+    fp8bq_quantize_act_dual(x, fmt_rows, q, s, fmt_cols, qt, st)
+    return q, s, qt, st
 
 
 def quantize_weight_128x128(w, fmt=E4M3):

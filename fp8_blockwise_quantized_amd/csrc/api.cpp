@@ -134,6 +134,18 @@ int fp8bq_quantize_act_128x1(const void* x, fp8bq_in xt, int64_t R, int64_t C, i
   return launched(launch_quant_128x1(x, (int)xt, R, C, ldx, (int)fmt, qt, ldqt, st_, ldst, (hipStream_t)stream));
 }
 
+int fp8bq_quantize_act_dual(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx, fp8bq_fp8 fmt_rows,
+                            uint8_t* q, int64_t ldq, float* s, int64_t lds, fp8bq_fp8 fmt_cols, uint8_t* qt,
+                            int64_t ldqt, float* st_, int64_t ldst, void* stream) {
+  bool empty = false;
+  int st = validate_quant_dual(x, (int)xt, R, C, ldx, (int)fmt_rows, q, ldq, s, lds, (int)fmt_cols, qt, ldqt, st_,
+                               ldst, &empty);
+  if (st != kOk || empty) return st;
+  if ((st = current_device(nullptr)) != kOk) return st;
+  return launched(launch_quant_dual(x, (int)xt, R, C, ldx, (int)fmt_rows, q, ldq, s, lds, (int)fmt_cols, qt, ldqt,
+                                    st_, ldst, (hipStream_t)stream));
+}
+
 int fp8bq_quantize_weight_128x128(const void* w, fp8bq_in wt, int64_t N, int64_t K, int64_t ldw, fp8bq_fp8 fmt,
                                   uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
   bool empty = false;

@@ -13,6 +13,11 @@ hipError_t launch_quant_1x128(const void* x, int xt, int64_t R, int64_t C, int64
                               int64_t ldq, float* s, int64_t lds, hipStream_t st);
 hipError_t launch_quant_128x1(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, uint8_t* qt,
                               int64_t ldqt, float* st_, int64_t ldst, hipStream_t st);
+// Both activation layouts (1x128 row groups with format fr, 128x1 column groups with format fc,
+// transposed) from one read of x; R % 128 == 0 and C % 128 == 0.
+hipError_t launch_quant_dual(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fr, uint8_t* q,
+                             int64_t ldq, float* s, int64_t lds, int fc, uint8_t* qt, int64_t ldqt, float* st_,
+                             int64_t ldst, hipStream_t st);
 hipError_t launch_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
                                 int64_t ldq, float* s, int64_t lds, hipStream_t st);
 

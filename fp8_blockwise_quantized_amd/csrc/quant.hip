@@ -188,6 +188,92 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
+// Both activation layouts from one read: grid (C/128, R/128), the 128x1 kernel's 128x128 tiles and
+// thread mapping.  The 16 threads that share a row patch are one DPP row, so each of a thread's 8
+// rows also gets its 1x128 group amax by DPP, and its 8 codes of that row go out as one 8-byte
+// store (16 threads write the row's 128 contiguous bytes).  Codes and scales are those of the two
+// separate kernels, bit for bit (same scale, division and conversion code).
+// ---------------------------------------------------------------------------------------------
+template <typename TIn, int FR, int FC>
+__global__ __launch_bounds__(256) void quant_dual_kernel(const TIn* __restrict__ x, int64_t ldx,
+                                                         uint8_t* __restrict__ q, int64_t ldq,
+                                                         float* __restrict__ s, int64_t lds,
+                                                         uint8_t* __restrict__ qt, int64_t ldqt,
+                                                         float* __restrict__ st, int64_t ldst) {
+  __shared__ float red[16][kQtCols + 1];
+  __shared__ float ssc[kQtCols];
+  __shared__ float src[kQtCols];
+  __shared__ __attribute__((aligned(8))) uint32_t tileT[kQtCols * kQtStride];
+
+  const int t = threadIdx.x;
+  const int cc = t & 15;
+  const int rg = t >> 4;
+  const int64_t rb = blockIdx.y;
+  const int64_t g = blockIdx.x;  // 128-column group
+  const int64_t c0 = g * kQtCols;
+  const int64_t col = c0 + 8 * cc;
+
+  float v[8][8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) Load8<TIn>::run(x + (rb * kGroup + 8 * rg + p) * ldx + col, v[p]);
+
+  // 1x128 groups: row r = 128*rb + 8*rg + p, columns c0 .. c0+127
+  float rs[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
+    const float sc = group_scale<FR>(row16_max(m));
+    rs[p] = sc;
+    store_codes8(q + (rb * kGroup + 8 * rg + p) * ldq + col, quant8<FR>(v[p], sc, 1.0f / sc));
+  }
+  if (cc == 0) {
+    f32x4* sp = reinterpret_cast<f32x4*>(s + g * lds + rb * kGroup + 8 * rg);
+    sp[0] = (f32x4){rs[0], rs[1], rs[2], rs[3]};
+    sp[1] = (f32x4){rs[4], rs[5], rs[6], rs[7]};
+  }
+
+  // 128x1 groups: column c0 + c, rows 128*rb .. +127 (as quant_128x1_kernel)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float m = __builtin_fabsf(v[0][i]);
+#pragma unroll
+    for (int p = 1; p < 8; ++p) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
+    red[rg][8 * cc + i] = m;
+  }
+  __syncthreads();
+  if (t < kQtCols) {
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = __builtin_fmaxf(m, red[k][t]);
+    const float sc = group_scale<FC>(m);
+    ssc[t] = sc;
+    src[t] = 1.0f / sc;
+    st[rb * ldst + c0 + t] = sc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = 8 * cc + i;
+    const float sc = ssc[c], rc = src[c];
+    float y[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) y[p] = clamp_fmt<FC>(div_by_scale(v[p][i], sc, rc));
+    const uint2 w = make_uint2(pack4<FC>(y[0], y[1], y[2], y[3]), pack4<FC>(y[4], y[5], y[6], y[7]));
+    *reinterpret_cast<uint2*>(tileT + c * kQtStride + 2 * rg) = w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int c = (t >> 3) + 32 * pass;
+    const int ch = t & 7;
+    const uint32_t* src4 = tileT + c * kQtStride + 4 * ch;
+    store_codes16(qt + (c0 + c) * ldqt + rb * kGroup + 16 * ch, make_uint4(src4[0], src4[1], src4[2], src4[3]));
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // 128x128: grid (K/128, N/128), one block per weight tile.  Thread t holds rows (t>>4) + 16*p,
 // p = 0..7, columns 8*(t&15)+0..7 (64 values).  amax: DPP within rows of 16 lanes, readlane across
 // the wave, LDS across the 4 waves.
@@ -260,6 +346,33 @@ hipError_t launch_quant_128x1(const void* x, int xt, int64_t R, int64_t C, int64
                         : launch_128x1_t<uint16_t, kE5M2>(x, R, C, ldx, qt, ldqt, st_, ldst, st);
   return fmt == kE4M3 ? launch_128x1_t<float, kE4M3>(x, R, C, ldx, qt, ldqt, st_, ldst, st)
                       : launch_128x1_t<float, kE5M2>(x, R, C, ldx, qt, ldqt, st_, ldst, st);
+}
+
+template <typename TIn, int FR, int FC>
+static hipError_t launch_dual_t(const void* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq, float* s,
+                                int64_t lds, uint8_t* qt, int64_t ldqt, float* st_, int64_t ldst, hipStream_t st) {
+  dim3 grid((unsigned)(C / kQtCols), (unsigned)(R / kGroup));
+  hipLaunchKernelGGL((quant_dual_kernel<TIn, FR, FC>), grid, dim3(256), 0, st, (const TIn*)x, ldx, q, ldq, s, lds, qt,
+                     ldqt, st_, ldst);
+  return hipGetLastError();
+}
+
+template <typename TIn>
+static hipError_t launch_dual_in(const void* x, int64_t R, int64_t C, int64_t ldx, int fr, uint8_t* q, int64_t ldq,
+                                 float* s, int64_t lds, int fc, uint8_t* qt, int64_t ldqt, float* st_, int64_t ldst,
+                                 hipStream_t st) {
+  if (fr == kE4M3)
+    return fc == kE4M3 ? launch_dual_t<TIn, kE4M3, kE4M3>(x, R, C, ldx, q, ldq, s, lds, qt, ldqt, st_, ldst, st)
+                       : launch_dual_t<TIn, kE4M3, kE5M2>(x, R, C, ldx, q, ldq, s, lds, qt, ldqt, st_, ldst, st);
+  return fc == kE4M3 ? launch_dual_t<TIn, kE5M2, kE4M3>(x, R, C, ldx, q, ldq, s, lds, qt, ldqt, st_, ldst, st)
+                     : launch_dual_t<TIn, kE5M2, kE5M2>(x, R, C, ldx, q, ldq, s, lds, qt, ldqt, st_, ldst, st);
+}
+
+hipError_t launch_quant_dual(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fr, uint8_t* q,
+                             int64_t ldq, float* s, int64_t lds, int fc, uint8_t* qt, int64_t ldqt, float* st_,
+                             int64_t ldst, hipStream_t st) {
+  if (xt == 0) return launch_dual_in<uint16_t>(x, R, C, ldx, fr, q, ldq, s, lds, fc, qt, ldqt, st_, ldst, st);
+  return launch_dual_in<float>(x, R, C, ldx, fr, q, ldq, s, lds, fc, qt, ldqt, st_, ldst, st);
 }
 
 template <typename TIn, int FMT>

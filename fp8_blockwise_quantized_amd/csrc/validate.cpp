@@ -65,6 +65,27 @@ int validate_quant_128x1(const void* x, int xt, int64_t R, int64_t C, int64_t ld
   return check_quant(Mat{x, R, C, ldx, in_esize(xt)}, Mat{qt, C, R, ldqt, 1}, Mat{st, R / 128, C, ldst, 4}, true);
 }
 
+int validate_quant_dual(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fr, const void* q, int64_t ldq,
+                        const void* s, int64_t lds, int fc, const void* qt, int64_t ldqt, const void* st,
+                        int64_t ldst, bool* empty) {
+  *empty = false;
+  if (in_esize(xt) == 0) return kErrDtype;
+  if (!fmt_ok(fr) || !fmt_ok(fc)) return kErrFormat;
+  if (R < 0 || C < 0 || R % 128 != 0 || C % 128 != 0) return kErrShape;
+  if (R == 0 || C == 0) {
+    *empty = true;
+    return kOk;
+  }
+  const Mat mx{x, R, C, ldx, in_esize(xt)};
+  const Mat mq{q, R, C, ldq, 1}, ms{s, C / 128, R, lds, 4};
+  const Mat mqt{qt, C, R, ldqt, 1}, mst{st, R / 128, C, ldst, 4};
+  int r;
+  if ((r = check_quant(mx, mq, ms, true)) != kOk) return r;
+  if ((r = check_quant(mx, mqt, mst, true)) != kOk) return r;
+  if (overlaps(mq, mqt) || overlaps(mq, mst) || overlaps(ms, mqt) || overlaps(ms, mst)) return kErrOverlap;
+  return kOk;
+}
+
 int validate_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, const void* q,
                            int64_t ldq, const void* s, int64_t lds, bool* empty) {
   *empty = false;

@@ -111,6 +111,25 @@ int fp8bq_quantize_act_128x1(const void* x, fp8bq_in xt, int64_t R, int64_t C, i
                              void* stream);
 
 /*
+ * Both activation layouts from one read of x: the outputs of
+ *   fp8bq_quantize_act_1x128(x, xt, R, C, ldx, fmt_rows, q, ldq, s, lds) and
+ *   fp8bq_quantize_act_128x1(x, xt, R, C, ldx, fmt_cols, qt, ldqt, st, ldst),
+ * bit for bit, for about two thirds of their combined memory traffic.  A layer quantizes its
+ * input X both ways (fprop, wgrad) and its output gradient dY both ways (dgrad, wgrad); the two
+ * formats are independent (e.g. E5M2 for dgrad's dY, E4M3 for wgrad's).  Defining passages: as the
+ * two quantizers above.
+ *
+ *   x  [R, C]  input, element type xt, row stride ldx (>= C).  R % 128 == 0; C % 128 == 0.
+ *   q, s       as fp8bq_quantize_act_1x128 (q [R, C], s [C/128][R]).
+ *   qt, st     as fp8bq_quantize_act_128x1 (qt [C, R], st [R/128][C]).
+ * No output may overlap x or another output (FP8BQ_ERR_OVERLAP).
+ */
+int fp8bq_quantize_act_dual(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx,
+                            fp8bq_fp8 fmt_rows, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                            fp8bq_fp8 fmt_cols, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst,
+                            void* stream);
+
+/*
  * Weight quantization, one scale per aligned 128x128 tile.
  * Defining passages: FP8Linear's rule (hankli.space, "核心挑战：Scale Factor 管理"); 2-D
  * 128x128 blocks for weights (AI Papers Daily, "FP8 blockwise 混合精度").

@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fq.lib()
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -59,8 +59,12 @@ def qw(w=P(0), wt=0, N=256, K=256, ldw=256, fmt=0, q=P(1), ldq=256, s=P(2), lds=
     return fq.lib().fp8bq_quantize_weight_128x128(w, wt, N, K, ldw, fmt, q, ldq, s, lds, S0)
 
 
-def valid_status():
-    return DEVICE if not HAVE_GPU else OK
+def valid(call):
+    """A call with valid arguments passes validation and stops at the device check on a machine
+    without a gfx950 GPU.  On a GPU machine it would launch kernels on the fake pointers, so it is
+    not made there."""
+    if not HAVE_GPU:
+        assert call() == DEVICE
 
 
 @pytest.mark.skipif(HAVE_GPU, reason="checks the no-device path")
@@ -68,6 +72,8 @@ def test_valid_arguments_reach_the_device_check():
     assert q1x128() == DEVICE
     assert q128x1() == DEVICE
     assert qw() == DEVICE
+    assert qw(lds=3) == DEVICE  # weight scales need no ld alignment
+    assert qdual() == DEVICE
 
 
 def test_quant_1x128_validation():
@@ -100,7 +106,6 @@ def test_quant_weight_validation():
     assert qw(N=200) == SHAPE
     assert qw(K=100, ldw=112, ldq=112) == SHAPE
     assert qw(lds=1) == LD
-    assert qw(lds=3) in (DEVICE, OK)  # weight scales need no ld alignment
     assert qw(wt=1, ldw=254) == LD
 
 
@@ -112,10 +117,10 @@ def gemm(fn, M=256, N=256, K=256, qa=P(0), ldqa=256, sa=P(1), ldsa=256, fa=0, qb
 
 def test_gemm_validation():
     for fn in ("fp8bq_gemm_fprop", "fp8bq_gemm_dgrad"):
-        assert gemm(fn) == valid_status()
+        valid(lambda: gemm(fn))
         assert gemm(fn, K=200) == SHAPE
         assert gemm(fn, N=200) == SHAPE
-        assert gemm(fn, M=100, ldsa=100) == valid_status()  # ragged token count is allowed
+        valid(lambda: gemm(fn, M=100, ldsa=100))  # ragged token count is allowed
         assert gemm(fn, fa=3) == FORMAT
         assert gemm(fn, out_t=5) == DTYPE
         assert gemm(fn, qa=NUL) == NULL
@@ -125,7 +130,7 @@ def test_gemm_validation():
         assert gemm(fn, out=P(0)) == OVERLAP
         assert gemm(fn, M=0, qa=NUL, out=NUL) == OK
     w = "fp8bq_gemm_wgrad"
-    assert gemm(w, ldsb=256) == valid_status()
+    valid(lambda: gemm(w, ldsb=256))
     assert gemm(w, M=200, ldqa=208, ldqb=208, ldsb=256) == SHAPE  # contraction must be a multiple of 128
     assert gemm(w, ldsb=2) == LD  # column scales are read as vectors
     # dgrad needs a workspace for the transposed weight codes
@@ -145,7 +150,7 @@ def test_workspace_sizes():
 
 def test_zero_contraction_is_valid():
     # K == 0 makes Y all zeros: only the output must be valid
-    assert gemm("fp8bq_gemm_fprop", K=0, qa=NUL, sa=NUL, qb=NUL, sb=NUL) == valid_status()
+    valid(lambda: gemm("fp8bq_gemm_fprop", K=0, qa=NUL, sa=NUL, qb=NUL, sb=NUL))
 
 
 def test_gemm_plan_query():
@@ -169,3 +174,21 @@ def test_gemm_plan_query():
             ws = fq.fp8bq_gemm_workspace_size(op, M, N, K)
             transpose = ((N * K + 255) // 256) * 256 if op == fq.OP_DGRAD else 0
             assert ws == transpose + (sk * rows * cols * 4 if sk > 1 else 0)
+
+
+def qdual(x=P(0), xt=0, R=256, C=256, ldx=256, fr=0, q=P(1), ldq=256, s=P(2), lds=256, fc=0, qt=P(3), ldqt=256,
+          st=P(4), ldst=256):
+    return fq.lib().fp8bq_quantize_act_dual(x, xt, R, C, ldx, fr, q, ldq, s, lds, fc, qt, ldqt, st, ldst, S0)
+
+
+def test_quant_dual_validation():
+    assert qdual(R=0) == OK and qdual(C=0) == OK  # empty: no-op
+    assert qdual(xt=2) == DTYPE
+    assert qdual(fr=2) == FORMAT and qdual(fc=-1) == FORMAT
+    assert qdual(R=200) == SHAPE  # 128x1 groups need R % 128 == 0
+    assert qdual(C=200, ldx=256) == SHAPE  # 1x128 groups need C % 128 == 0
+    assert qdual(q=NUL) == NULL and qdual(st=NUL) == NULL
+    assert qdual(ldqt=200) == LD and qdual(lds=250) == LD
+    assert qdual(qt=P(1)) == OVERLAP  # the two code arrays coincide
+    assert qdual(st=P(2)) == OVERLAP
+    assert qdual(s=P(0)) == OVERLAP  # scales on top of the input

@@ -251,3 +251,65 @@ def test_heavy_tailed_gradients_sampled():
     _check_act_sampled(c["dY"], oracle.E4M3, "dY E4M3", 4)
     _check_act_sampled(c["X"], oracle.E4M3, "X", 5)
     same(gpu_w(c["W"], oracle.E4M3), oracle.quant_weight_128x128(c["W"].float().numpy(), oracle.E4M3), "W")
+
+
+# ------------------------------------------------------------------------------------------
+# both activation layouts from one pass
+# ------------------------------------------------------------------------------------------
+
+def gpu_dual(x, fr, fc):
+    q, s, qt, st = fq.quantize_act_dual(x.to(DEV), FP[fr], FP[fc])
+    torch.cuda.synchronize()
+    return (q.cpu().numpy(), s.cpu().numpy().T), (qt.cpu().numpy().T, st.cpu().numpy())
+
+
+@pytest.mark.parametrize("fr,fc", [(oracle.E4M3, oracle.E4M3), (oracle.E5M2, oracle.E4M3),
+                                   (oracle.E4M3, oracle.E5M2), (oracle.E5M2, oracle.E5M2)])
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (640, 256)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_dual_shapes(fr, fc, shape, dt):
+    R, C = shape
+    x = synth.random_bf16(shape, seed=R + C, outliers=True) if dt == "bf16" else synth.random_f32(shape, seed=R + C)
+    xf = x.float().numpy()
+    rows, cols = gpu_dual(x, fr, fc)
+    same(rows, oracle.quant_act_1x128(xf, fr), f"dual 1x128 {shape} {dt}")
+    same(cols, oracle.quant_act_128x1(xf, fc), f"dual 128x1 {shape} {dt}")
+
+
+def test_dual_edge_values_and_strides():
+    x = _edge_matrix()
+    xf = x.float().numpy()
+    for fr, fc in [(oracle.E4M3, oracle.E5M2), (oracle.E5M2, oracle.E4M3)]:
+        rows, cols = gpu_dual(x, fr, fc)
+        same(rows, oracle.quant_act_1x128(xf, fr), "edge dual 1x128")
+        same(cols, oracle.quant_act_128x1(xf, fc), "edge dual 128x1")
+    big = synth.random_bf16((384, 512), seed=8, outliers=True).to(DEV)
+    xs = big[:256, 128:384]  # R=256, C=256, ldx=512
+    q = torch.zeros((256, 272), dtype=torch.uint8, device=DEV)[:, :256]
+    s = torch.zeros((2, 264), dtype=torch.float32, device=DEV)[:, :256]
+    qt = torch.zeros((256, 288), dtype=torch.uint8, device=DEV)[:, :256]
+    st = torch.zeros((2, 260), dtype=torch.float32, device=DEV)[:, :256]
+    fq.fp8bq_quantize_act_dual(xs, fq.E4M3, q, s, fq.E5M2, qt, st)
+    torch.cuda.synchronize()
+    xsf = xs.float().cpu().numpy()
+    same((q.cpu().numpy(), s.cpu().numpy().T), oracle.quant_act_1x128(xsf, oracle.E4M3), "strided dual 1x128")
+    same((qt.cpu().numpy().T, st.cpu().numpy()), oracle.quant_act_128x1(xsf, oracle.E5M2), "strided dual 128x1")
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_dual_decoder_block_sampled(name):
+    """Full-size decoder-block activations: rows and columns sampled as in the single-layout checks."""
+    c = synth.config3_linear(name)
+    for key, fr, fc, seed in [("X", oracle.E4M3, oracle.E4M3, 11), ("dY", oracle.E5M2, oracle.E4M3, 12)]:
+        x = c[key]
+        R, C = x.shape
+        say(f"dual {name} {key} {R}x{C}")
+        q, s, qt, st = fq.quantize_act_dual(x.to(DEV), FP[fr], FP[fc])
+        torch.cuda.synchronize()
+        rows = _sample(R, 256, seed)
+        cols = _sample(C, 64, seed + 1)
+        same((q.cpu().numpy()[rows], s.cpu().numpy().T[rows]), oracle.quant_act_1x128(x[rows].float().numpy(), fr),
+             f"dual {name} {key} 1x128")
+        xc = np.ascontiguousarray(x[:, cols].float().numpy())
+        same((qt.cpu().numpy()[cols].T, st.cpu().numpy()[:, cols]), oracle.quant_act_128x1(xc, fc),
+             f"dual {name} {key} 128x1")
