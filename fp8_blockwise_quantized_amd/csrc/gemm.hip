@@ -13,8 +13,8 @@
 // Operand roles: the MFMA's first operand is the B patch (16 output columns) and its second the A
 // patch (16 output rows).  A lane then holds output row (lane % 16) and four output columns of the B
 // patch, so the A-side scale is one value per lane and patch.  For fprop and dgrad the B patches'
-// rows are permuted so that a lane's columns over all of its wave's B patches are consecutive: the
-// epilogue writes 16-byte runs (eight BF16 values) per lane.
+// rows are permuted so that a lane holds runs of 8 consecutive columns and the 4 lanes of an output
+// row hold 32 consecutive columns: the epilogue writes 64 contiguous bytes of BF16 per row and store.
 //
 // Data movement: per 128-long contraction block the workgroup stages a BM x 128 A tile and a
 // BN x 128 B tile in LDS (double-buffered, one barrier per block), with 16-byte chunks XOR-swizzled
@@ -79,14 +79,14 @@ __device__ __forceinline__ PatchLane patch_lane(int lane) {
   return PatchLane{r * 128 + ((c0 ^ s) << 4), r * 128 + (((c0 + 1) ^ s) << 4)};
 }
 // B-side patches are permuted: row rho of B patch j (a wave's four patches of 16 output columns)
-// is output column 16*(rho/4) + 4*j + rho%4 of the wave's 64 columns.  Lane l then holds, over
-// the four patches, the 16 consecutive columns 16*(l/16) .. +15 of its output row, so the epilogue
-// writes 16-byte runs.  B tile rows get their own chunk swizzle, which for these row sets is
-// conflict-free and the same for all four patches (their offsets differ by 512 bytes):
-// swzb(row) = 2 * ((row / 16) % 4) + (row / 2) % 2.
-__device__ __forceinline__ int swzb(int row) { return (((row >> 4) & 3) << 1) | ((row >> 1) & 1); }
+// is output column 8*(rho/4) + 32*(j/2) + 4*(j%2) + rho%4 of the wave's 64 columns.  Lane l then
+// holds, for patches 2t and 2t+1, the 8 consecutive columns 32*t + 8*(l/16) .. +7 of its output row,
+// so the four lanes of a row write 64 contiguous bytes per store.  B tile rows get their own chunk
+// swizzle, which for these row sets is conflict-free and the same for all four patches (their rows
+// differ by 32*(j/2) + 4*(j%2)): swzb(row) = 2 * ((row / 8) % 4) + (row / 2) % 2.
+__device__ __forceinline__ int swzb(int row) { return (((row >> 3) & 3) << 1) | ((row >> 1) & 1); }
 __device__ __forceinline__ PatchLane b_patch_lane(int lane) {
-  const int rho = lane & 15, r = 16 * (rho >> 2) + (rho & 3), s = swzb(r), c0 = 2 * (lane >> 4);
+  const int rho = lane & 15, r = 8 * (rho >> 2) + (rho & 3), s = swzb(r), c0 = 2 * (lane >> 4);
   return PatchLane{r * 128 + ((c0 ^ s) << 4), r * 128 + (((c0 + 1) ^ s) << 4)};
 }
 // The MFMA operand of the 16-row patch starting at patch_base (a multiple of 16 rows into a tile).
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   const PatchLane plb = PERM ? b_patch_lane(lane) : pl;
   auto apatch = [&](const uint8_t* stg, int i) { return lds_patch(stg + wm * WTM * 128 + 16 * i * 128, pl); };
   auto bpatch = [&](const uint8_t* stg, int j) {
-    return lds_patch(stg + BM * 128 + wn * WTN * 128 + (PERM ? 512 : 2048) * j, plb);
+    return lds_patch(stg + BM * 128 + wn * WTN * 128 + (PERM ? (4096 * (j >> 1) + 512 * (j & 1)) : 2048 * j), plb);
   };
   auto streamed = [&](const uint8_t* stg, int o) { return STREAM_B ? bpatch(stg, o) : apatch(stg, o); };
   auto resident = [&](const uint8_t* stg, int k) { return STREAM_B ? apatch(stg, k) : bpatch(stg, k); };
@@ -452,13 +452,13 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
     if (++ckb < C.kb1) continue;
 
     // unit finished: write the tile (or its partial sum) and move on.  Lane l holds row l % 16 of
-    // each 16-row A patch and, of the wave's 64 columns, 16*(l/16) .. +15 (permuted B rows: patch j
-    // gives +4j .. +4j+3) or 4*(l/16) .. +3 of each 16-column patch (natural order); only tiles that
-    // reach past M or N check bounds.
+    // each 16-row A patch and, of the wave's 64 columns, 8*(l/16) + 32*(j/2) + 4*(j%2) .. +3 for
+    // patch j (permuted B rows) or 16*j + 4*(l/16) .. +3 (natural order); only tiles that reach past
+    // M or N check bounds.
     {
       const int64_t mrow = (int64_t)C.m0 + wm * WTM + (lane & 15);
-      const int64_t ncol = (int64_t)C.n0 + wn * WTN + (PERM ? 16 : 4) * (lane >> 4);
-      constexpr int JSTEP = PERM ? 4 : 16;  // column offset of patch j from ncol
+      const int64_t ncol = (int64_t)C.n0 + wn * WTN + (PERM ? 8 : 4) * (lane >> 4);
+      auto jcol = [](int j) { return PERM ? 32 * (j >> 1) + 4 * (j & 1) : 16 * j; };  // patch j's offset from ncol
       const bool full = (int64_t)C.m0 + BM <= M && (int64_t)C.n0 + BN <= N;
       auto write = [&](auto checked) {
         constexpr bool CHK = decltype(checked)::value;
@@ -470,8 +470,8 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
             float* ci = c0 + 16 * i * ldc;
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
-              if (CHK && !(mrow + 16 * i < M && ncol + JSTEP * j < N)) continue;
-              *reinterpret_cast<v4f*>(ci + JSTEP * j) = acc[i][j];
+              if (CHK && !(mrow + 16 * i < M && ncol + jcol(j) < N)) continue;
+              *reinterpret_cast<v4f*>(ci + jcol(j)) = acc[i][j];
             }
           }
         } else if constexpr (PERM) {
@@ -481,11 +481,11 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
             uint16_t* ci = c0 + 16 * i * d.ldc;
 #pragma unroll
             for (int t = 0; t < NI / 2; ++t) {
-              if (CHK && !(mrow + 16 * i < M && ncol + 8 * t < N)) continue;
+              if (CHK && !(mrow + 16 * i < M && ncol + 32 * t < N)) continue;
               const v4f& a = acc[i][2 * t];
               const v4f& b = acc[i][2 * t + 1];
-              *reinterpret_cast<uint4*>(ci + 8 * t) = make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
-                                                                  pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
+              *reinterpret_cast<uint4*>(ci + 32 * t) = make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                                   pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
             }
           }
         } else {
