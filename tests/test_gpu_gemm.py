@@ -286,3 +286,36 @@ def test_split_is_deterministic():
     torch.cuda.synchronize()
     assert fq.fp8bq_gemm_workspace_size(fq.OP_WGRAD, 4096, 256, 256) > 0
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------------------------------
+# the 256x256 tile path with ragged tiles (rows past M, columns past N) and split partials
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_large_tile_ragged_edges(out_dtype):
+    """Shapes the planner runs on 256x256 tiles whose last tile row and column reach past the
+    output (4200 = 16*256 + 104 rows; 2432 = 9.5 tiles of columns); every output compared."""
+    f32 = out_dtype == torch.float32
+    M, N, K = 4200, 2432, 2048
+    assert fq.fp8bq_gemm_plan(fq.OP_FPROP, M, N, K)[:2] == (256, 256)
+    X = synth.random_bf16((M, K), seed=301, outliers=True)
+    W = synth.random_bf16((N, K), seed=302, std=0.02)
+    checked(run_fprop(X, W, out_dtype=out_dtype), "256x256 ragged fprop", f32)
+    Md, Nd, Kd = 4200, 2048, 2432
+    assert fq.fp8bq_gemm_plan(fq.OP_DGRAD, Md, Nd, Kd)[:2] == (256, 256)
+    dY = synth.random_bf16((Md, Nd), seed=303, std=1e-3)
+    Wd = synth.random_bf16((Nd, Kd), seed=304, std=0.02)
+    checked(run_dgrad(dY, Wd, out_dtype=out_dtype), "256x256 ragged dgrad", f32)
+
+
+@pytest.mark.parametrize("shape", [(4096, 4480, 2432), (16384, 2432, 1408)])
+def test_large_tile_wgrad(shape):
+    """wgrad on 256x256 tiles: ragged output columns (2432 = 9.5 tiles) without and with a split
+    contraction (FP32 partial sums)."""
+    M, N, K = shape
+    tm, tn, split = fq.fp8bq_gemm_plan(fq.OP_WGRAD, M, N, K)
+    assert (tm, tn) == (256, 256)
+    dY = synth.random_bf16((M, N), seed=305 + N, std=1e-3)
+    X = synth.random_bf16((M, K), seed=306 + K, outliers=True)
+    checked(run_wgrad(dY, X, ncols=_sample(N, 160, 7), kcols=_sample(K, 160, 8)), f"256x256 wgrad {shape} split {split}")
