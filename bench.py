@@ -3,8 +3,8 @@
 
 One step = the whole path for one synthetic 2B-class decoder block at M = 16384 tokens (hidden
 2048; QKV 2048->2560, O 2048->2048, gate+up 2048->11264, down 5632->2048).  Per linear:
-    quantize X both ways (1x128 for fprop, 128x1 for wgrad) in one pass, quantize W 128x128,
-    fprop Y = X W^T,
+    quantize X both ways (1x128 for fprop, 128x1 for wgrad) in one pass, quantize W 128x128
+    (codes also written transposed for dgrad), fprop Y = X W^T,
     quantize dY both ways in one pass, dgrad dX = dY W, wgrad dW = dY^T X
 i.e. 12 quantize passes and 12 GEMMs, all E4M3, BF16 in and out, inputs resident in HBM.
 
@@ -193,16 +193,20 @@ def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True):
     bufs = [qx, sx, qw, sw, y, ws_f]
     if with_backward:
         qxt, sxt = _alloc_128x1(torch, M, K, dev)
-        bufs += [qxt, sxt]
+        qwt = torch.empty((K, N), dtype=torch.uint8, device=dev)
+        bufs += [qxt, sxt, qwt]
         quant_x = dict(name=f"{name}.quant_x_dual", kind="quant_dual", bytes=_qdual_bytes(M, K), flops=0,
                        fn=lambda: fq.fp8bq_quantize_act_dual(X, E4, qx, sx, E4, qxt, sxt))
+        quant_w = dict(name=f"{name}.quant_w_dual", kind="quant_w_dual", bytes=_qw_bytes(N, K) + N * K, flops=0,
+                       fn=lambda: fq.fp8bq_quantize_weight_dual(W, E4, qw, sw, qwt))
     else:
         quant_x = dict(name=f"{name}.quant_x_1x128", kind="quant_1x128", bytes=_q1x128_bytes(M, K), flops=0,
                        fn=lambda: fq.fp8bq_quantize_act_1x128(X, E4, qx, sx))
+        quant_w = dict(name=f"{name}.quant_w_128x128", kind="quant_128x128", bytes=_qw_bytes(N, K), flops=0,
+                       fn=lambda: fq.fp8bq_quantize_weight_128x128(W, E4, qw, sw))
     ops = [
         quant_x,
-        dict(name=f"{name}.quant_w_128x128", kind="quant_128x128", bytes=_qw_bytes(N, K), flops=0,
-             fn=lambda: fq.fp8bq_quantize_weight_128x128(W, E4, qw, sw)),
+        quant_w,
         dict(name=f"{name}.fprop", kind="fprop", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
              fn=lambda: fq.fp8bq_gemm_fprop(qx, sx, E4, qw, sw, E4, y, ws_f)),
     ]
@@ -211,13 +215,13 @@ def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True):
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         qdyt, sdyt = _alloc_128x1(torch, M, N, dev)
         dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-        ws_d = fq._workspace(fq.OP_DGRAD, M, N, K, dev)
+        ws_d = fq._workspace(fq.OP_DGRAD_WT, M, N, K, dev)
         ws_w = fq._workspace(fq.OP_WGRAD, M, N, K, dev)
         ops += [
             dict(name=f"{name}.quant_dy_dual", kind="quant_dual", bytes=_qdual_bytes(M, N), flops=0,
                  fn=lambda: fq.fp8bq_quantize_act_dual(dY, E4, qdy, sdy, E4, qdyt, sdyt)),
             dict(name=f"{name}.dgrad", kind="dgrad", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
-                 fn=lambda: fq.fp8bq_gemm_dgrad(qdy, sdy, E4, qw, sw, E4, dx, ws_d)),
+                 fn=lambda: fq.fp8bq_gemm_dgrad_wt(qdy, sdy, E4, qwt, sw, E4, dx, ws_d)),
             dict(name=f"{name}.wgrad", kind="wgrad", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
                  fn=lambda: fq.fp8bq_gemm_wgrad(qdyt, sdyt, E4, qxt, sxt, E4, dw, ws_w)),
         ]
@@ -316,12 +320,13 @@ _OP_ID = {"fprop": 0, "dgrad": 1, "wgrad": 2}
 
 
 def gemm_kernel(fq, kind, M, N, K):
-    """(kernel name, isolated): isolated when the call launches that one kernel (dgrad's calls also
-    transpose the weight codes; a split contraction adds a reduction pass)."""
-    tm, tn, split = fq.fp8bq_gemm_plan(_OP_ID[kind], M, N, K)
+    """(kernel name, isolated): isolated when the call launches that one kernel (a split
+    contraction adds a reduction pass).  The step's dgrad runs on pre-transposed weight codes."""
+    op = fq.OP_DGRAD_WT if kind == "dgrad" else _OP_ID[kind]
+    tm, tn, split = fq.fp8bq_gemm_plan(op, M, N, K)
     name = (f"void fp8bq::gemm_tn_kernel<{_OP_ID[kind]}, {_TILE_ARGS[(tm, tn)]}, {1 if kind == 'wgrad' else 0}, "
             f"0, 0, 0>(fp8bq::GemmDesc, unsigned int, unsigned int, int, float*)")
-    return name, kind != "dgrad" and split == 1
+    return name, split == 1
 
 
 def _traffic(kernel):

@@ -11,8 +11,10 @@ Raw entry points (same names and argument order as the C ABI, tensors in place o
     fp8bq_quantize_act_128x1(x, fmt, qt, st)
     fp8bq_quantize_act_dual(x, fmt_rows, q, s, fmt_cols, qt, st)
     fp8bq_quantize_weight_128x128(w, fmt, q, s)
+    fp8bq_quantize_weight_dual(w, fmt, q, s, qt)
     fp8bq_gemm_fprop(qx, sx, fx, qw, sw, fw, y, ws=None)
     fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws=None)
+    fp8bq_gemm_dgrad_wt(qdy, sdy, fdy, qwt, sw, fw, dx, ws=None)
     fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None)
     fp8bq_gemm_workspace_size(op, M, N, K)
     fp8bq_gemm_plan(op, M, N, K) -> (tile_m, tile_n, split_k)
@@ -23,8 +25,10 @@ Allocating helpers (outputs created with torch on the input's device):
     quantize_act_128x1(x, fmt) -> (qt [C, R] uint8, st [R/128, C] float32)
     quantize_act_dual(x, fmt_rows, fmt_cols) -> (q, s, qt, st) of the two above, one pass over x
     quantize_weight_128x128(w, fmt) -> (q [N, K] uint8, s [N/128, K/128] float32)
+    quantize_weight_dual(w, fmt) -> (q, s, qt [K, N]): the above plus the transposed codes
     gemm_fprop(qx, sx, qw, sw, fx=E4M3, fw=E4M3, out_dtype=bf16) -> y [M, N]
     gemm_dgrad(qdy, sdy, qw, sw, fdy=E4M3, fw=E4M3, out_dtype=bf16) -> dx [M, K]
+    gemm_dgrad_wt(qdy, sdy, qwt, sw, fdy=E4M3, fw=E4M3, out_dtype=bf16) -> dx [M, K] (qwt = W^T codes)
     gemm_wgrad(qdyt, sdyt, qxt, sxt, fdy=E4M3, fx=E4M3, out_dtype=bf16) -> dw [N, K]
 """
 
@@ -42,6 +46,7 @@ OUT_F32 = 1
 OP_FPROP = 0
 OP_DGRAD = 1
 OP_WGRAD = 2
+OP_DGRAD_WT = 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfp8bq.so")
 
@@ -55,12 +60,16 @@ _SIGS = {
     "fp8bq_quantize_act_128x1": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
     "fp8bq_quantize_act_dual": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_int,
                                 _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
+    "fp8bq_quantize_weight_dual": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp,
+                                   _c_i64, _c_vp],
     "fp8bq_quantize_weight_128x128": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
                                       _c_vp],
     "fp8bq_gemm_fprop": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
                          _c_int, _c_vp, _c_int, _c_i64, _c_vp, _c_sz, _c_vp],
     "fp8bq_gemm_dgrad": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
                          _c_int, _c_vp, _c_int, _c_i64, _c_vp, _c_sz, _c_vp],
+    "fp8bq_gemm_dgrad_wt": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp,
+                            _c_i64, _c_int, _c_vp, _c_int, _c_i64, _c_vp, _c_sz, _c_vp],
     "fp8bq_gemm_wgrad": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
                          _c_int, _c_vp, _c_int, _c_i64, _c_vp, _c_sz, _c_vp],
     "fp8bq_gemm_workspace_size": [_c_int, _c_i64, _c_i64, _c_i64],
@@ -157,6 +166,12 @@ def fp8bq_quantize_act_dual(x, fmt_rows, q, s, fmt_cols, qt, st):
            "fp8bq_quantize_act_dual")
 
 
+def fp8bq_quantize_weight_dual(w, fmt, q, s, qt):
+    N, K = w.shape
+    _check(lib().fp8bq_quantize_weight_dual(_ptr(w), _in_type(w), N, K, _ld(w), fmt, _ptr(q), _ld(q), _ptr(s), _ld(s),
+                                            _ptr(qt), _ld(qt), _stream(w)), "fp8bq_quantize_weight_dual")
+
+
 def fp8bq_quantize_weight_128x128(w, fmt, q, s):
     N, K = w.shape
     _check(lib().fp8bq_quantize_weight_128x128(_ptr(w), _in_type(w), N, K, _ld(w), fmt, _ptr(q), _ld(q), _ptr(s),
@@ -197,6 +212,15 @@ def fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws=None):
     _check(lib().fp8bq_gemm_dgrad(M, N, K, _ptr(qdy), _ld(qdy), _ptr(sdy), _ld(sdy), fdy, _ptr(qw), _ld(qw),
                                   _ptr(sw), _ld(sw), fw, _ptr(dx), _out_type(dx), _ld(dx), wsp, wsb, _stream(dx)),
            "fp8bq_gemm_dgrad")
+
+
+def fp8bq_gemm_dgrad_wt(qdy, sdy, fdy, qwt, sw, fw, dx, ws=None):
+    M, N = qdy.shape
+    K = qwt.shape[0]
+    wsp, wsb = _ws_args(ws)
+    _check(lib().fp8bq_gemm_dgrad_wt(M, N, K, _ptr(qdy), _ld(qdy), _ptr(sdy), _ld(sdy), fdy, _ptr(qwt), _ld(qwt),
+                                     _ptr(sw), _ld(sw), fw, _ptr(dx), _out_type(dx), _ld(dx), wsp, wsb, _stream(dx)),
+           "fp8bq_gemm_dgrad_wt")
 
 
 def fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None):
@@ -244,6 +268,16 @@ def quantize_act_dual(x, fmt_rows=E4M3, fmt_cols=E4M3):
     return q, s, qt, st
 
 
+def quantize_weight_dual(w, fmt=E4M3):
+    """(q, s) of quantize_weight_128x128(w, fmt) and the transposed codes qt [K, N], one pass over w."""
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    qt = torch.empty((K, N), dtype=torch.uint8, device=w.device)
+    fp8bq_quantize_weight_dual(w, fmt, q, s, qt)
+    return q, s, qt
+
+
 def quantize_weight_128x128(w, fmt=E4M3):
     N, K = w.shape
     q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
@@ -274,6 +308,16 @@ def gemm_dgrad(qdy, sdy, qw, sw, fdy=E4M3, fw=E4M3, out_dtype=torch.bfloat16, ou
     if ws is None:
         ws = _workspace(OP_DGRAD, M, N, K, qdy.device)
     fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws)
+    return dx
+
+
+def gemm_dgrad_wt(qdy, sdy, qwt, sw, fdy=E4M3, fw=E4M3, out_dtype=torch.bfloat16, out=None, ws=None):
+    M, N = qdy.shape
+    K = qwt.shape[0]
+    dx = out if out is not None else torch.empty((M, K), dtype=out_dtype, device=qdy.device)
+    if ws is None:
+        ws = _workspace(OP_DGRAD_WT, M, N, K, qdy.device)
+    fp8bq_gemm_dgrad_wt(qdy, sdy, fdy, qwt, sw, fw, dx, ws)
     return dx
 
 

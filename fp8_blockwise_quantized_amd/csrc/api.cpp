@@ -59,7 +59,7 @@ static int run_gemm(const GemmArgs& g, void* stream) {
   int64_t out_rows, out_cols;
   if (g.op == kOpFprop) {
     out_rows = g.M; out_cols = g.N;
-  } else if (g.op == kOpDgrad) {
+  } else if (g.op == kOpDgrad || g.op == kOpDgradWt) {
     out_rows = g.M; out_cols = g.K;
   } else {
     out_rows = g.N; out_cols = g.K;
@@ -98,6 +98,14 @@ static int run_gemm(const GemmArgs& g, void* stream) {
     d.sb_mode = kSbBlock128;
     d.sb_kstride = g.ldsb;     // sw[nb * ldsw + k / 128]
     d.sb_nstride = 1;
+  } else if (g.op == kOpDgradWt) {
+    // the caller passes W^T [K, N]: already contiguous along the contraction
+    d.K = g.N;
+    d.b = (const uint8_t*)g.qb;
+    d.ldb = g.ldqb;
+    d.sb_mode = kSbBlock128;
+    d.sb_kstride = g.ldsb;     // sw[nb * ldsw + k / 128]
+    d.sb_nstride = 1;
   } else {
     d.K = g.M;
     d.b = (const uint8_t*)g.qb;
@@ -107,7 +115,7 @@ static int run_gemm(const GemmArgs& g, void* stream) {
     d.sb_nstride = 0;
   }
   void* ws_gemm = plan.ws_gemm ? (uint8_t*)g.ws + plan.ws_transpose : nullptr;
-  return launched(launch_gemm(g.op, d, plan, ws_gemm, s));
+  return launched(launch_gemm(g.op == kOpDgradWt ? kOpDgrad : g.op, d, plan, ws_gemm, s));
 }
 
 }  // namespace fp8bq
@@ -146,6 +154,17 @@ int fp8bq_quantize_act_dual(const void* x, fp8bq_in xt, int64_t R, int64_t C, in
                                     st_, ldst, (hipStream_t)stream));
 }
 
+int fp8bq_quantize_weight_dual(const void* w, fp8bq_in wt, int64_t N, int64_t K, int64_t ldw, fp8bq_fp8 fmt,
+                               uint8_t* q, int64_t ldq, float* s, int64_t lds, uint8_t* qt, int64_t ldqt,
+                               void* stream) {
+  bool empty = false;
+  int st = validate_quant_128x128_dual(w, (int)wt, N, K, ldw, (int)fmt, q, ldq, s, lds, qt, ldqt, &empty);
+  if (st != kOk || empty) return st;
+  if ((st = current_device(nullptr)) != kOk) return st;
+  return launched(
+      launch_quant_128x128_dual(w, (int)wt, N, K, ldw, (int)fmt, q, ldq, s, lds, qt, ldqt, (hipStream_t)stream));
+}
+
 int fp8bq_quantize_weight_128x128(const void* w, fp8bq_in wt, int64_t N, int64_t K, int64_t ldw, fp8bq_fp8 fmt,
                                   uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
   bool empty = false;
@@ -171,6 +190,15 @@ int fp8bq_gemm_dgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, int64_
   return run_gemm(g, stream);
 }
 
+int fp8bq_gemm_dgrad_wt(int64_t M, int64_t N, int64_t K, const uint8_t* qdy, int64_t ldqdy, const float* sdy,
+                        int64_t ldsdy, fp8bq_fp8 fdy, const uint8_t* qwt, int64_t ldqwt, const float* sw,
+                        int64_t ldsw, fp8bq_fp8 fw, void* dx, fp8bq_out dxt, int64_t lddx, void* ws, size_t ws_bytes,
+                        void* stream) {
+  GemmArgs g{kOpDgradWt, M, N, K, qdy, ldqdy, sdy, ldsdy, (int)fdy, qwt, ldqwt, sw, ldsw, (int)fw, dx, (int)dxt,
+             lddx, ws, ws_bytes};
+  return run_gemm(g, stream);
+}
+
 int fp8bq_gemm_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdyt, int64_t ldqdyt, const float* sdyt,
                      int64_t ldsdyt, fp8bq_fp8 fdy, const uint8_t* qxt, int64_t ldqxt, const float* sxt,
                      int64_t ldsxt, fp8bq_fp8 fx, void* dw, fp8bq_out dwt, int64_t lddw, void* ws, size_t ws_bytes,
@@ -181,14 +209,14 @@ int fp8bq_gemm_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdyt, int64
 }
 
 size_t fp8bq_gemm_workspace_size(fp8bq_op op, int64_t M, int64_t N, int64_t K) {
-  if ((int)op < 0 || (int)op > 2 || M < 0 || N < 0 || K < 0) return 0;
+  if ((int)op < 0 || (int)op > 3 || M < 0 || N < 0 || K < 0) return 0;
   return plan_gemm((int)op, M, N, K, cu_count_or_default()).ws_total();
 }
 
 int fp8bq_gemm_plan(fp8bq_op op, int64_t M, int64_t N, int64_t K, int32_t* tile_m, int32_t* tile_n,
                     int32_t* split_k) {
   if (!tile_m || !tile_n || !split_k) return kErrNull;
-  if ((int)op < 0 || (int)op > 2 || M < 0 || N < 0 || K < 0) return kErrShape;
+  if ((int)op < 0 || (int)op > 3 || M < 0 || N < 0 || K < 0) return kErrShape;
   const GemmPlan p = plan_gemm((int)op, M, N, K, cu_count_or_default());
   *tile_m = p.tile_m;
   *tile_n = p.tile_n;

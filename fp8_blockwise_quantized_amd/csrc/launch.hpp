@@ -18,6 +18,9 @@ hipError_t launch_quant_128x1(const void* x, int xt, int64_t R, int64_t C, int64
 hipError_t launch_quant_dual(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fr, uint8_t* q,
                              int64_t ldq, float* s, int64_t lds, int fc, uint8_t* qt, int64_t ldqt, float* st_,
                              int64_t ldst, hipStream_t st);
+// Weight codes and scales as launch_quant_128x128 plus the transposed codes qt [K, N].
+hipError_t launch_quant_128x128_dual(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
+                                     int64_t ldq, float* s, int64_t lds, uint8_t* qt, int64_t ldqt, hipStream_t st);
 hipError_t launch_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
                                 int64_t ldq, float* s, int64_t lds, hipStream_t st);
 

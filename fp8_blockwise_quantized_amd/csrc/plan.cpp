@@ -54,7 +54,7 @@ GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count) {
   int64_t rows, cols, contraction;
   if (op == kOpFprop) {
     rows = M; cols = N; contraction = K;
-  } else if (op == kOpDgrad) {
+  } else if (op == kOpDgrad || op == kOpDgradWt) {
     rows = M; cols = K; contraction = N;
   } else {
     rows = N; cols = K; contraction = M;

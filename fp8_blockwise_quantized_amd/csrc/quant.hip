@@ -311,6 +311,71 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const TIn* __restric
 }
 
 // ---------------------------------------------------------------------------------------------
+// 128x128 with a transposed copy: grid (K/128, N/128), one block per weight tile, the 128x1
+// kernel's thread mapping (8 consecutive rows x 8 columns per thread).  The tile's amax goes
+// through readlane and LDS; codes are written row-major (8-byte runs) and, staged transposed in
+// LDS, as W^T codes (16-byte runs), the operand layout of dgrad's contraction over N.
+// ---------------------------------------------------------------------------------------------
+template <typename TIn, int FMT>
+__global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __restrict__ w, int64_t ldw,
+                                                                 uint8_t* __restrict__ q, int64_t ldq,
+                                                                 float* __restrict__ s, int64_t lds,
+                                                                 uint8_t* __restrict__ qt, int64_t ldqt) {
+  __shared__ float wmax[4];
+  __shared__ __attribute__((aligned(8))) uint32_t tileT[kQtCols * kQtStride];
+  const int t = threadIdx.x;
+  const int cc = t & 15;
+  const int rg = t >> 4;
+  const int64_t kb = blockIdx.x, nb = blockIdx.y;
+  const int64_t col = kb * kGroup + 8 * cc;
+
+  float v[8][8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) Load8<TIn>::run(w + (nb * kGroup + 8 * rg + p) * ldw + col, v[p]);
+  float m = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
+  m = wave_max(m);
+  if ((t & 63) == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  const float amax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+  const float sc = group_scale<FMT>(amax);
+  const float rc = 1.0f / sc;
+  uint8_t cb[8][8];  // codes [row p][column i]
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint2 wd = quant8<FMT>(v[p], sc, rc);
+    store_codes8(q + (nb * kGroup + 8 * rg + p) * ldq + col, wd);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      cb[p][i] = (uint8_t)(wd.x >> (8 * i));
+      cb[p][4 + i] = (uint8_t)(wd.y >> (8 * i));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      lo |= (uint32_t)cb[p][i] << (8 * p);
+      hi |= (uint32_t)cb[4 + p][i] << (8 * p);
+    }
+    *reinterpret_cast<uint2*>(tileT + (8 * cc + i) * kQtStride + 2 * rg) = make_uint2(lo, hi);
+  }
+  if (t == 0) s[nb * lds + kb] = sc;
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int c = (t >> 3) + 32 * pass;
+    const int ch = t & 7;
+    const uint32_t* src4 = tileT + c * kQtStride + 4 * ch;
+    store_codes16(qt + (kb * kGroup + c) * ldqt + nb * kGroup + 16 * ch, make_uint4(src4[0], src4[1], src4[2], src4[3]));
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Host launchers (arguments already validated; sizes non-empty).
 // ---------------------------------------------------------------------------------------------
 template <typename TIn, int FMT>
@@ -390,6 +455,24 @@ hipError_t launch_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int
                         : launch_128x128_t<uint16_t, kE5M2>(w, N, K, ldw, q, ldq, s, lds, st);
   return fmt == kE4M3 ? launch_128x128_t<float, kE4M3>(w, N, K, ldw, q, ldq, s, lds, st)
                       : launch_128x128_t<float, kE5M2>(w, N, K, ldw, q, ldq, s, lds, st);
+}
+
+template <typename TIn, int FMT>
+static hipError_t launch_128x128_dual_t(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, int64_t ldq,
+                                        float* s, int64_t lds, uint8_t* qt, int64_t ldqt, hipStream_t st) {
+  dim3 grid((unsigned)(K / kGroup), (unsigned)(N / kGroup));
+  hipLaunchKernelGGL((quant_128x128_dual_kernel<TIn, FMT>), grid, dim3(256), 0, st, (const TIn*)w, ldw, q, ldq, s,
+                     lds, qt, ldqt);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_128x128_dual(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
+                                     int64_t ldq, float* s, int64_t lds, uint8_t* qt, int64_t ldqt, hipStream_t st) {
+  if (wt == 0)
+    return fmt == kE4M3 ? launch_128x128_dual_t<uint16_t, kE4M3>(w, N, K, ldw, q, ldq, s, lds, qt, ldqt, st)
+                        : launch_128x128_dual_t<uint16_t, kE5M2>(w, N, K, ldw, q, ldq, s, lds, qt, ldqt, st);
+  return fmt == kE4M3 ? launch_128x128_dual_t<float, kE4M3>(w, N, K, ldw, q, ldq, s, lds, qt, ldqt, st)
+                      : launch_128x128_dual_t<float, kE5M2>(w, N, K, ldw, q, ldq, s, lds, qt, ldqt, st);
 }
 
 }  // namespace fp8bq

@@ -86,6 +86,26 @@ int validate_quant_dual(const void* x, int xt, int64_t R, int64_t C, int64_t ldx
   return kOk;
 }
 
+int validate_quant_128x128_dual(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, const void* q,
+                                int64_t ldq, const void* s, int64_t lds, const void* qt, int64_t ldqt, bool* empty) {
+  *empty = false;
+  if (in_esize(wt) == 0) return kErrDtype;
+  if (!fmt_ok(fmt)) return kErrFormat;
+  if (N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return kErrShape;
+  if (N == 0 || K == 0) {
+    *empty = true;
+    return kOk;
+  }
+  const Mat mw{w, N, K, ldw, in_esize(wt)}, mq{q, N, K, ldq, 1}, ms{s, N / 128, K / 128, lds, 4};
+  const Mat mqt{qt, K, N, ldqt, 1};
+  int r;
+  if ((r = check_quant(mw, mq, ms, false)) != kOk) return r;
+  if (qt == nullptr) return kErrNull;
+  if ((r = check_mat(mqt, true)) != kOk) return r;
+  if (overlaps(mqt, mw) || overlaps(mqt, mq) || overlaps(mqt, ms)) return kErrOverlap;
+  return kOk;
+}
+
 int validate_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, const void* q,
                            int64_t ldq, const void* s, int64_t lds, bool* empty) {
   *empty = false;
@@ -103,7 +123,7 @@ int validate_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t 
 int validate_gemm(const GemmArgs& g, size_t ws_needed, bool* empty, bool* zero_fill) {
   *empty = false;
   *zero_fill = false;
-  if (g.op < 0 || g.op > 2) return kErrShape;
+  if (g.op < 0 || g.op > 3) return kErrShape;
   if (!fmt_ok(g.fa) || !fmt_ok(g.fb)) return kErrFormat;
   if (g.out_t != 0 && g.out_t != 1) return kErrDtype;
   const int64_t M = g.M, N = g.N, K = g.K;
@@ -120,6 +140,12 @@ int validate_gemm(const GemmArgs& g, size_t ws_needed, bool* empty, bool* zero_f
     qb = Mat{g.qb, N, K, g.ldqb, 1};
     sb = Mat{g.sb, N / 128, K / 128, g.ldsb, 4};
     out_rows = M; out_cols = N; contraction = K;
+  } else if (g.op == 3) {  // dgrad on W^T codes: dY[M,N] (1x128), W^T[K,N] (128x128) -> dX[M,K]
+    qa = Mat{g.qa, M, N, g.ldqa, 1};
+    sa = Mat{g.sa, N / 128, M, g.ldsa, 4};
+    qb = Mat{g.qb, K, N, g.ldqb, 1};
+    sb = Mat{g.sb, N / 128, K / 128, g.ldsb, 4};
+    out_rows = M; out_cols = K; contraction = N;
   } else if (g.op == 1) {  // dgrad: dY[M,N] (1x128), W[N,K] (128x128) -> dX[M,K]
     qa = Mat{g.qa, M, N, g.ldqa, 1};
     sa = Mat{g.sa, N / 128, M, g.ldsa, 4};

@@ -42,6 +42,8 @@ int validate_quant_128x1(const void* x, int xt, int64_t R, int64_t C, int64_t ld
 int validate_quant_dual(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fr, const void* q, int64_t ldq,
                         const void* s, int64_t lds, int fc, const void* qt, int64_t ldqt, const void* st,
                         int64_t ldst, bool* empty);
+int validate_quant_128x128_dual(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, const void* q,
+                                int64_t ldq, const void* s, int64_t lds, const void* qt, int64_t ldqt, bool* empty);
 int validate_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, const void* q,
                            int64_t ldq, const void* s, int64_t lds, bool* empty);
 

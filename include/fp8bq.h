@@ -74,8 +74,9 @@ typedef enum { FP8BQ_IN_BF16 = 0, FP8BQ_IN_F32 = 1 } fp8bq_in;
  * FP32 (the accumulator itself). */
 typedef enum { FP8BQ_OUT_BF16 = 0, FP8BQ_OUT_F32 = 1 } fp8bq_out;
 
-/* GEMM selector for fp8bq_gemm_workspace_size and fp8bq_gemm_plan. */
-typedef enum { FP8BQ_OP_FPROP = 0, FP8BQ_OP_DGRAD = 1, FP8BQ_OP_WGRAD = 2 } fp8bq_op;
+/* GEMM selector for fp8bq_gemm_workspace_size and fp8bq_gemm_plan (FP8BQ_OP_DGRAD_WT:
+ * fp8bq_gemm_dgrad_wt). */
+typedef enum { FP8BQ_OP_FPROP = 0, FP8BQ_OP_DGRAD = 1, FP8BQ_OP_WGRAD = 2, FP8BQ_OP_DGRAD_WT = 3 } fp8bq_op;
 
 /*
  * Activation quantization, one scale per 1x128 group (128 consecutive elements of a row).
@@ -109,6 +110,16 @@ int fp8bq_quantize_act_1x128(const void* x, fp8bq_in xt, int64_t R, int64_t C, i
 int fp8bq_quantize_act_128x1(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx,
                              fp8bq_fp8 fmt, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst,
                              void* stream);
+
+/*
+ * Weight quantization with a transposed copy of the codes, from one read of w: q and s exactly as
+ * fp8bq_quantize_weight_128x128, plus qt [K, N] with qt[k*ldqt + n] = q[n*ldq + k] (ldqt >= N,
+ * ldqt % 16 == 0), the operand layout of fp8bq_gemm_dgrad_wt.  N % 128 == 0; K % 128 == 0.  No
+ * output may overlap w or another output.  Defining passages: as fp8bq_quantize_weight_128x128.
+ */
+int fp8bq_quantize_weight_dual(const void* w, fp8bq_in wt, int64_t N, int64_t K, int64_t ldw, fp8bq_fp8 fmt,
+                               uint8_t* q, int64_t ldq, float* s, int64_t lds, uint8_t* qt, int64_t ldqt,
+                               void* stream);
 
 /*
  * Both activation layouts from one read of x: the outputs of
@@ -181,6 +192,18 @@ int fp8bq_gemm_dgrad(int64_t M, int64_t N, int64_t K,
                      const uint8_t* qdy, int64_t ldqdy, const float* sdy, int64_t ldsdy, fp8bq_fp8 fdy,
                      const uint8_t* qw, int64_t ldqw, const float* sw, int64_t ldsw, fp8bq_fp8 fw,
                      void* dx, fp8bq_out dxt, int64_t lddx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dgrad with the weight codes already transposed: the result of fp8bq_gemm_dgrad, computed from
+ * qwt [K, N] (ldqwt >= N), the W^T codes of fp8bq_quantize_weight_dual, instead of qw.  No
+ * transpose runs, so the workspace holds only split partial sums:
+ * fp8bq_gemm_workspace_size(FP8BQ_OP_DGRAD_WT, M, N, K) bytes (often 0; ws may then be NULL).
+ * Other arguments as fp8bq_gemm_dgrad (sw: the weight scales, [N/128][K/128]).
+ */
+int fp8bq_gemm_dgrad_wt(int64_t M, int64_t N, int64_t K,
+                        const uint8_t* qdy, int64_t ldqdy, const float* sdy, int64_t ldsdy, fp8bq_fp8 fdy,
+                        const uint8_t* qwt, int64_t ldqwt, const float* sw, int64_t ldsw, fp8bq_fp8 fw,
+                        void* dx, fp8bq_out dxt, int64_t lddx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Weight-gradient GEMM  dW[N, K] = dY[M, N]^T . X[M, K]  (contraction over the M tokens):

@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fq.lib()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -74,6 +74,8 @@ def test_valid_arguments_reach_the_device_check():
     assert qw() == DEVICE
     assert qw(lds=3) == DEVICE  # weight scales need no ld alignment
     assert qdual() == DEVICE
+    assert qwdual() == DEVICE
+    assert gemm("fp8bq_gemm_dgrad_wt", ws=NUL, ws_bytes=0) == DEVICE  # no transpose: no workspace
 
 
 def test_quant_1x128_validation():
@@ -161,16 +163,16 @@ def test_gemm_plan_query():
     a, b, c = i32(-1), i32(-1), i32(-1)
     ref = lambda v: ctypes.cast(ctypes.byref(v), ctypes.c_void_p)
     assert lib.fp8bq_gemm_plan(0, 256, 256, 256, NUL, ref(b), ref(c)) == NULL
-    assert lib.fp8bq_gemm_plan(3, 256, 256, 256, ref(a), ref(b), ref(c)) == SHAPE
+    assert lib.fp8bq_gemm_plan(4, 256, 256, 256, ref(a), ref(b), ref(c)) == SHAPE
     assert lib.fp8bq_gemm_plan(0, -1, 256, 256, ref(a), ref(b), ref(c)) == SHAPE
     assert a.value == -1 and b.value == -1 and c.value == -1
-    for op in (fq.OP_FPROP, fq.OP_DGRAD, fq.OP_WGRAD):
+    for op in (fq.OP_FPROP, fq.OP_DGRAD, fq.OP_WGRAD, fq.OP_DGRAD_WT):
         for (M, N, K) in [(256, 256, 256), (512, 2048, 2048), (16384, 2560, 2048), (16384, 11264, 2048),
                           (16384, 2048, 5632)]:
             tm, tn, sk = fq.fp8bq_gemm_plan(op, M, N, K)
             assert (tm, tn) in [(128, 128), (128, 256), (256, 128), (256, 256)]
             assert 1 <= sk <= 8
-            rows, cols = {fq.OP_FPROP: (M, N), fq.OP_DGRAD: (M, K), fq.OP_WGRAD: (N, K)}[op]
+            rows, cols = {fq.OP_FPROP: (M, N), fq.OP_DGRAD: (M, K), fq.OP_WGRAD: (N, K), fq.OP_DGRAD_WT: (M, K)}[op]
             ws = fq.fp8bq_gemm_workspace_size(op, M, N, K)
             transpose = ((N * K + 255) // 256) * 256 if op == fq.OP_DGRAD else 0
             assert ws == transpose + (sk * rows * cols * 4 if sk > 1 else 0)
@@ -192,3 +194,26 @@ def test_quant_dual_validation():
     assert qdual(qt=P(1)) == OVERLAP  # the two code arrays coincide
     assert qdual(st=P(2)) == OVERLAP
     assert qdual(s=P(0)) == OVERLAP  # scales on top of the input
+
+
+def qwdual(w=P(0), wt=0, N=256, K=256, ldw=256, fmt=0, q=P(1), ldq=256, s=P(2), lds=2, qt=P(3), ldqt=256):
+    return fq.lib().fp8bq_quantize_weight_dual(w, wt, N, K, ldw, fmt, q, ldq, s, lds, qt, ldqt, S0)
+
+
+def test_quant_weight_dual_validation():
+    assert qwdual(N=0) == OK
+    assert qwdual(wt=3) == DTYPE and qwdual(fmt=5) == FORMAT
+    assert qwdual(N=200) == SHAPE and qwdual(K=100, ldw=112, ldq=112) == SHAPE
+    assert qwdual(qt=NUL) == NULL
+    assert qwdual(ldqt=200) == LD  # ldqt >= N
+    assert qwdual(ldqt=264) == LD  # 16-byte rows
+    assert qwdual(qt=P(1)) == OVERLAP and qwdual(qt=P(0)) == OVERLAP
+
+
+def test_gemm_dgrad_wt_validation():
+    g = "fp8bq_gemm_dgrad_wt"
+    assert gemm(g, K=200) == SHAPE and gemm(g, N=200) == SHAPE
+    assert gemm(g, qb=NUL) == NULL
+    assert gemm(g, out=P(2)) == OVERLAP
+    assert gemm(g, ldqb=100) == LD  # W^T rows hold N codes
+    assert fq.fp8bq_gemm_workspace_size(fq.OP_DGRAD_WT, 16384, 11264, 2048) < 11264 * 2048  # no transpose buffer

@@ -319,3 +319,30 @@ def test_large_tile_wgrad(shape):
     dY = synth.random_bf16((M, N), seed=305 + N, std=1e-3)
     X = synth.random_bf16((M, K), seed=306 + K, outliers=True)
     checked(run_wgrad(dY, X, ncols=_sample(N, 160, 7), kcols=_sample(K, 160, 8)), f"256x256 wgrad {shape} split {split}")
+
+
+# ------------------------------------------------------------------------------------------
+# dgrad on pre-transposed weight codes
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(256, 256, 384), (300, 640, 256), (4200, 2048, 2432)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_dgrad_wt_matches_dgrad_and_oracle(shape, out_dtype):
+    """fp8bq_gemm_dgrad_wt on the W^T codes of fp8bq_quantize_weight_dual gives fp8bq_gemm_dgrad's
+    result bit for bit (same kernel, no transpose pass), and holds the oracle tolerance."""
+    M, N, K = shape
+    dY = synth.random_bf16((M, N), seed=401 + M, std=1e-3)
+    W = synth.random_bf16((N, K), seed=402 + K, std=0.02)
+    qdy, sdy = fq.quantize_act_1x128(dY.to(DEV), fq.E5M2)
+    qw, sw, qwt = fq.quantize_weight_dual(W.to(DEV), fq.E4M3)
+    ref = fq.gemm_dgrad(qdy, sdy, qw, sw, fq.E5M2, fq.E4M3, out_dtype=out_dtype)
+    got = fq.gemm_dgrad_wt(qdy, sdy, qwt, sw, fq.E5M2, fq.E4M3, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref), "dgrad_wt differs from dgrad"
+    rows = _sample(M, 128, 9)
+    oq, os_ = oracle.quant_act_1x128(dY[rows].float().numpy(), E5)
+    oqw, osw = oracle.quant_weight_128x128(W.float().numpy(), E4)
+    a = oracle.dequant_act_1x128(oq, os_, E5)
+    b = oracle.dequant_weight_128x128(oqw, osw, E4)
+    checked((to_np_f64(got[torch.from_numpy(rows).to(DEV)]), a @ b, row_norms(a), row_norms(b.T)),
+            f"dgrad_wt {shape}", out_dtype == torch.float32)

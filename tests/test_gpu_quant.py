@@ -313,3 +313,33 @@ def test_dual_decoder_block_sampled(name):
         xc = np.ascontiguousarray(x[:, cols].float().numpy())
         same((qt.cpu().numpy()[cols].T, st.cpu().numpy()[:, cols]), oracle.quant_act_128x1(xc, fc),
              f"dual {name} {key} 128x1")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(128, 128), (384, 256), (256, 640)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_weight_dual_shapes(fmt, shape, dt):
+    """Weight codes, scales and the transposed codes from one pass: all bit-identical to the oracle."""
+    N, K = shape
+    w = synth.random_bf16(shape, seed=N + 2 * K, std=0.02) if dt == "bf16" else synth.random_f32(shape, seed=N + 2 * K)
+    q, s, qt = fq.quantize_weight_dual(w.to(DEV), FP[fmt])
+    torch.cuda.synchronize()
+    oq, os_ = oracle.quant_weight_128x128(w.float().numpy(), fmt)
+    same((q.cpu().numpy(), s.cpu().numpy()), (oq, os_), f"weight dual {shape} {dt}")
+    assert np.array_equal(qt.cpu().numpy(), oq.T), "transposed codes"
+
+
+def test_weight_dual_full_size_and_edges():
+    c = synth.config3_linear("gate_up")
+    W = c["W"]
+    q, s, qt = fq.quantize_weight_dual(W.to(DEV), fq.E4M3)
+    torch.cuda.synchronize()
+    oq, os_ = oracle.quant_weight_128x128(W.float().numpy(), oracle.E4M3)
+    same((q.cpu().numpy(), s.cpu().numpy()), (oq, os_), "gate_up W dual")
+    assert np.array_equal(qt.cpu().numpy(), oq.T)
+    x = _edge_matrix()
+    q, s, qt = fq.quantize_weight_dual(x.to(DEV), fq.E5M2)
+    torch.cuda.synchronize()
+    oq, os_ = oracle.quant_weight_128x128(x.float().numpy(), oracle.E5M2)
+    same((q.cpu().numpy(), s.cpu().numpy()), (oq, os_), "edge weight dual")
+    assert np.array_equal(qt.cpu().numpy(), oq.T)
