@@ -361,13 +361,15 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   };
   auto streamed = [&](const uint8_t* stg, int o) { return STREAM_B ? bpatch(stg, o) : apatch(stg, o); };
   auto resident = [&](const uint8_t* stg, int k) { return STREAM_B ? apatch(stg, k) : bpatch(stg, k); };
-  // The next block's first reads (its resident patches and first streamed patch), in the order the
-  // current block's tail frees their registers: read h goes out at tail step 2 + 2h.
-  constexpr int NHEAD = NIN + 1;
+  // Streamed patches are read RA patches ahead of their first MFMA (two where the registers allow).
+  constexpr int RA = (PERM && NOUT >= 3) ? 2 : 1;
+  // The next block's first reads (its resident patches and first RA streamed patches), in the order
+  // the current block's tail frees their registers: read h goes out at tail step 2 + 2h.
+  constexpr int NHEAD = NIN + RA;
   auto head_read = [&](const uint8_t* stg, int h, v8i* res, v8i* str) {
     if (h == 0) res[0] = resident(stg, 0);
-    else if (h == 1) str[0] = streamed(stg, 0);
-    else res[h - 1] = resident(stg, h - 1);
+    else if (h <= RA) str[h - 1] = streamed(stg, h - 1);
+    else res[h - RA] = resident(stg, h - RA);
   };
 
   // prologue: every ring slot's block in flight, the first landed, its first reads issued
@@ -411,7 +413,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
       if (u < NTILE) {
         int o, k;
         order(u, o, k);
-        if (k == 0 && o + 1 < NOUT) str[o + 1] = streamed(stage, o + 1);
+        if (k == 0 && o + RA < NOUT) str[o + RA] = streamed(stage, o + RA);
         p[u] = STREAM_B ? mfma_block<FA, FB>(str[o], res[k]) : mfma_block<FA, FB>(res[k], str[o]);
       }
       if (u == UB) stage_barrier();

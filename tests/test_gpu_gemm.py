@@ -8,6 +8,8 @@ on the error beyond the BF16 output rounding).  Small cases compare every output
 full-size workloads compare sampled rows / columns computed one by one by the oracle.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -19,6 +21,7 @@ from parity import FP, check_gemm, row_norms, say, to_np_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+TILE_FORCED = "FP8BQ_GEMM_TILE" in os.environ  # the planner's tile choice is overridden (tuning runs)
 E4, E5 = oracle.E4M3, oracle.E5M2
 
 
@@ -298,12 +301,12 @@ def test_large_tile_ragged_edges(out_dtype):
     output (4200 = 16*256 + 104 rows; 2432 = 9.5 tiles of columns); every output compared."""
     f32 = out_dtype == torch.float32
     M, N, K = 4200, 2432, 2048
-    assert fq.fp8bq_gemm_plan(fq.OP_FPROP, M, N, K)[:2] == (256, 256)
+    assert TILE_FORCED or fq.fp8bq_gemm_plan(fq.OP_FPROP, M, N, K)[:2] == (256, 256)
     X = synth.random_bf16((M, K), seed=301, outliers=True)
     W = synth.random_bf16((N, K), seed=302, std=0.02)
     checked(run_fprop(X, W, out_dtype=out_dtype), "256x256 ragged fprop", f32)
     Md, Nd, Kd = 4200, 2048, 2432
-    assert fq.fp8bq_gemm_plan(fq.OP_DGRAD, Md, Nd, Kd)[:2] == (256, 256)
+    assert TILE_FORCED or fq.fp8bq_gemm_plan(fq.OP_DGRAD, Md, Nd, Kd)[:2] == (256, 256)
     dY = synth.random_bf16((Md, Nd), seed=303, std=1e-3)
     Wd = synth.random_bf16((Nd, Kd), seed=304, std=0.02)
     checked(run_dgrad(dY, Wd, out_dtype=out_dtype), "256x256 ragged dgrad", f32)
@@ -315,7 +318,7 @@ def test_large_tile_wgrad(shape):
     contraction (FP32 partial sums)."""
     M, N, K = shape
     tm, tn, split = fq.fp8bq_gemm_plan(fq.OP_WGRAD, M, N, K)
-    assert (tm, tn) == (256, 256)
+    assert TILE_FORCED or (tm, tn) == (256, 256)
     dY = synth.random_bf16((M, N), seed=305 + N, std=1e-3)
     X = synth.random_bf16((M, K), seed=306 + K, outliers=True)
     checked(run_wgrad(dY, X, ncols=_sample(N, 160, 7), kcols=_sample(K, 160, 8)), f"256x256 wgrad {shape} split {split}")
