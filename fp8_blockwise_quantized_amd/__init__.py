@@ -29,7 +29,8 @@ Allocating helpers (outputs created with torch on the input's device):
     gemm_fprop(qx, sx, qw, sw, fx=E4M3, fw=E4M3, out_dtype=bf16) -> y [M, N]
     gemm_dgrad(qdy, sdy, qw, sw, fdy=E4M3, fw=E4M3, out_dtype=bf16) -> dx [M, K]
     gemm_dgrad_wt(qdy, sdy, qwt, sw, fdy=E4M3, fw=E4M3, out_dtype=bf16) -> dx [M, K] (qwt = W^T codes)
-    gemm_wgrad(qdyt, sdyt, qxt, sxt, fdy=E4M3, fx=E4M3, out_dtype=bf16) -> dw [N, K]
+    gemm_wgrad(qdyt, sdyt, qxt, sxt, fdy=E4M3, fx=E4M3, out_dtype=bf16, accumulate=False) -> dw [N, K]
+        (accumulate=True: out, an FP32 main-grad buffer, receives out + dW)
 """
 
 import ctypes
@@ -43,6 +44,7 @@ IN_BF16 = 0
 IN_F32 = 1
 OUT_BF16 = 0
 OUT_F32 = 1
+OUT_F32_ACCUM = 2  # wgrad only: the FP32 output receives out + result
 OP_FPROP = 0
 OP_DGRAD = 1
 OP_WGRAD = 2
@@ -223,12 +225,13 @@ def fp8bq_gemm_dgrad_wt(qdy, sdy, fdy, qwt, sw, fw, dx, ws=None):
            "fp8bq_gemm_dgrad_wt")
 
 
-def fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None):
+def fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None, accumulate=False):
     N, M = qdyt.shape
     K = qxt.shape[0]
     wsp, wsb = _ws_args(ws)
+    ot = OUT_F32_ACCUM if accumulate else _out_type(dw)
     _check(lib().fp8bq_gemm_wgrad(M, N, K, _ptr(qdyt), _ld(qdyt), _ptr(sdyt), _ld(sdyt), fdy, _ptr(qxt), _ld(qxt),
-                                  _ptr(sxt), _ld(sxt), fx, _ptr(dw), _out_type(dw), _ld(dw), wsp, wsb, _stream(dw)),
+                                  _ptr(sxt), _ld(sxt), fx, _ptr(dw), ot, _ld(dw), wsp, wsb, _stream(dw)),
            "fp8bq_gemm_wgrad")
 
 
@@ -321,11 +324,15 @@ def gemm_dgrad_wt(qdy, sdy, qwt, sw, fdy=E4M3, fw=E4M3, out_dtype=torch.bfloat16
     return dx
 
 
-def gemm_wgrad(qdyt, sdyt, qxt, sxt, fdy=E4M3, fx=E4M3, out_dtype=torch.bfloat16, out=None, ws=None):
+def gemm_wgrad(qdyt, sdyt, qxt, sxt, fdy=E4M3, fx=E4M3, out_dtype=torch.bfloat16, out=None, ws=None,
+               accumulate=False):
+    """accumulate=True adds the result to `out` (an FP32 main-grad buffer) instead of overwriting it."""
     N, M = qdyt.shape
     K = qxt.shape[0]
+    if accumulate and (out is None or out.dtype != torch.float32):
+        raise ValueError("accumulate=True needs an FP32 `out` tensor holding the running sum")
     dw = out if out is not None else torch.empty((N, K), dtype=out_dtype, device=qdyt.device)
     if ws is None:
         ws = _workspace(OP_WGRAD, M, N, K, qdyt.device)
-    fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws)
+    fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws, accumulate=accumulate)
     return dw

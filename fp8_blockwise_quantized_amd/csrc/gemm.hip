@@ -473,7 +473,11 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
               if (CHK && !(mrow + 16 * i < M && ncol + jcol(j) < N)) continue;
-              *reinterpret_cast<v4f*>(ci + jcol(j)) = acc[i][j];
+              v4f* cij = reinterpret_cast<v4f*>(ci + jcol(j));
+              if (OUTF32 == 2 && nsplit == 1)
+                *cij = *cij + acc[i][j];
+              else
+                *cij = acc[i][j];
             }
           }
         } else if constexpr (PERM) {
@@ -524,7 +528,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
 }
 
 // Sum of the split partial sums in split order, converted to the output type:
-// out[m, n] = sum_s partial[s][m][n].
+// out[m, n] = sum_s partial[s][m][n]  (OUTF32 == 2: out[m, n] += that sum, in FP32).
 template <int OUTF32>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int nsplit, int64_t M,
                                                             int64_t N, void* __restrict__ out, int64_t ldo) {
@@ -533,7 +537,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     const int64_t m = i / (N / 4), n = 4 * (i - m * (N / 4));
     v4f s = *reinterpret_cast<const v4f*>(partial + m * N + n);
     for (int k = 1; k < nsplit; ++k) s += *reinterpret_cast<const v4f*>(partial + ((int64_t)k * M + m) * N + n);
-    if constexpr (OUTF32) {
+    if constexpr (OUTF32 == 2) {
+      v4f* o = reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + m * ldo + n);
+      *o = *o + s;
+    } else if constexpr (OUTF32) {
       *reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + m * ldo + n) = s;
     } else {
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + m * ldo + n) =
@@ -569,6 +576,9 @@ static hipError_t launch_formats(const GemmDesc& d, const GemmPlan& p, float* pa
 
 template <int OP, int SBM>
 static hipError_t launch_out(const GemmDesc& d, const GemmPlan& p, float* partial, hipStream_t st) {
+  if constexpr (OP == kOpWgrad) {
+    if (d.out_f32 == 2) return launch_formats<OP, SBM, 2>(d, p, partial, st);
+  }
   return d.out_f32 ? launch_formats<OP, SBM, 1>(d, p, partial, st) : launch_formats<OP, SBM, 0>(d, p, partial, st);
 }
 
@@ -585,7 +595,10 @@ hipError_t launch_gemm(int op, const GemmDesc& d, const GemmPlan& p, void* ws, h
   const int64_t total = d.M * (d.N / 4);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  if (d.out_f32)
+  if (d.out_f32 == 2)
+    hipLaunchKernelGGL(splitk_reduce_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, st, partial, p.split_k, d.M,
+                       d.N, d.c, d.ldc);
+  else if (d.out_f32)
     hipLaunchKernelGGL(splitk_reduce_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, partial, p.split_k, d.M,
                        d.N, d.c, d.ldc);
   else

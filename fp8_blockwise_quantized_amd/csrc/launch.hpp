@@ -43,7 +43,7 @@ struct GemmDesc {
   int64_t ldc;
   int64_t M, N, K;
   int fa, fb;    // FP8 format of A and B
-  int out_f32;   // 0: BF16 output, 1: FP32 output
+  int out_f32;   // 0: BF16 output, 1: FP32 output, 2: FP32 output accumulated into (c += result)
   int sb_mode;   // SbMode
 };
 

@@ -125,7 +125,7 @@ int validate_gemm(const GemmArgs& g, size_t ws_needed, bool* empty, bool* zero_f
   *zero_fill = false;
   if (g.op < 0 || g.op > 3) return kErrShape;
   if (!fmt_ok(g.fa) || !fmt_ok(g.fb)) return kErrFormat;
-  if (g.out_t != 0 && g.out_t != 1) return kErrDtype;
+  if (g.out_t != 0 && g.out_t != 1 && !(g.out_t == 2 && g.op == 2)) return kErrDtype;
   const int64_t M = g.M, N = g.N, K = g.K;
   if (M < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return kErrShape;
   if (g.op == 2 && M % 128 != 0) return kErrShape;

@@ -71,8 +71,12 @@ typedef enum { FP8BQ_E4M3 = 0, FP8BQ_E5M2 = 1 } fp8bq_fp8;
 typedef enum { FP8BQ_IN_BF16 = 0, FP8BQ_IN_F32 = 1 } fp8bq_in;
 
 /* Element type of a GEMM output: BF16 (round to nearest even from the FP32 accumulator), or
- * FP32 (the accumulator itself). */
-typedef enum { FP8BQ_OUT_BF16 = 0, FP8BQ_OUT_F32 = 1 } fp8bq_out;
+ * FP32 (the accumulator itself).  FP8BQ_OUT_F32_ACCUM (fp8bq_gemm_wgrad only) adds the FP32
+ * result to the FP32 values already in the output, for a main-grad buffer kept in FP32 across
+ * micro-batches: out = fp32(out + result).  The pages keep precision-sensitive state in BF16/FP32
+ * while the linear GEMMs run in FP8 ("Puro-2B" summary, method key points: FP8 blockwise mixed
+ * precision). */
+typedef enum { FP8BQ_OUT_BF16 = 0, FP8BQ_OUT_F32 = 1, FP8BQ_OUT_F32_ACCUM = 2 } fp8bq_out;
 
 /* GEMM selector for fp8bq_gemm_workspace_size and fp8bq_gemm_plan (FP8BQ_OP_DGRAD_WT:
  * fp8bq_gemm_dgrad_wt). */
@@ -213,7 +217,9 @@ int fp8bq_gemm_dgrad_wt(int64_t M, int64_t N, int64_t K,
  *
  *   qdyt/sdyt  from fp8bq_quantize_act_128x1(dY): qdyt [N, M] (ldqdyt >= M), sdyt [M/128][N].
  *   qxt/sxt    from fp8bq_quantize_act_128x1(X):  qxt [K, M] (ldqxt >= M),  sxt [M/128][K].
- *   dw         [N, K] output of type dwt, row stride lddw (>= K).
+ *   dw         [N, K] output of type dwt, row stride lddw (>= K).  With FP8BQ_OUT_F32_ACCUM, dw
+ *              holds FP32 values on entry and receives dw + dW (a zero-length contraction, M == 0,
+ *              leaves it unchanged); the other GEMMs reject that type with FP8BQ_ERR_DTYPE.
  *   M % 128 == 0; N % 128 == 0; K % 128 == 0.
  *   ws         at least fp8bq_gemm_workspace_size(FP8BQ_OP_WGRAD, M, N, K) bytes (FP32 partial
  *              sums when the contraction is split across workgroups).

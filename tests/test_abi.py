@@ -131,8 +131,13 @@ def test_gemm_validation():
         assert gemm(fn, ldsa=250) == LD
         assert gemm(fn, out=P(0)) == OVERLAP
         assert gemm(fn, M=0, qa=NUL, out=NUL) == OK
+        assert gemm(fn, out_t=2) == DTYPE  # FP32 accumulation is a wgrad option only
+    assert gemm("fp8bq_gemm_dgrad_wt", out_t=2, ws=NUL, ws_bytes=0) == DTYPE
     w = "fp8bq_gemm_wgrad"
     valid(lambda: gemm(w, ldsb=256))
+    valid(lambda: gemm(w, ldsb=256, out_t=2))
+    assert gemm(w, ldsb=256, out_t=3) == DTYPE
+    valid(lambda: gemm(w, M=0, qa=NUL, sa=NUL, qb=NUL, sb=NUL, ldsb=256, out_t=2))  # an empty sum
     assert gemm(w, M=200, ldqa=208, ldqb=208, ldsb=256) == SHAPE  # contraction must be a multiple of 128
     assert gemm(w, ldsb=2) == LD  # column scales are read as vectors
     # dgrad needs a workspace for the transposed weight codes

@@ -349,3 +349,56 @@ def test_dgrad_wt_matches_dgrad_and_oracle(shape, out_dtype):
     b = oracle.dequant_weight_128x128(oqw, osw, E4)
     checked((to_np_f64(got[torch.from_numpy(rows).to(DEV)]), a @ b, row_norms(a), row_norms(b.T)),
             f"dgrad_wt {shape}", out_dtype == torch.float32)
+
+
+# ------------------------------------------------------------------------------------------
+# FP32 main-grad accumulation (wgrad epilogue option)
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(1024, 256, 256), (512, 2048, 1536), (4096, 4480, 2432)])
+def test_wgrad_fp32_accumulate(shape):
+    """Two micro-batches accumulated into one FP32 buffer that starts non-zero:
+    out = out0 + dW1 + dW2, each GEMM as accurate as the FP32-output wgrad (1e-4 of |a||b|) and each
+    addition one FP32 rounding (2^-24 of the running magnitude).  The shapes cover the split
+    (partial sums added by the reduction pass) and unsplit (added in the GEMM's own epilogue) paths."""
+    M, N, K = shape
+    rng = np.random.default_rng(M + N + K)
+    ncols, kcols = np.sort(rng.choice(N, 48, replace=False)), np.sort(rng.choice(K, 48, replace=False))
+    out0 = torch.from_numpy(rng.standard_normal((N, K)).astype(np.float32) * 0.3)
+    out = out0.to(DEV)
+    ref = out0.numpy().astype(np.float64)[np.ix_(ncols, kcols)]
+    mag = np.abs(ref)
+    bound = np.zeros_like(ref)
+    for mb in range(2):
+        dY = synth.random_bf16((M, N), seed=7000 + 10 * mb + M, std=1e-3)
+        X = synth.random_bf16((M, K), seed=7001 + 10 * mb + K, outliers=True)
+        qdyt, sdyt = fq.quantize_act_128x1(dY.to(DEV))
+        qxt, sxt = fq.quantize_act_128x1(X.to(DEV))
+        fq.gemm_wgrad(qdyt, sdyt, qxt, sxt, out=out, accumulate=True)
+        oq, os_ = oracle.quant_act_128x1(np.ascontiguousarray(dY[:, ncols].float().numpy()), E4)
+        oqx, osx = oracle.quant_act_128x1(np.ascontiguousarray(X[:, kcols].float().numpy()), E4)
+        a = oracle.dequant_act_128x1(oq, os_, E4)
+        b = oracle.dequant_act_128x1(oqx, osx, E4)
+        y64 = a.T @ b
+        ref = ref + y64
+        mag = mag + np.abs(y64)
+        bound = bound + np.outer(row_norms(a.T), row_norms(b.T))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)[np.ix_(ncols, kcols)]
+    err = np.abs(got - ref)
+    lim = 1e-4 * bound + 2.0 ** -23 * mag
+    worst = float(np.max(err / lim))
+    assert np.all(err <= lim), f"accumulate {shape}: max err / limit = {worst:.3f}"
+    split = fq.fp8bq_gemm_plan(fq.OP_WGRAD, M, N, K)[2]
+    say(f"wgrad accumulate {shape} (split {split}): max err / limit = {worst:.3f}")
+
+
+def test_wgrad_accumulate_paths_and_empty_sum():
+    splits = {fq.fp8bq_gemm_plan(fq.OP_WGRAD, *s)[2] > 1 for s in [(1024, 256, 256), (512, 2048, 1536)]}
+    assert splits == {True, False}  # the cases above reach both epilogues
+    # a zero-length contraction adds nothing: the buffer is left as it was
+    out = torch.full((128, 256), 3.25, dtype=torch.float32, device=DEV)
+    st = fq.lib().fp8bq_gemm_wgrad(0, 128, 256, None, 16, None, 128, 0, None, 16, None, 256, 0, out.data_ptr(),
+                                   fq.OUT_F32_ACCUM, 256, None, 0, None)
+    torch.cuda.synchronize()
+    assert st == 0 and torch.all(out == 3.25)
