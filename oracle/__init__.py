@@ -18,6 +18,8 @@ Sources (cited by page title and section; the pages are the authority):
         section "常见错误：直接转换而不加 Scale" fix the quantize rule
         (scale = amax / fmt_max with a 1e-12 floor, divide, clamp, cast) and
         the dequantize rule (code value times scale).
+  The same listing's running (EMA) amax with one scale per tensor is the
+        per-tensor delayed-scaling variant in ``delayed.py``.
 * [XZY] "小团队也能预训练！普罗2B：RTX5090训练成本不到5090美元" (66bd.net,
         新智元), paragraph "FP8发挥RTX 5090的低精度效率优势": fine-grained
         block quantization after DeepSeek-V3, main linear GEMMs in FP8,
@@ -62,4 +64,13 @@ from .gemm import (  # noqa: F401
     gemm_fprop_blockloops,
     gemm_dgrad_blockloops,
     gemm_wgrad_blockloops,
+)
+from .delayed import (  # noqa: F401
+    amax_ema_update,
+    dequant_tensor,
+    ema_constants,
+    gemm_tensor,
+    quant_tensor,
+    quant_tensor_delayed,
+    tensor_scale,
 )
