@@ -8,7 +8,11 @@ One step = the whole path for one synthetic 2B-class decoder block at M = 16384 
     quantize dY both ways in one pass, dgrad dX = dY W, wgrad dW = dY^T X
 i.e. 12 quantize passes and 12 GEMMs, all E4M3, BF16 in and out, inputs resident in HBM.
 
-    python bench.py [--steps K] [--warmup W] [--workload decoder|linear|sweep] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload decoder|delayed|linear|sweep] [--no-cpu-baseline]
+
+`--workload delayed` runs the same decoder-block step with per-tensor delayed scaling instead (one
+running amax and one scale per tensor, X / W / dY each quantized once with transposed codes, the
+three GEMMs with per-tensor scales): the pages' own alternative recipe, as a comparison point.
 
 Prints ONE JSON line on stdout.  `value` = GEMM FLOPs of the step / wall time of the step (the
 quantize passes are inside the timed step).  `breakdown` holds per-product TFLOP/s and per-pass GB/s
@@ -40,7 +44,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", choices=["decoder", "linear", "sweep"], default="decoder")
+    p.add_argument("--workload", choices=["decoder", "delayed", "linear", "sweep"], default="decoder")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=4096)
     p.add_argument("--calibrate", action="store_true",
@@ -78,6 +82,8 @@ def main():
 
     if args.workload == "decoder":
         ops, bufs, desc = build_decoder(torch, fq, synth, dev)
+    elif args.workload == "delayed":
+        ops, bufs, desc = build_delayed(torch, fq, synth, dev)
     elif args.workload == "linear":
         ops, bufs, desc = build_linear(torch, fq, synth, dev)
     else:
@@ -121,7 +127,7 @@ def main():
 
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     breakdown = summarize(ops, dur_ms)
-    roof = roofline(fq, ops, dur_ms)
+    roof = roofline(fq, ops, dur_ms, with_traffic=args.workload == "decoder")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -144,7 +150,7 @@ def main():
         "cpu_baseline": None,
     }
     del bufs
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "decoder":
         out["cpu_baseline"] = cpu_baseline(args.cpu_tokens, desc)
     print(json.dumps(out), flush=True)
 
@@ -207,7 +213,7 @@ def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True):
     ops = [
         quant_x,
         quant_w,
-        dict(name=f"{name}.fprop", kind="fprop", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
+        dict(name=f"{name}.fprop", kind="fprop", bytes=0, flops=2 * M * N * K, plan=(fq.OP_FPROP, M, N, K), kid=(0, 0),
              fn=lambda: fq.fp8bq_gemm_fprop(qx, sx, E4, qw, sw, E4, y, ws_f)),
     ]
     if with_backward:
@@ -220,10 +226,10 @@ def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True):
         ops += [
             dict(name=f"{name}.quant_dy_dual", kind="quant_dual", bytes=_qdual_bytes(M, N), flops=0,
                  fn=lambda: fq.fp8bq_quantize_act_dual(dY, E4, qdy, sdy, E4, qdyt, sdyt)),
-            dict(name=f"{name}.dgrad", kind="dgrad", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
-                 fn=lambda: fq.fp8bq_gemm_dgrad_wt(qdy, sdy, E4, qwt, sw, E4, dx, ws_d)),
-            dict(name=f"{name}.wgrad", kind="wgrad", bytes=0, flops=2 * M * N * K, shape=(M, N, K),
-                 fn=lambda: fq.fp8bq_gemm_wgrad(qdyt, sdyt, E4, qxt, sxt, E4, dw, ws_w)),
+            dict(name=f"{name}.dgrad", kind="dgrad", bytes=0, flops=2 * M * N * K, plan=(fq.OP_DGRAD_WT, M, N, K),
+                 kid=(1, 0), fn=lambda: fq.fp8bq_gemm_dgrad_wt(qdy, sdy, E4, qwt, sw, E4, dx, ws_d)),
+            dict(name=f"{name}.wgrad", kind="wgrad", bytes=0, flops=2 * M * N * K, plan=(fq.OP_WGRAD, M, N, K),
+                 kid=(2, 1), fn=lambda: fq.fp8bq_gemm_wgrad(qdyt, sdyt, E4, qxt, sxt, E4, dw, ws_w)),
         ]
         bufs += [qdy, sdy, dx, qdyt, sdyt, dw, ws_d, ws_w]
     return ops, bufs
@@ -247,6 +253,69 @@ def build_decoder(torch, fq, synth, dev):
         "linears": [[n, k, nn] for n, k, nn in synth.DECODER_LINEARS],
         "gemms_per_step": 12,
         "quant_passes_per_step": 12,
+    }
+    return ops, bufs, desc
+
+
+def _qtensor_bytes(R, C, transpose, in_bytes=2):
+    # algorithmic: one read of the input and the codes (twice with the transposed copy); the
+    # kernels read the input a second time, after the whole-tensor amax is known
+    return R * C * in_bytes + R * C * (2 if transpose else 1) + 8
+
+
+def delayed_linear_ops(torch, fq, name, X, W, dY, dev):
+    """One linear's step with per-tensor delayed scaling: X, W and dY each quantized once (codes and
+    their transpose) against their running amax (beta 0.99), then fprop, dgrad and wgrad as per-tensor
+    GEMMs on those codes."""
+    M, K = X.shape
+    N = W.shape[0]
+    E4 = fq.E4M3
+    u8 = lambda r, c: torch.empty((r, c), dtype=torch.uint8, device=dev)
+    one = lambda: torch.ones(1, dtype=torch.float32, device=dev)
+    qx, qxt, qw, qwt, qdy, qdyt = u8(M, K), u8(K, M), u8(N, K), u8(K, N), u8(M, N), u8(N, M)
+    ax, aw, ady, sx, sw, sdy = one(), one(), one(), one(), one(), one()
+    wsq = torch.empty(max(fq.fp8bq_quantize_tensor_workspace_size(M, max(K, N)), 16), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    ws_f = fq._workspace(fq.OP_TENSOR, M, N, K, dev)
+    ws_d = fq._workspace(fq.OP_TENSOR, M, K, N, dev)
+    ws_w = fq._workspace(fq.OP_TENSOR, N, K, M, dev)
+    ops = [
+        dict(name=f"{name}.quant_x_tensor", kind="quant_tensor", bytes=_qtensor_bytes(M, K, True), flops=0,
+             fn=lambda: fq.fp8bq_quantize_tensor_delayed(X, E4, ax, 0.99, qx, qxt, sx, wsq)),
+        dict(name=f"{name}.quant_w_tensor", kind="quant_tensor", bytes=_qtensor_bytes(N, K, True), flops=0,
+             fn=lambda: fq.fp8bq_quantize_tensor_delayed(W, E4, aw, 0.99, qw, qwt, sw, wsq)),
+        dict(name=f"{name}.fprop", kind="fprop", bytes=0, flops=2 * M * N * K, plan=(fq.OP_TENSOR, M, N, K),
+             kid=(0, 0), fn=lambda: fq.fp8bq_gemm_tensor(qx, sx, E4, qw, sw, E4, y, ws_f)),
+        dict(name=f"{name}.quant_dy_tensor", kind="quant_tensor", bytes=_qtensor_bytes(M, N, True), flops=0,
+             fn=lambda: fq.fp8bq_quantize_tensor_delayed(dY, E4, ady, 0.99, qdy, qdyt, sdy, wsq)),
+        dict(name=f"{name}.dgrad", kind="dgrad", bytes=0, flops=2 * M * N * K, plan=(fq.OP_TENSOR, M, K, N),
+             kid=(0, 0), fn=lambda: fq.fp8bq_gemm_tensor(qdy, sdy, E4, qwt, sw, E4, dx, ws_d)),
+        dict(name=f"{name}.wgrad", kind="wgrad", bytes=0, flops=2 * M * N * K, plan=(fq.OP_TENSOR, N, K, M),
+             kid=(0, 0), fn=lambda: fq.fp8bq_gemm_tensor(qdyt, sdy, E4, qxt, sx, E4, dw, ws_w)),
+    ]
+    bufs = [qx, qxt, qw, qwt, qdy, qdyt, ax, aw, ady, sx, sw, sdy, wsq, y, dx, dw, ws_f, ws_d, ws_w]
+    return ops, bufs
+
+
+def build_delayed(torch, fq, synth, dev):
+    log("generating the decoder-block inputs ...")
+    ops, bufs = [], []
+    for name, K, N in synth.DECODER_LINEARS:
+        c = synth.config3_linear(name)
+        X, W, dY = c["X"].to(dev), c["W"].to(dev), c["dY"].to(dev)
+        o, b = delayed_linear_ops(torch, fq, name, X, W, dY, dev)
+        ops += o
+        bufs += b + [X, W, dY]
+    desc = {
+        "workload": "decoder block fprop+dgrad+wgrad, M=16384 tokens, shapes as the blockwise step; per-tensor "
+                    "delayed scaling (running amax, beta 0.99, one scale per tensor), E4M3, X / W / dY each "
+                    "quantized once with transposed codes; BF16 in/out",
+        "tokens": synth.DECODER_M,
+        "linears": [[n, k, nn] for n, k, nn in synth.DECODER_LINEARS],
+        "gemms_per_step": 12,
+        "quant_calls_per_step": 12,
     }
     return ops, bufs, desc
 
@@ -316,15 +385,13 @@ def summarize(ops, dur_ms):
 # stages, scale mode, fmtA, fmtB, f32 out>; the tile shape comes from the library's plan query.
 _TILE_ARGS = {(128, 128): "128, 128, 2, 2, 2", (128, 256): "128, 256, 2, 4, 2", (256, 128): "256, 128, 4, 2, 2",
               (256, 256): "256, 256, 2, 4, 2"}
-_OP_ID = {"fprop": 0, "dgrad": 1, "wgrad": 2}
-
-
-def gemm_kernel(fq, kind, M, N, K):
-    """(kernel name, isolated): isolated when the call launches that one kernel (a split
-    contraction adds a reduction pass).  The step's dgrad runs on pre-transposed weight codes."""
-    op = fq.OP_DGRAD_WT if kind == "dgrad" else _OP_ID[kind]
-    tm, tn, split = fq.fp8bq_gemm_plan(op, M, N, K)
-    name = (f"void fp8bq::gemm_tn_kernel<{_OP_ID[kind]}, {_TILE_ARGS[(tm, tn)]}, {1 if kind == 'wgrad' else 0}, "
+def gemm_kernel(fq, o):
+    """(kernel name, isolated) of a GEMM op: o["plan"] is its plan query (op, M, N, K) and o["kid"]
+    the kernel's (OP, scale mode) template arguments.  Isolated when the call launches that one kernel
+    (a split contraction adds a reduction pass)."""
+    tm, tn, split = fq.fp8bq_gemm_plan(*o["plan"])
+    kop, sbm = o["kid"]
+    name = (f"void fp8bq::gemm_tn_kernel<{kop}, {_TILE_ARGS[(tm, tn)]}, {sbm}, "
             f"0, 0, 0>(fp8bq::GemmDesc, unsigned int, unsigned int, int, float*)")
     return name, split == 1
 
@@ -346,7 +413,7 @@ def _traffic(kernel):
         return None
 
 
-def roofline(fq, ops, dur_ms):
+def roofline(fq, ops, dur_ms, with_traffic=True):
     """The dominant GEMM kernel among those whose every launch in the step is that kernel alone:
     achieved = its algorithmic FLOPs per launch / its mean launch duration (HIP events on the launch
     stream, one pair per call), over all of its launches in the step."""
@@ -354,7 +421,7 @@ def roofline(fq, ops, dur_ms):
     for o, d in zip(ops, dur_ms):
         if not o["flops"]:
             continue
-        name, isolated = gemm_kernel(fq, o["kind"], *o["shape"])
+        name, isolated = gemm_kernel(fq, o)
         g = groups.setdefault(name, {"ok": True, "sel": []})
         g["ok"] &= isolated
         g["sel"].append((o, float(d)))
@@ -372,7 +439,7 @@ def roofline(fq, ops, dur_ms):
         "peak": FP8_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-        "traffic": _traffic(name),
+        "traffic": _traffic(name) if with_traffic else None,
         "launches_per_step": len(sel),
         "launches": [o["name"] for o, _ in sel],
         "flops_per_launch": flops_per_launch,

@@ -30,6 +30,9 @@ Allocating helpers (outputs created with torch on the input's device):
     gemm_dgrad(qdy, sdy, qw, sw, fdy=E4M3, fw=E4M3, out_dtype=bf16) -> dx [M, K]
     gemm_dgrad_wt(qdy, sdy, qwt, sw, fdy=E4M3, fw=E4M3, out_dtype=bf16) -> dx [M, K] (qwt = W^T codes)
     gemm_wgrad(qdyt, sdyt, qxt, sxt, fdy=E4M3, fx=E4M3, out_dtype=bf16, accumulate=False) -> dw [N, K]
+    quantize_tensor_delayed(x, amax, beta=0.99, fmt=E4M3, transpose=False) -> (q, s, qt or None):
+        per-tensor delayed scaling (running amax updated in place, one scale per tensor)
+    gemm_tensor(qa, sa, qb, sb, fa=E4M3, fb=E4M3, out_dtype=bf16) -> y [M, N] (per-tensor scales)
         (accumulate=True: out, an FP32 main-grad buffer, receives out + dW)
 """
 
@@ -49,6 +52,7 @@ OP_FPROP = 0
 OP_DGRAD = 1
 OP_WGRAD = 2
 OP_DGRAD_WT = 3
+OP_TENSOR = 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfp8bq.so")
 
@@ -74,12 +78,18 @@ _SIGS = {
                             _c_i64, _c_int, _c_vp, _c_int, _c_i64, _c_vp, _c_sz, _c_vp],
     "fp8bq_gemm_wgrad": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
                          _c_int, _c_vp, _c_int, _c_i64, _c_vp, _c_sz, _c_vp],
+    "fp8bq_gemm_tensor": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_int, _c_vp, _c_i64, _c_vp, _c_int, _c_vp,
+                          _c_int, _c_i64, _c_vp, _c_sz, _c_vp],
+    "fp8bq_quantize_tensor_workspace_size": [_c_i64, _c_i64],
+    "fp8bq_quantize_tensor_delayed": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, ctypes.c_double, _c_vp,
+                                      _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_sz, _c_vp],
     "fp8bq_gemm_workspace_size": [_c_int, _c_i64, _c_i64, _c_i64],
     "fp8bq_gemm_plan": [_c_int, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
     "fp8bq_status_string": [_c_int],
     "fp8bq_version": [],
 }
-_RESTYPES = {"fp8bq_gemm_workspace_size": _c_sz, "fp8bq_status_string": ctypes.c_char_p}
+_RESTYPES = {"fp8bq_gemm_workspace_size": _c_sz, "fp8bq_quantize_tensor_workspace_size": _c_sz,
+             "fp8bq_status_string": ctypes.c_char_p}
 
 _lib = None
 
@@ -235,6 +245,26 @@ def fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None, accumulate=Fals
            "fp8bq_gemm_wgrad")
 
 
+def fp8bq_quantize_tensor_workspace_size(R, C):
+    return int(lib().fp8bq_quantize_tensor_workspace_size(int(R), int(C)))
+
+
+def fp8bq_quantize_tensor_delayed(x, fmt, amax, beta, q, qt, s, ws):
+    R, C = x.shape
+    wsp, wsb = _ws_args(ws)
+    _check(lib().fp8bq_quantize_tensor_delayed(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(amax), float(beta), _ptr(q),
+                                               _ld(q), _ptr(qt), _ld(qt) if qt is not None else 0, _ptr(s), wsp, wsb,
+                                               _stream(x)), "fp8bq_quantize_tensor_delayed")
+
+
+def fp8bq_gemm_tensor(qa, sa, fa, qb, sb, fb, out, ws=None):
+    M, K = qa.shape
+    N = qb.shape[0]
+    wsp, wsb = _ws_args(ws)
+    _check(lib().fp8bq_gemm_tensor(M, N, K, _ptr(qa), _ld(qa), _ptr(sa), fa, _ptr(qb), _ld(qb), _ptr(sb), fb,
+                                   _ptr(out), _out_type(out), _ld(out), wsp, wsb, _stream(out)), "fp8bq_gemm_tensor")
+
+
 # ---------------------------------------------------------------------------------------------
 # allocating helpers
 # ---------------------------------------------------------------------------------------------
@@ -336,3 +366,27 @@ def gemm_wgrad(qdyt, sdyt, qxt, sxt, fdy=E4M3, fx=E4M3, out_dtype=torch.bfloat16
         ws = _workspace(OP_WGRAD, M, N, K, qdyt.device)
     fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws, accumulate=accumulate)
     return dw
+
+
+def quantize_tensor_delayed(x, amax, beta=0.99, fmt=E4M3, transpose=False):
+    """Per-tensor delayed scaling: updates the one-element FP32 running amax `amax` in place with
+    max|x| and returns (q [R, C] codes of x's BF16 copy, s (one-element FP32 scale), qt [C, R] or None)."""
+    R, C = x.shape
+    q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    qt = torch.empty((C, R), dtype=torch.uint8, device=x.device) if transpose else None
+    s = torch.empty(1, dtype=torch.float32, device=x.device)
+    n = fp8bq_quantize_tensor_workspace_size(R, C)
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device=x.device)
+    fp8bq_quantize_tensor_delayed(x, fmt, amax, beta, q, qt, s, ws)
+    return q, s, qt
+
+
+def gemm_tensor(qa, sa, qb, sb, fa=E4M3, fb=E4M3, out_dtype=torch.bfloat16, out=None, ws=None):
+    """out [M, N] = sa * sb * dec(qa) . dec(qb)^T for per-tensor scales sa, sb (one-element tensors)."""
+    M, K = qa.shape
+    N = qb.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    if ws is None:
+        ws = _workspace(OP_TENSOR, M, N, K, qa.device)
+    fp8bq_gemm_tensor(qa, sa, fa, qb, sb, fb, y, ws)
+    return y

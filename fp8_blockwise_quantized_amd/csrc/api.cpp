@@ -57,7 +57,7 @@ static int run_gemm(const GemmArgs& g, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int oes = g.out_t == 0 ? 2 : 4;
   int64_t out_rows, out_cols;
-  if (g.op == kOpFprop) {
+  if (g.op == kOpFprop || g.op == kOpTensor) {
     out_rows = g.M; out_cols = g.N;
   } else if (g.op == kOpDgrad || g.op == kOpDgradWt) {
     out_rows = g.M; out_cols = g.K;
@@ -79,8 +79,19 @@ static int run_gemm(const GemmArgs& g, void* stream) {
   d.lda = g.ldqa;
   d.sa = (const float*)g.sa;
   d.ldsa = g.ldsa;
+  d.sa_mstride = 1;
   d.sb = (const float*)g.sb;
-  if (g.op == kOpFprop) {
+  if (g.op == kOpTensor) {
+    // one scale per operand: every scale read of the fprop kernel lands on sa[0] / sb[0]
+    d.K = g.K;
+    d.b = (const uint8_t*)g.qb;
+    d.ldb = g.ldqb;
+    d.ldsa = 0;
+    d.sa_mstride = 0;
+    d.sb_mode = kSbBlock128;
+    d.sb_kstride = 0;
+    d.sb_nstride = 0;
+  } else if (g.op == kOpFprop) {
     d.K = g.K;
     d.b = (const uint8_t*)g.qb;
     d.ldb = g.ldqb;
@@ -116,7 +127,8 @@ static int run_gemm(const GemmArgs& g, void* stream) {
     d.sb_nstride = 0;
   }
   void* ws_gemm = plan.ws_gemm ? (uint8_t*)g.ws + plan.ws_transpose : nullptr;
-  return launched(launch_gemm(g.op == kOpDgradWt ? kOpDgrad : g.op, d, plan, ws_gemm, s));
+  const int kop = g.op == kOpDgradWt ? kOpDgrad : (g.op == kOpTensor ? kOpFprop : g.op);
+  return launched(launch_gemm(kop, d, plan, ws_gemm, s));
 }
 
 }  // namespace fp8bq
@@ -209,15 +221,40 @@ int fp8bq_gemm_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* qdyt, int64
   return run_gemm(g, stream);
 }
 
+int fp8bq_gemm_tensor(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_t ldqa, const float* sa,
+                      fp8bq_fp8 fa, const uint8_t* qb, int64_t ldqb, const float* sb, fp8bq_fp8 fb, void* out,
+                      fp8bq_out out_t, int64_t ldout, void* ws, size_t ws_bytes, void* stream) {
+  GemmArgs g{kOpTensor, M, N, K, qa, ldqa, sa, 1, (int)fa, qb, ldqb, sb, 1, (int)fb, out, (int)out_t, ldout, ws,
+             ws_bytes};
+  return run_gemm(g, stream);
+}
+
+size_t fp8bq_quantize_tensor_workspace_size(int64_t R, int64_t C) {
+  if (R <= 0 || C <= 0) return 0;
+  return (size_t)kTensorAmaxBlocks * sizeof(float);
+}
+
+int fp8bq_quantize_tensor_delayed(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx, fp8bq_fp8 fmt,
+                                  float* amax, double beta, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
+                                  float* s, void* ws, size_t ws_bytes, void* stream) {
+  bool empty = false;
+  int st = validate_quant_tensor(x, (int)xt, R, C, ldx, (int)fmt, amax, beta, q, ldq, qt, ldqt, s, ws, ws_bytes,
+                                 fp8bq_quantize_tensor_workspace_size(R, C), &empty);
+  if (st != kOk || empty) return st;
+  if ((st = current_device(nullptr)) != kOk) return st;
+  return launched(launch_quant_tensor_delayed(x, (int)xt, R, C, ldx, (int)fmt, amax, beta, q, ldq, qt, ldqt, s, ws,
+                                              (hipStream_t)stream));
+}
+
 size_t fp8bq_gemm_workspace_size(fp8bq_op op, int64_t M, int64_t N, int64_t K) {
-  if ((int)op < 0 || (int)op > 3 || M < 0 || N < 0 || K < 0) return 0;
+  if ((int)op < 0 || (int)op > 4 || M < 0 || N < 0 || K < 0) return 0;
   return plan_gemm((int)op, M, N, K, cu_count_or_default()).ws_total();
 }
 
 int fp8bq_gemm_plan(fp8bq_op op, int64_t M, int64_t N, int64_t K, int32_t* tile_m, int32_t* tile_n,
                     int32_t* split_k) {
   if (!tile_m || !tile_n || !split_k) return kErrNull;
-  if ((int)op < 0 || (int)op > 3 || M < 0 || N < 0 || K < 0) return kErrShape;
+  if ((int)op < 0 || (int)op > 4 || M < 0 || N < 0 || K < 0) return kErrShape;
   const GemmPlan p = plan_gemm((int)op, M, N, K, cu_count_or_default());
   *tile_m = p.tile_m;
   *tile_n = p.tile_n;
@@ -238,6 +275,7 @@ const char* fp8bq_status_string(int status) {
     case kErrDevice: return "FP8BQ_ERR_DEVICE: no current HIP device or it is not gfx950";
     case kErrLaunch: return "FP8BQ_ERR_LAUNCH: kernel launch failed";
     case kErrOverlap: return "FP8BQ_ERR_OVERLAP: an output overlaps an input";
+    case kErrValue: return "FP8BQ_ERR_VALUE: a scalar argument is out of range";
     default: return "FP8BQ_ERR_UNKNOWN";
   }
 }

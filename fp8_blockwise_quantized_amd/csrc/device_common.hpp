@@ -103,4 +103,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// fp32 value of the nearest BF16 number (ties to even).
+__device__ __forceinline__ float round_bf16(float v) { return bf16lo(pack_bf16x2(v, 0.0f)); }
+
 }  // namespace fp8bq

@@ -245,9 +245,9 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
         int64_t m = u.m0 + 64 * j + lane;
         m = m < M ? m : M - 1;
         gs[q] = d.sa;
-        gvo[q] = (uint32_t)(m * 4);
+        gvo[q] = (uint32_t)(m * 4 * d.sa_mstride);
         gsk[q] = d.ldsa;
-        gsbytes[q] = sat32(M * 4);
+        gsbytes[q] = d.sa_mstride ? sat32(M * 4) : 4;
         lso[q] = SA_OFF + 256 * j;
       } else if (j < SJOBS) {
         const int v = j - SAJOBS;

@@ -24,9 +24,18 @@ hipError_t launch_quant_128x128_dual(const void* w, int wt, int64_t N, int64_t K
 hipError_t launch_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
                                 int64_t ldq, float* s, int64_t lds, hipStream_t st);
 
+// Per-tensor delayed scaling: the running amax *amax is updated with max|x| (beta = EMA decay) and
+// gives the scale *s; q[R, C] gets the codes of x's BF16 copy, and qt[C, R] the same codes
+// transposed when qt is non-null (then R % 128 == 0).  ws holds kTensorAmaxBlocks floats.
+constexpr int kTensorAmaxBlocks = 1024;
+int tensor_amax_blocks(int64_t R);
+hipError_t launch_quant_tensor_delayed(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, float* amax,
+                                       double beta, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s,
+                                       void* ws, hipStream_t st);
+
 // One scaled FP8 GEMM in "TN" form: C[m, n] = sum_kb sa(kb, m) * sb(kb, n) * sum_{k in kb} A[m, k] B[n, k],
 // where A [Mr, K] and B [Nc, K] are both contiguous along the contraction.
-//   sa(kb, m) = sa[kb * ldsa + m]
+//   sa(kb, m) = sa[kb * ldsa + m * sa_mstride]
 //   sb(kb, n) = sb[kb * sb_kstride + (n / 128) * sb_nstride]   (SbMode::kBlock128)
 //   sb(kb, n) = sb[kb * sb_kstride + n]                         (SbMode::kColumn)
 struct GemmDesc {
@@ -36,6 +45,7 @@ struct GemmDesc {
   int64_t ldb;
   const float* sa;
   int64_t ldsa;
+  int64_t sa_mstride;  // 1: one A scale per row; 0: one scale for all rows (per-tensor scaling)
   const float* sb;
   int64_t sb_kstride;
   int64_t sb_nstride;

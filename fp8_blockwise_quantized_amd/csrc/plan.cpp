@@ -52,7 +52,7 @@ GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count) {
   GemmPlan p;
   // Output shape and contraction length in the kernel's TN frame.
   int64_t rows, cols, contraction;
-  if (op == kOpFprop) {
+  if (op == kOpFprop || op == kOpTensor) {
     rows = M; cols = N; contraction = K;
   } else if (op == kOpDgrad || op == kOpDgradWt) {
     rows = M; cols = K; contraction = N;

@@ -12,7 +12,9 @@ namespace fp8bq {
 
 enum SbMode : int { kSbBlock128 = 0, kSbColumn = 1 };
 // kOpDgradWt: dgrad on weight codes already transposed (W^T [K, N]): the dgrad kernel, no transpose.
-enum Op : int { kOpFprop = 0, kOpDgrad = 1, kOpWgrad = 2, kOpDgradWt = 3 };
+// kOpTensor: Y[M, N] = sa sb A[M, K] B[N, K]^T with one scale per operand (per-tensor scaling): the
+// fprop kernel with broadcast scales, planned as fprop.
+enum Op : int { kOpFprop = 0, kOpDgrad = 1, kOpWgrad = 2, kOpDgradWt = 3, kOpTensor = 4 };
 
 // Workgroup tile shapes (output rows x columns of one work unit).  All use 64x64 wave tiles:
 //   k128x128: 4 waves, two workgroups per CU;  k128x256 / k256x128 / k256x256: 8 waves, one

@@ -315,8 +315,10 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const TIn* __restric
 // kernel's thread mapping (8 consecutive rows x 8 columns per thread).  The tile's amax goes
 // through readlane and LDS; codes are written row-major (8-byte runs) and, staged transposed in
 // LDS, as W^T codes (16-byte runs), the operand layout of dgrad's contraction over N.
+// TENSOR: the per-tensor scale is given (s[0], read only) and the codes are those of the input's
+// BF16 copy (the delayed-scaling rule below); no amax is taken and no scale is written.
 // ---------------------------------------------------------------------------------------------
-template <typename TIn, int FMT>
+template <typename TIn, int FMT, bool TENSOR = false>
 __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __restrict__ w, int64_t ldw,
                                                                  uint8_t* __restrict__ q, int64_t ldq,
                                                                  float* __restrict__ s, int64_t lds,
@@ -332,16 +334,27 @@ __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __re
   float v[8][8];
 #pragma unroll
   for (int p = 0; p < 8; ++p) Load8<TIn>::run(w + (nb * kGroup + 8 * rg + p) * ldw + col, v[p]);
-  float m = 0.0f;
+  float sc;
+  if constexpr (TENSOR) {
+    sc = s[0];
+    if constexpr (sizeof(TIn) == 4) {
 #pragma unroll
-  for (int p = 0; p < 8; ++p)
+      for (int p = 0; p < 8; ++p)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
-  m = wave_max(m);
-  if ((t & 63) == 0) wmax[t >> 6] = m;
-  __syncthreads();
-  const float amax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
-  const float sc = group_scale<FMT>(amax);
+        for (int i = 0; i < 8; ++i) v[p][i] = round_bf16(v[p][i]);
+    }
+  } else {
+    float m = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
+    m = wave_max(m);
+    if ((t & 63) == 0) wmax[t >> 6] = m;
+    __syncthreads();
+    const float amax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+    sc = group_scale<FMT>(amax);
+  }
   const float rc = 1.0f / sc;
   uint8_t cb[8][8];  // codes [row p][column i]
 #pragma unroll
@@ -364,7 +377,7 @@ __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __re
     }
     *reinterpret_cast<uint2*>(tileT + (8 * cc + i) * kQtStride + 2 * rg) = make_uint2(lo, hi);
   }
-  if (t == 0) s[nb * lds + kb] = sc;
+  if (!TENSOR && t == 0) s[nb * lds + kb] = sc;
   __syncthreads();
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
@@ -373,6 +386,87 @@ __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __re
     const uint32_t* src4 = tileT + c * kQtStride + 4 * ch;
     store_codes16(qt + (kb * kGroup + c) * ldqt + nb * kGroup + 16 * ch, make_uint4(src4[0], src4[1], src4[2], src4[3]));
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-tensor delayed scaling ("用 RTX 5090 花 $7000 训练 2B 大模型：Puro-2B 低成本预训练技术解析",
+// section "核心挑战：Scale Factor 管理", FP8Linear: _update_amax, _quantize, forward).  One scale per
+// tensor from a running amax: the tensor's current max|x| (of the values as given) updates the
+// running value, a = fp32(fp32(a * beta) + fp32(cur * (1 - beta))), and the tensor's BF16 copy is
+// quantized with s = max(fp32(a / fmt_max), 1e-12).  The global max needs the whole tensor before
+// any code can be written, so it takes three passes:
+//   tensor_amax_kernel    per-block partial maxima (grid-stride over rows, 16-byte loads);
+//   tensor_scale_kernel   one block: max of the partials, the running-amax update, the scale;
+//   tensor_quant_kernel   codes with the given scale (any row count), or the TENSOR mode of the
+//                         128x128 dual kernel above when transposed codes are wanted as well.
+// ---------------------------------------------------------------------------------------------
+constexpr int kTensorRowsPerIter = 4;
+
+// Visit (row, 8-column chunk) work items, rows strided by the grid and 4 rows per iteration so each
+// thread keeps several 16-byte loads in flight.
+template <typename TIn, typename F>
+__device__ __forceinline__ void for_tensor_chunks(const TIn* x, int64_t R, int64_t C, int64_t ldx, F&& f) {
+  const int64_t chunks = C / 8;
+  for (int64_t r0 = (int64_t)blockIdx.x * kTensorRowsPerIter; r0 < R; r0 += (int64_t)gridDim.x * kTensorRowsPerIter) {
+    for (int64_t c8 = threadIdx.x; c8 < chunks; c8 += blockDim.x) {
+      float v[kTensorRowsPerIter][8];
+#pragma unroll
+      for (int i = 0; i < kTensorRowsPerIter; ++i)
+        if (r0 + i < R) Load8<TIn>::run(x + (r0 + i) * ldx + 8 * c8, v[i]);
+#pragma unroll
+      for (int i = 0; i < kTensorRowsPerIter; ++i)
+        if (r0 + i < R) f(r0 + i, 8 * c8, v[i]);
+    }
+  }
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void tensor_amax_kernel(const TIn* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
+                                                          float* __restrict__ partial) {
+  __shared__ float wmax[4];
+  float m = 0.0f;
+  for_tensor_chunks(x, R, C, ldx, [&](int64_t, int64_t, const float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+  });
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    partial[blockIdx.x] = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+}
+
+// One block of 256 threads.  b1 = fp32(beta), b2 = fp32(1 - beta) (formed in double on the host).
+template <int FMT>
+__global__ __launch_bounds__(256) void tensor_scale_kernel(const float* __restrict__ partial, int n,
+                                                           float* __restrict__ amax, float b1, float b2,
+                                                           float* __restrict__ s) {
+  __shared__ float wmax[4];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) m = __builtin_fmaxf(m, partial[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float cur = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+    const float a = __fadd_rn(__fmul_rn(amax[0], b1), __fmul_rn(cur, b2));  // two products, one sum
+    amax[0] = a;
+    s[0] = group_scale<FMT>(a);
+  }
+}
+
+template <typename TIn, int FMT>
+__global__ __launch_bounds__(256) void tensor_quant_kernel(const TIn* __restrict__ x, int64_t R, int64_t C,
+                                                           int64_t ldx, const float* __restrict__ s,
+                                                           uint8_t* __restrict__ q, int64_t ldq) {
+  const float sc = s[0];
+  const float rc = 1.0f / sc;
+  for_tensor_chunks(x, R, C, ldx, [&](int64_t r, int64_t c, const float (&v)[8]) {
+    float b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = sizeof(TIn) == 4 ? round_bf16(v[i]) : v[i];
+    store_codes8(q + r * ldq + c, quant8<FMT>(b, sc, rc));
+  });
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -473,6 +567,42 @@ hipError_t launch_quant_128x128_dual(const void* w, int wt, int64_t N, int64_t K
                         : launch_128x128_dual_t<uint16_t, kE5M2>(w, N, K, ldw, q, ldq, s, lds, qt, ldqt, st);
   return fmt == kE4M3 ? launch_128x128_dual_t<float, kE4M3>(w, N, K, ldw, q, ldq, s, lds, qt, ldqt, st)
                       : launch_128x128_dual_t<float, kE5M2>(w, N, K, ldw, q, ldq, s, lds, qt, ldqt, st);
+}
+
+int tensor_amax_blocks(int64_t R) {
+  const int64_t want = (R + kTensorRowsPerIter - 1) / kTensorRowsPerIter;
+  return (int)(want < kTensorAmaxBlocks ? (want > 0 ? want : 1) : kTensorAmaxBlocks);
+}
+
+template <typename TIn, int FMT>
+static hipError_t launch_tensor_t(const void* x, int64_t R, int64_t C, int64_t ldx, float* amax, float b1, float b2,
+                                  uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s, float* partial,
+                                  hipStream_t st) {
+  const int nb = tensor_amax_blocks(R);
+  hipLaunchKernelGGL((tensor_amax_kernel<TIn>), dim3(nb), dim3(256), 0, st, (const TIn*)x, R, C, ldx, partial);
+  hipLaunchKernelGGL((tensor_scale_kernel<FMT>), dim3(1), dim3(256), 0, st, (const float*)partial, nb, amax, b1, b2,
+                     s);
+  if (qt) {
+    dim3 grid((unsigned)(C / kGroup), (unsigned)(R / kGroup));
+    hipLaunchKernelGGL((quant_128x128_dual_kernel<TIn, FMT, true>), grid, dim3(256), 0, st, (const TIn*)x, ldx, q,
+                       ldq, s, (int64_t)0, qt, ldqt);
+  } else {
+    hipLaunchKernelGGL((tensor_quant_kernel<TIn, FMT>), dim3(nb), dim3(256), 0, st, (const TIn*)x, R, C, ldx,
+                       (const float*)s, q, ldq);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tensor_delayed(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, float* amax,
+                                       double beta, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s,
+                                       void* ws, hipStream_t st) {
+  const float b1 = (float)beta, b2 = (float)(1.0 - beta);
+  float* partial = reinterpret_cast<float*>(ws);
+  if (xt == 0)
+    return fmt == kE4M3 ? launch_tensor_t<uint16_t, kE4M3>(x, R, C, ldx, amax, b1, b2, q, ldq, qt, ldqt, s, partial, st)
+                        : launch_tensor_t<uint16_t, kE5M2>(x, R, C, ldx, amax, b1, b2, q, ldq, qt, ldqt, s, partial, st);
+  return fmt == kE4M3 ? launch_tensor_t<float, kE4M3>(x, R, C, ldx, amax, b1, b2, q, ldq, qt, ldqt, s, partial, st)
+                      : launch_tensor_t<float, kE5M2>(x, R, C, ldx, amax, b1, b2, q, ldq, qt, ldqt, s, partial, st);
 }
 
 }  // namespace fp8bq

@@ -120,10 +120,46 @@ int validate_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t 
                      false);
 }
 
+static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int validate_quant_tensor(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, const void* amax,
+                          double beta, const void* q, int64_t ldq, const void* qt, int64_t ldqt, const void* s,
+                          const void* ws, size_t ws_bytes, size_t ws_needed, bool* empty) {
+  *empty = false;
+  if (in_esize(xt) == 0) return kErrDtype;
+  if (!fmt_ok(fmt)) return kErrFormat;
+  if (!(beta >= 0.0 && beta <= 1.0)) return kErrValue;  // also rejects NaN
+  if (R < 0 || C < 0 || C % 128 != 0 || (qt != nullptr && R % 128 != 0)) return kErrShape;
+  if (R == 0 || C == 0) {
+    *empty = true;
+    return kOk;
+  }
+  if (x == nullptr || q == nullptr || amax == nullptr || s == nullptr || ws == nullptr) return kErrNull;
+  int st;
+  const Mat mx{x, R, C, ldx, in_esize(xt)}, mq{q, R, C, ldq, 1}, mqt{qt, C, R, ldqt, 1};
+  const Mat ma{amax, 1, 1, 1, 4}, ms{s, 1, 1, 1, 4};
+  if ((st = check_mat(mx, true)) != kOk) return st;
+  if ((st = check_mat(mq, true)) != kOk) return st;
+  if (qt != nullptr && (st = check_mat(mqt, true)) != kOk) return st;
+  if (!aligned4(amax) || !aligned4(s) || !aligned16(ws)) return kErrAlign;
+  if (ws_bytes < ws_needed) return kErrWorkspace;
+  const Mat mw{ws, 1, (int64_t)ws_needed, (int64_t)ws_needed, 1};
+  const Mat outs[4] = {mq, mqt, ma, ms};
+  const int nout = 4;
+  for (int i = 0; i < nout; ++i) {
+    if (outs[i].p == nullptr) continue;
+    if (overlaps(outs[i], mx) || overlaps(outs[i], mw)) return kErrOverlap;
+    for (int j = i + 1; j < nout; ++j)
+      if (outs[j].p != nullptr && overlaps(outs[i], outs[j])) return kErrOverlap;
+  }
+  if (overlaps(mw, mx)) return kErrOverlap;
+  return kOk;
+}
+
 int validate_gemm(const GemmArgs& g, size_t ws_needed, bool* empty, bool* zero_fill) {
   *empty = false;
   *zero_fill = false;
-  if (g.op < 0 || g.op > 3) return kErrShape;
+  if (g.op < 0 || g.op > 4) return kErrShape;
   if (!fmt_ok(g.fa) || !fmt_ok(g.fb)) return kErrFormat;
   if (g.out_t != 0 && g.out_t != 1 && !(g.out_t == 2 && g.op == 2)) return kErrDtype;
   const int64_t M = g.M, N = g.N, K = g.K;
@@ -134,7 +170,13 @@ int validate_gemm(const GemmArgs& g, size_t ws_needed, bool* empty, bool* zero_f
   Mat qa, sa, qb, sb, out;
   int64_t out_rows, out_cols, contraction;
   const int oes = g.out_t == 0 ? 2 : 4;
-  if (g.op == 0) {  // fprop: X[M,K] (1x128), W[N,K] (128x128) -> Y[M,N]
+  if (g.op == 4) {  // per-tensor scales: A[M,K], B[N,K] (one scale each) -> Y[M,N]
+    qa = Mat{g.qa, M, K, g.ldqa, 1};
+    sa = Mat{g.sa, 1, 1, 1, 4};
+    qb = Mat{g.qb, N, K, g.ldqb, 1};
+    sb = Mat{g.sb, 1, 1, 1, 4};
+    out_rows = M; out_cols = N; contraction = K;
+  } else if (g.op == 0) {  // fprop: X[M,K] (1x128), W[N,K] (128x128) -> Y[M,N]
     qa = Mat{g.qa, M, K, g.ldqa, 1};
     sa = Mat{g.sa, K / 128, M, g.ldsa, 4};
     qb = Mat{g.qb, N, K, g.ldqb, 1};
@@ -173,10 +215,14 @@ int validate_gemm(const GemmArgs& g, size_t ws_needed, bool* empty, bool* zero_f
   }
   if (g.qa == nullptr || g.sa == nullptr || g.qb == nullptr || g.sb == nullptr) return kErrNull;
   if ((st = check_mat(qa, true)) != kOk) return st;
-  if ((st = check_mat(sa, true)) != kOk) return st;
   if ((st = check_mat(qb, true)) != kOk) return st;
-  // weight scales are read one value at a time; the wgrad column scales as 16-byte vectors
-  if ((st = check_mat(sb, g.op == 2)) != kOk) return st;
+  if (g.op == 4) {  // the two scales are single floats
+    if (!aligned4(g.sa) || !aligned4(g.sb)) return kErrAlign;
+  } else {
+    if ((st = check_mat(sa, true)) != kOk) return st;
+    // weight scales are read one value at a time; the wgrad column scales as 16-byte vectors
+    if ((st = check_mat(sb, g.op == 2)) != kOk) return st;
+  }
   if (overlaps(out, qa) || overlaps(out, sa) || overlaps(out, qb) || overlaps(out, sb)) return kErrOverlap;
   if (ws_needed > 0) {
     if (g.ws == nullptr || g.ws_bytes < ws_needed) return kErrWorkspace;

@@ -20,6 +20,7 @@ enum Status : int {
   kErrDevice = 8,
   kErrLaunch = 9,
   kErrOverlap = 10,
+  kErrValue = 11,
 };
 
 // A row-major matrix view for validation: base pointer, rows, columns, leading dimension (elements),
@@ -46,6 +47,12 @@ int validate_quant_128x128_dual(const void* w, int wt, int64_t N, int64_t K, int
                                 int64_t ldq, const void* s, int64_t lds, const void* qt, int64_t ldqt, bool* empty);
 int validate_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, const void* q,
                            int64_t ldq, const void* s, int64_t lds, bool* empty);
+
+// Per-tensor delayed scaling: x [R, C] (C % 128 == 0), running amax and scale one float each (4-byte
+// aligned), q [R, C], optional qt [C, R] (then R % 128 == 0), beta in [0, 1], ws >= ws_needed bytes.
+int validate_quant_tensor(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, const void* amax,
+                          double beta, const void* q, int64_t ldq, const void* qt, int64_t ldqt, const void* s,
+                          const void* ws, size_t ws_bytes, size_t ws_needed, bool* empty);
 
 // The three GEMMs share one validator: op selects the operand shapes.
 struct GemmArgs {

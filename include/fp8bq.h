@@ -60,7 +60,8 @@ typedef enum {
   FP8BQ_ERR_WORKSPACE = 7, /* workspace NULL or smaller than fp8bq_gemm_workspace_size() */
   FP8BQ_ERR_DEVICE = 8,    /* no current HIP device, or it is not gfx950 */
   FP8BQ_ERR_LAUNCH = 9,    /* the kernel launch itself failed */
-  FP8BQ_ERR_OVERLAP = 10   /* an output overlaps an input the same call reads */
+  FP8BQ_ERR_OVERLAP = 10,  /* an output overlaps an input the same call reads */
+  FP8BQ_ERR_VALUE = 11     /* a scalar argument is out of range (beta outside [0, 1]) */
 } fp8bq_status;
 
 /* OCP FP8 formats: E4M3 = float8_e4m3fn (bias 7, no Inf, max 448);
@@ -79,8 +80,14 @@ typedef enum { FP8BQ_IN_BF16 = 0, FP8BQ_IN_F32 = 1 } fp8bq_in;
 typedef enum { FP8BQ_OUT_BF16 = 0, FP8BQ_OUT_F32 = 1, FP8BQ_OUT_F32_ACCUM = 2 } fp8bq_out;
 
 /* GEMM selector for fp8bq_gemm_workspace_size and fp8bq_gemm_plan (FP8BQ_OP_DGRAD_WT:
- * fp8bq_gemm_dgrad_wt). */
-typedef enum { FP8BQ_OP_FPROP = 0, FP8BQ_OP_DGRAD = 1, FP8BQ_OP_WGRAD = 2, FP8BQ_OP_DGRAD_WT = 3 } fp8bq_op;
+ * fp8bq_gemm_dgrad_wt; FP8BQ_OP_TENSOR: fp8bq_gemm_tensor). */
+typedef enum {
+  FP8BQ_OP_FPROP = 0,
+  FP8BQ_OP_DGRAD = 1,
+  FP8BQ_OP_WGRAD = 2,
+  FP8BQ_OP_DGRAD_WT = 3,
+  FP8BQ_OP_TENSOR = 4
+} fp8bq_op;
 
 /*
  * Activation quantization, one scale per 1x128 group (128 consecutive elements of a row).
@@ -228,6 +235,52 @@ int fp8bq_gemm_wgrad(int64_t M, int64_t N, int64_t K,
                      const uint8_t* qdyt, int64_t ldqdyt, const float* sdyt, int64_t ldsdyt, fp8bq_fp8 fdy,
                      const uint8_t* qxt, int64_t ldqxt, const float* sxt, int64_t ldsxt, fp8bq_fp8 fx,
                      void* dw, fp8bq_out dwt, int64_t lddw, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Per-tensor delayed scaling: the pages' own alternative to the blockwise recipe.
+ * Defining passage: "用 RTX 5090 花 $7000 训练 2B 大模型：Puro-2B 低成本预训练技术解析", section
+ * "核心挑战：Scale Factor 管理", the FP8Linear listing (_update_amax, _quantize, forward): one scale
+ * per tensor from a running amax that is updated before the tensor is quantized.
+ *
+ * fp8bq_quantize_tensor_delayed, for x [R, C] (row-major, ldx >= C):
+ *   1. cur = max |x| over the whole tensor, of the values as given (BF16 or FP32);
+ *   2. *amax = fp32(fp32(*amax * fp32(beta)) + fp32(cur * fp32(1 - beta))), 1 - beta formed in
+ *      double; the listing uses beta = 0.99 and starts the running amax at 1.0;
+ *   3. *s = max(fp32(*amax / fmt_max), fp32(1e-12));
+ *   4. q[r, c] = RNE code of clamp(fp32(bf16(x[r, c]) / *s), +-fmt_max): the codes of x's BF16
+ *      copy (identical to x for BF16 input); and, if qt is not NULL, qt[c, r] = q[r, c] (the
+ *      operand layout of dgrad and wgrad).
+ *   amax, s    device pointers to one float each (4-byte aligned); *amax is read and updated in
+ *              place, *s is written.  Calls that share an amax buffer must be ordered (one stream).
+ *   q          [R, C] codes (ldq >= C); qt NULL or [C, R] codes (ldqt >= R, R % 128 == 0).
+ *   C % 128 == 0; R >= 0.  R == 0 or C == 0: nothing is enqueued and *amax, *s stay as they are.
+ *   ws         at least fp8bq_quantize_tensor_workspace_size(R, C) bytes, 16-byte aligned
+ *              (per-block partial maxima; its contents are not needed between calls).
+ * Errors: FP8BQ_ERR_VALUE for beta outside [0, 1] (or NaN); FP8BQ_ERR_ALIGN for amax or s not
+ * 4-byte aligned; otherwise as the blockwise quantizers.  Three kernels run on `stream` in order
+ * (partial maxima, the running-amax update and scale, the codes).
+ */
+size_t fp8bq_quantize_tensor_workspace_size(int64_t R, int64_t C);
+int fp8bq_quantize_tensor_delayed(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx, fp8bq_fp8 fmt,
+                                  float* amax, double beta, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
+                                  float* s, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * GEMM of two per-tensor-scaled operands, both contiguous along the contraction ("TN"):
+ *   out[m, n] = (*sa) * (*sb) * sum_k dec(qa[m, k]) * dec(qb[n, k]),  FP32 accumulation.
+ * Defining passage: as fp8bq_quantize_tensor_delayed (the listing's forward dequantizes both
+ * operands with their scales and contracts; its production note runs that product as an FP8 GEMM).
+ * fprop: qa = X codes [M, K], qb = W codes [N, K]; dgrad: qa = dY codes [M, N], qb = W^T codes
+ * (qt of the weight) with K and N swapped; wgrad: qa = dY^T codes, qb = X^T codes (the qt outputs),
+ * contraction over the tokens.
+ *   sa, sb     device pointers to one float each (4-byte aligned).
+ *   M >= 0 (any); N % 128 == 0; K % 128 == 0; out [M, N] of type out_t (BF16 or FP32), ldout >= N.
+ *   ws         at least fp8bq_gemm_workspace_size(FP8BQ_OP_TENSOR, M, N, K) bytes.
+ * Errors as fp8bq_gemm_fprop.
+ */
+int fp8bq_gemm_tensor(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_t ldqa, const float* sa,
+                      fp8bq_fp8 fa, const uint8_t* qb, int64_t ldqb, const float* sb, fp8bq_fp8 fb, void* out,
+                      fp8bq_out out_t, int64_t ldout, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes the given GEMM needs at these sizes on the current device (0 if none).
  * Returns 0 for invalid arguments too; the GEMM call itself reports those. */

@@ -17,7 +17,7 @@ import fp8_blockwise_quantized_amd as fq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8bq.h")
 
-OK, NULL, SHAPE, LD, ALIGN, DTYPE, FORMAT, WORKSPACE, DEVICE, LAUNCH, OVERLAP = range(11)
+OK, NULL, SHAPE, LD, ALIGN, DTYPE, FORMAT, WORKSPACE, DEVICE, LAUNCH, OVERLAP, VALUE = range(12)
 HAVE_GPU = torch.cuda.is_available()
 
 P = lambda i: ctypes.c_void_p(0x100000 * (i + 1))  # disjoint, 16-byte aligned fake buffers
@@ -34,14 +34,14 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fq.lib()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings():
     assert fq.lib().fp8bq_version() >= 100
-    for st in range(11):
+    for st in range(12):
         s = fq.status_string(st)
         assert s.startswith("FP8BQ_")
     assert fq.status_string(4242) == "FP8BQ_ERR_UNKNOWN"
@@ -168,16 +168,17 @@ def test_gemm_plan_query():
     a, b, c = i32(-1), i32(-1), i32(-1)
     ref = lambda v: ctypes.cast(ctypes.byref(v), ctypes.c_void_p)
     assert lib.fp8bq_gemm_plan(0, 256, 256, 256, NUL, ref(b), ref(c)) == NULL
-    assert lib.fp8bq_gemm_plan(4, 256, 256, 256, ref(a), ref(b), ref(c)) == SHAPE
+    assert lib.fp8bq_gemm_plan(5, 256, 256, 256, ref(a), ref(b), ref(c)) == SHAPE
     assert lib.fp8bq_gemm_plan(0, -1, 256, 256, ref(a), ref(b), ref(c)) == SHAPE
     assert a.value == -1 and b.value == -1 and c.value == -1
-    for op in (fq.OP_FPROP, fq.OP_DGRAD, fq.OP_WGRAD, fq.OP_DGRAD_WT):
+    for op in (fq.OP_FPROP, fq.OP_DGRAD, fq.OP_WGRAD, fq.OP_DGRAD_WT, fq.OP_TENSOR):
         for (M, N, K) in [(256, 256, 256), (512, 2048, 2048), (16384, 2560, 2048), (16384, 11264, 2048),
                           (16384, 2048, 5632)]:
             tm, tn, sk = fq.fp8bq_gemm_plan(op, M, N, K)
             assert (tm, tn) in [(128, 128), (128, 256), (256, 128), (256, 256)]
             assert 1 <= sk <= 8
-            rows, cols = {fq.OP_FPROP: (M, N), fq.OP_DGRAD: (M, K), fq.OP_WGRAD: (N, K), fq.OP_DGRAD_WT: (M, K)}[op]
+            rows, cols = {fq.OP_FPROP: (M, N), fq.OP_DGRAD: (M, K), fq.OP_WGRAD: (N, K), fq.OP_DGRAD_WT: (M, K),
+                          fq.OP_TENSOR: (M, N)}[op]
             ws = fq.fp8bq_gemm_workspace_size(op, M, N, K)
             transpose = ((N * K + 255) // 256) * 256 if op == fq.OP_DGRAD else 0
             assert ws == transpose + (sk * rows * cols * 4 if sk > 1 else 0)
@@ -222,3 +223,45 @@ def test_gemm_dgrad_wt_validation():
     assert gemm(g, out=P(2)) == OVERLAP
     assert gemm(g, ldqb=100) == LD  # W^T rows hold N codes
     assert fq.fp8bq_gemm_workspace_size(fq.OP_DGRAD_WT, 16384, 11264, 2048) < 11264 * 2048  # no transpose buffer
+
+
+def qtensor(x=P(0), xt=0, R=256, C=256, ldx=256, fmt=0, amax=P(1), beta=0.99, q=P(2), ldq=256, qt=P(3), ldqt=256,
+            s=ctypes.c_void_p(0x100000 * 2 + 64), ws=P(4), ws_bytes=4096):
+    return fq.lib().fp8bq_quantize_tensor_delayed(x, xt, R, C, ldx, fmt, amax, beta, q, ldq, qt, ldqt, s, ws, ws_bytes,
+                                                  S0)
+
+
+def test_quant_tensor_delayed_validation():
+    assert fq.fp8bq_quantize_tensor_workspace_size(256, 256) == 4096
+    assert fq.fp8bq_quantize_tensor_workspace_size(0, 256) == 0
+    valid(lambda: qtensor(s=P(5)))
+    valid(lambda: qtensor(s=P(5), qt=NUL, R=200))  # ragged rows without the transposed codes
+    assert qtensor(R=0) == OK and qtensor(C=0) == OK  # empty: nothing enqueued
+    assert qtensor(xt=2) == DTYPE and qtensor(fmt=2) == FORMAT
+    assert qtensor(beta=1.5) == VALUE and qtensor(beta=-0.01) == VALUE and qtensor(beta=float("nan")) == VALUE
+    valid(lambda: qtensor(s=P(5), beta=0.0))
+    valid(lambda: qtensor(s=P(5), beta=1.0))
+    assert qtensor(C=200, ldx=256) == SHAPE
+    assert qtensor(R=200) == SHAPE  # the transposed codes need R % 128 == 0
+    assert qtensor(amax=NUL) == NULL and qtensor(ws=NUL) == NULL and qtensor(q=NUL) == NULL
+    assert qtensor(amax=ctypes.c_void_p(0x200002)) == ALIGN
+    assert qtensor(ws_bytes=100) == WORKSPACE
+    assert qtensor(ldq=100) == LD and qtensor(ldqt=100) == LD
+    assert qtensor(q=P(0)) == OVERLAP  # codes over the input
+    assert qtensor(s=P(1)) == OVERLAP  # scale and running amax in one float
+    assert qtensor(s=P(5), amax=P(4)) == OVERLAP  # running amax inside the workspace
+
+
+def test_gemm_tensor_validation():
+    def gt(M=256, N=256, K=256, qa=P(0), ldqa=256, sa=P(1), fa=0, qb=P(2), ldqb=256, sb=P(3), fb=0, out=P(4),
+           out_t=0, ldout=256, ws=P(5), ws_bytes=1 << 20):
+        return fq.lib().fp8bq_gemm_tensor(M, N, K, qa, ldqa, sa, fa, qb, ldqb, sb, fb, out, out_t, ldout, ws,
+                                          ws_bytes, S0)
+    valid(lambda: gt())
+    valid(lambda: gt(M=100, sa=ctypes.c_void_p(0x200004)))  # ragged rows; a scale needs 4-byte alignment only
+    assert gt(sa=ctypes.c_void_p(0x200002)) == ALIGN
+    assert gt(K=200) == SHAPE and gt(N=200) == SHAPE
+    assert gt(sb=NUL) == NULL and gt(fb=4) == FORMAT and gt(out_t=2) == DTYPE
+    assert gt(out=P(0)) == OVERLAP
+    assert gt(M=0, qa=NUL, out=NUL) == OK
+    assert fq.fp8bq_gemm_plan(fq.OP_TENSOR, 4096, 2048, 2048) == fq.fp8bq_gemm_plan(fq.OP_FPROP, 4096, 2048, 2048)
