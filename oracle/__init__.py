@@ -19,7 +19,9 @@ Sources (cited by page title and section; the pages are the authority):
         (scale = amax / fmt_max with a 1e-12 floor, divide, clamp, cast) and
         the dequantize rule (code value times scale).
   The same listing's running (EMA) amax with one scale per tensor is the
-        per-tensor delayed-scaling variant in ``delayed.py``.
+        per-tensor delayed-scaling variant in ``delayed.py``; its section
+        "Hyperball 优化：让 FP8 训练不爆炸" (``HyperballSGD``) is the
+        normalized update in ``hyperball.py``.
 * [XZY] "小团队也能预训练！普罗2B：RTX5090训练成本不到5090美元" (66bd.net,
         新智元), paragraph "FP8发挥RTX 5090的低精度效率优势": fine-grained
         block quantization after DeepSeek-V3, main linear GEMMs in FP8,
@@ -74,3 +76,4 @@ from .delayed import (  # noqa: F401
     quant_tensor_delayed,
     tensor_scale,
 )
+from .hyperball import hyperball_step  # noqa: F401
