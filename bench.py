@@ -8,11 +8,13 @@ One step = the whole path for one synthetic 2B-class decoder block at M = 16384 
     quantize dY both ways in one pass, dgrad dX = dY W, wgrad dW = dY^T X
 i.e. 12 quantize passes and 12 GEMMs, all E4M3, BF16 in and out, inputs resident in HBM.
 
-    python bench.py [--steps K] [--warmup W] [--workload decoder|delayed|linear|sweep] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload decoder|delayed|hyperball|linear|sweep] [--no-cpu-baseline]
 
 `--workload delayed` runs the same decoder-block step with per-tensor delayed scaling instead (one
 running amax and one scale per tensor, X / W / dY each quantized once with transposed codes, the
 three GEMMs with per-tensor scales): the pages' own alternative recipe, as a comparison point.
+`--workload hyperball` times the Hyperball update (with the fixed-radius projection) of the decoder
+block's four FP32 master weights from BF16 gradients, and reports GB/s.
 
 Prints ONE JSON line on stdout.  `value` = GEMM FLOPs of the step / wall time of the step (the
 quantize passes are inside the timed step).  `breakdown` holds per-product TFLOP/s and per-pass GB/s
@@ -44,7 +46,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", choices=["decoder", "delayed", "linear", "sweep"], default="decoder")
+    p.add_argument("--workload", choices=["decoder", "delayed", "hyperball", "linear", "sweep"], default="decoder")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=4096)
     p.add_argument("--calibrate", action="store_true",
@@ -84,6 +86,8 @@ def main():
         ops, bufs, desc = build_decoder(torch, fq, synth, dev)
     elif args.workload == "delayed":
         ops, bufs, desc = build_delayed(torch, fq, synth, dev)
+    elif args.workload == "hyperball":
+        return run_hyperball(args, torch, fq, synth, dev)
     elif args.workload == "linear":
         ops, bufs, desc = build_linear(torch, fq, synth, dev)
     else:
@@ -318,6 +322,54 @@ def build_delayed(torch, fq, synth, dev):
         "quant_calls_per_step": 12,
     }
     return ops, bufs, desc
+
+
+def run_hyperball(args, torch, fq, synth, dev):
+    """Hyperball update with projection of the four decoder weights (FP32 masters, BF16 gradients).
+    Algorithmic bytes per element: gradient read 2 + weight read and write 8 + the projection's second
+    weight read and write 8 (it needs the whole updated tensor's norm first) = 18."""
+    import numpy as np
+    items = []
+    for name, K, N in synth.DECODER_LINEARS:
+        w = synth.random_f32((N, K), seed=7 + N, std=0.02).to(dev)
+        g = synth.random_bf16((N, K), seed=8 + N, std=1e-3).to(dev)
+        radius = float(torch.linalg.vector_norm(w.double()).item())
+        norms = torch.empty(2, dtype=torch.float32, device=dev)
+        ws = torch.empty(fq.fp8bq_hyperball_workspace_size(N, K), dtype=torch.uint8, device=dev)
+        items.append((name, w, g, radius, norms, ws, 18 * N * K))
+
+    def step():
+        for _, w, g, radius, norms, ws, _ in items:
+            fq.fp8bq_hyperball_step(w, g, 1e-4, 0.1, 1e-8, radius, norms, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    total = sum(it[-1] for it in items)
+    gbs = total / (ms * 1e-3) / 1e9
+    stream = torch.cuda.current_stream(dev)
+    per = []
+    for name, w, g, radius, norms, ws, nbytes in items:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fq.fp8bq_hyperball_step(w, g, 1e-4, 0.1, 1e-8, radius, norms, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / args.steps
+        per.append({"weight": name, "shape": list(w.shape), "ms": round(t, 5),
+                    "gbs": round(nbytes / (t * 1e-3) / 1e9, 1)})
+    print(json.dumps({"metric": "Hyperball update with fixed-radius projection, GB/s (18 B per weight element)",
+                      "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(ms, 4),
+                      "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "steps": args.steps,
+                      "config": {"workload": "decoder-block weights (QKV, O, gate+up, down), FP32 masters, "
+                                             "BF16 gradients"},
+                      "per_weight": per}), flush=True)
 
 
 def build_linear(torch, fq, synth, dev):

@@ -33,6 +33,8 @@ Allocating helpers (outputs created with torch on the input's device):
     quantize_tensor_delayed(x, amax, beta=0.99, fmt=E4M3, transpose=False) -> (q, s, qt or None):
         per-tensor delayed scaling (running amax updated in place, one scale per tensor)
     gemm_tensor(qa, sa, qb, sb, fa=E4M3, fb=E4M3, out_dtype=bf16) -> y [M, N] (per-tensor scales)
+    hyperball_step(w, g, lr=1e-4, weight_decay=0.1, eps=1e-8, radius=0.0) -> norms:
+        in-place normalized update of an FP32 weight (and projection onto `radius` if > 0)
         (accumulate=True: out, an FP32 main-grad buffer, receives out + dW)
 """
 
@@ -83,12 +85,16 @@ _SIGS = {
     "fp8bq_quantize_tensor_workspace_size": [_c_i64, _c_i64],
     "fp8bq_quantize_tensor_delayed": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, ctypes.c_double, _c_vp,
                                       _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_sz, _c_vp],
+    "fp8bq_hyperball_workspace_size": [_c_i64, _c_i64],
+    "fp8bq_hyperball_step": [_c_vp, _c_i64, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, ctypes.c_double, ctypes.c_double,
+                             ctypes.c_double, ctypes.c_double, _c_vp, _c_vp, _c_sz, _c_vp],
     "fp8bq_gemm_workspace_size": [_c_int, _c_i64, _c_i64, _c_i64],
     "fp8bq_gemm_plan": [_c_int, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
     "fp8bq_status_string": [_c_int],
     "fp8bq_version": [],
 }
 _RESTYPES = {"fp8bq_gemm_workspace_size": _c_sz, "fp8bq_quantize_tensor_workspace_size": _c_sz,
+             "fp8bq_hyperball_workspace_size": _c_sz,
              "fp8bq_status_string": ctypes.c_char_p}
 
 _lib = None
@@ -265,6 +271,18 @@ def fp8bq_gemm_tensor(qa, sa, fa, qb, sb, fb, out, ws=None):
                                    _ptr(out), _out_type(out), _ld(out), wsp, wsb, _stream(out)), "fp8bq_gemm_tensor")
 
 
+def fp8bq_hyperball_workspace_size(R, C):
+    return int(lib().fp8bq_hyperball_workspace_size(int(R), int(C)))
+
+
+def fp8bq_hyperball_step(w, g, lr, weight_decay, eps, radius, norms, ws):
+    R, C = w.shape
+    wsp, wsb = _ws_args(ws)
+    _check(lib().fp8bq_hyperball_step(_ptr(w), _ld(w), _ptr(g), _in_type(g), _ld(g), R, C, float(lr),
+                                      float(weight_decay), float(eps), float(radius), _ptr(norms), wsp, wsb,
+                                      _stream(w)), "fp8bq_hyperball_step")
+
+
 # ---------------------------------------------------------------------------------------------
 # allocating helpers
 # ---------------------------------------------------------------------------------------------
@@ -390,3 +408,17 @@ def gemm_tensor(qa, sa, qb, sb, fa=E4M3, fb=E4M3, out_dtype=torch.bfloat16, out=
         ws = _workspace(OP_TENSOR, M, N, K, qa.device)
     fp8bq_gemm_tensor(qa, sa, fa, qb, sb, fb, y, ws)
     return y
+
+
+def hyperball_step(w, g, lr=1e-4, weight_decay=0.1, eps=1e-8, radius=0.0, ws=None):
+    """In-place Hyperball update of the FP32 weight w with gradient g (BF16 or FP32); returns a
+    two-element FP32 device tensor (||g||, ||w|| after the update and before the projection)."""
+    if w.dtype != torch.float32:
+        raise TypeError("w must be the FP32 master weight")
+    if w.shape != g.shape:
+        raise ValueError("w and g must have one shape")
+    norms = torch.empty(2, dtype=torch.float32, device=w.device)
+    if ws is None:
+        ws = torch.empty(max(fp8bq_hyperball_workspace_size(*w.shape), 16), dtype=torch.uint8, device=w.device)
+    fp8bq_hyperball_step(w, g, lr, weight_decay, eps, radius, norms, ws)
+    return norms

@@ -6,6 +6,7 @@
 
 #include "../../include/fp8bq.h"
 #include "launch.hpp"
+#include "optim.hpp"
 #include "plan.hpp"
 #include "validate.hpp"
 
@@ -231,7 +232,7 @@ int fp8bq_gemm_tensor(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_
 
 size_t fp8bq_quantize_tensor_workspace_size(int64_t R, int64_t C) {
   if (R <= 0 || C <= 0) return 0;
-  return (size_t)kTensorAmaxBlocks * sizeof(float);
+  return kTensorWorkspace;
 }
 
 int fp8bq_quantize_tensor_delayed(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx, fp8bq_fp8 fmt,
@@ -244,6 +245,23 @@ int fp8bq_quantize_tensor_delayed(const void* x, fp8bq_in xt, int64_t R, int64_t
   if ((st = current_device(nullptr)) != kOk) return st;
   return launched(launch_quant_tensor_delayed(x, (int)xt, R, C, ldx, (int)fmt, amax, beta, q, ldq, qt, ldqt, s, ws,
                                               (hipStream_t)stream));
+}
+
+size_t fp8bq_hyperball_workspace_size(int64_t R, int64_t C) {
+  if (R <= 0 || C <= 0) return 0;
+  return kHyperballWorkspace;
+}
+
+int fp8bq_hyperball_step(float* w, int64_t ldw, const void* g, fp8bq_in gt, int64_t ldg, int64_t R, int64_t C,
+                         double lr, double weight_decay, double eps, double radius, float* norms, void* ws,
+                         size_t ws_bytes, void* stream) {
+  bool empty = false;
+  int st = validate_hyperball(w, ldw, g, (int)gt, ldg, R, C, lr, weight_decay, eps, radius, norms, ws, ws_bytes,
+                              fp8bq_hyperball_workspace_size(R, C), &empty);
+  if (st != kOk || empty) return st;
+  if ((st = current_device(nullptr)) != kOk) return st;
+  return launched(launch_hyperball_step(w, ldw, g, (int)gt, ldg, R, C, lr, weight_decay, eps, radius, norms, ws,
+                                        (hipStream_t)stream));
 }
 
 size_t fp8bq_gemm_workspace_size(fp8bq_op op, int64_t M, int64_t N, int64_t K) {
@@ -275,7 +293,7 @@ const char* fp8bq_status_string(int status) {
     case kErrDevice: return "FP8BQ_ERR_DEVICE: no current HIP device or it is not gfx950";
     case kErrLaunch: return "FP8BQ_ERR_LAUNCH: kernel launch failed";
     case kErrOverlap: return "FP8BQ_ERR_OVERLAP: an output overlaps an input";
-    case kErrValue: return "FP8BQ_ERR_VALUE: a scalar argument is out of range";
+    case kErrValue: return "FP8BQ_ERR_VALUE: a scalar argument is out of range or not finite";
     default: return "FP8BQ_ERR_UNKNOWN";
   }
 }

@@ -26,8 +26,10 @@ hipError_t launch_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int
 
 // Per-tensor delayed scaling: the running amax *amax is updated with max|x| (beta = EMA decay) and
 // gives the scale *s; q[R, C] gets the codes of x's BF16 copy, and qt[C, R] the same codes
-// transposed when qt is non-null (then R % 128 == 0).  ws holds kTensorAmaxBlocks floats.
+// transposed when qt is non-null (then R % 128 == 0).  ws holds kTensorAmaxBlocks partial maxima
+// and the running amax as it was (kTensorWorkspace bytes).
 constexpr int kTensorAmaxBlocks = 1024;
+constexpr size_t kTensorWorkspace = (kTensorAmaxBlocks + 64) * sizeof(float);
 int tensor_amax_blocks(int64_t R);
 hipError_t launch_quant_tensor_delayed(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, float* amax,
                                        double beta, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s,

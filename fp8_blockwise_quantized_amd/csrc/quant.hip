@@ -310,19 +310,50 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const TIn* __restric
   if (t == 0) s[nb * lds + kb] = sc;
 }
 
+// Per-tensor scale of the delayed-scaling rule (below), computed by every block of the code pass
+// from the amax pass's partial maxima and the running amax it saved: cur = max of the partials;
+// a = fp32(fp32(a_old * b1) + fp32(cur * b2)); s = max(fp32(a / fmt_max), 1e-12).  The first block
+// stores the new running amax and the scale.  b1 = fp32(beta), b2 = fp32(1 - beta).
+struct TensorScaleArgs {
+  const float* partial;  // n partial maxima, then the running amax as it was before this call
+  int n;
+  float b1, b2;
+  float* amax;
+  float* s;
+};
+
+template <int FMT>
+__device__ __forceinline__ float tensor_scale(const TensorScaleArgs& a) {
+  __shared__ float tmax[4];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < a.n; i += blockDim.x) m = __builtin_fmaxf(m, a.partial[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) tmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float cur = __builtin_fmaxf(__builtin_fmaxf(tmax[0], tmax[1]), __builtin_fmaxf(tmax[2], tmax[3]));
+  const float am = __fadd_rn(__fmul_rn(a.partial[kTensorAmaxBlocks], a.b1), __fmul_rn(cur, a.b2));
+  const float sc = group_scale<FMT>(am);
+  if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) {
+    a.amax[0] = am;
+    a.s[0] = sc;
+  }
+  return sc;
+}
+
 // ---------------------------------------------------------------------------------------------
 // 128x128 with a transposed copy: grid (K/128, N/128), one block per weight tile, the 128x1
 // kernel's thread mapping (8 consecutive rows x 8 columns per thread).  The tile's amax goes
 // through readlane and LDS; codes are written row-major (8-byte runs) and, staged transposed in
 // LDS, as W^T codes (16-byte runs), the operand layout of dgrad's contraction over N.
-// TENSOR: the per-tensor scale is given (s[0], read only) and the codes are those of the input's
-// BF16 copy (the delayed-scaling rule below); no amax is taken and no scale is written.
+// TENSOR: the per-tensor scale comes from tensor_scale (the delayed-scaling rule below; s and lds
+// are unused) and the codes are those of the input's BF16 copy.
 // ---------------------------------------------------------------------------------------------
 template <typename TIn, int FMT, bool TENSOR = false>
 __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __restrict__ w, int64_t ldw,
                                                                  uint8_t* __restrict__ q, int64_t ldq,
                                                                  float* __restrict__ s, int64_t lds,
-                                                                 uint8_t* __restrict__ qt, int64_t ldqt) {
+                                                                 uint8_t* __restrict__ qt, int64_t ldqt,
+                                                                 TensorScaleArgs ta) {
   __shared__ float wmax[4];
   __shared__ __attribute__((aligned(8))) uint32_t tileT[kQtCols * kQtStride];
   const int t = threadIdx.x;
@@ -336,7 +367,7 @@ __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __re
   for (int p = 0; p < 8; ++p) Load8<TIn>::run(w + (nb * kGroup + 8 * rg + p) * ldw + col, v[p]);
   float sc;
   if constexpr (TENSOR) {
-    sc = s[0];
+    sc = tensor_scale<FMT>(ta);
     if constexpr (sizeof(TIn) == 4) {
 #pragma unroll
       for (int p = 0; p < 8; ++p)
@@ -394,11 +425,12 @@ __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __re
 // tensor from a running amax: the tensor's current max|x| (of the values as given) updates the
 // running value, a = fp32(fp32(a * beta) + fp32(cur * (1 - beta))), and the tensor's BF16 copy is
 // quantized with s = max(fp32(a / fmt_max), 1e-12).  The global max needs the whole tensor before
-// any code can be written, so it takes three passes:
-//   tensor_amax_kernel    per-block partial maxima (grid-stride over rows, 16-byte loads);
-//   tensor_scale_kernel   one block: max of the partials, the running-amax update, the scale;
-//   tensor_quant_kernel   codes with the given scale (any row count), or the TENSOR mode of the
-//                         128x128 dual kernel above when transposed codes are wanted as well.
+// any code can be written, so it takes two passes:
+//   tensor_amax_kernel    per-block partial maxima (grid-stride over rows, 16-byte loads); block 0
+//                         also saves the running amax as it was;
+//   tensor_quant_kernel   each block reduces the partials to the scale (tensor_scale) and writes
+//                         codes (any row count); or the TENSOR mode of the 128x128 dual kernel
+//                         above when transposed codes are wanted as well.
 // ---------------------------------------------------------------------------------------------
 constexpr int kTensorRowsPerIter = 4;
 
@@ -422,8 +454,9 @@ __device__ __forceinline__ void for_tensor_chunks(const TIn* x, int64_t R, int64
 
 template <typename TIn>
 __global__ __launch_bounds__(256) void tensor_amax_kernel(const TIn* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
-                                                          float* __restrict__ partial) {
+                                                          const float* __restrict__ amax, float* __restrict__ partial) {
   __shared__ float wmax[4];
+  if (blockIdx.x == 0 && threadIdx.x == 0) partial[kTensorAmaxBlocks] = amax[0];
   float m = 0.0f;
   for_tensor_chunks(x, R, C, ldx, [&](int64_t, int64_t, const float (&v)[8]) {
 #pragma unroll
@@ -436,30 +469,11 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const TIn* __restrict_
     partial[blockIdx.x] = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
 }
 
-// One block of 256 threads.  b1 = fp32(beta), b2 = fp32(1 - beta) (formed in double on the host).
-template <int FMT>
-__global__ __launch_bounds__(256) void tensor_scale_kernel(const float* __restrict__ partial, int n,
-                                                           float* __restrict__ amax, float b1, float b2,
-                                                           float* __restrict__ s) {
-  __shared__ float wmax[4];
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) m = __builtin_fmaxf(m, partial[i]);
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float cur = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
-    const float a = __fadd_rn(__fmul_rn(amax[0], b1), __fmul_rn(cur, b2));  // two products, one sum
-    amax[0] = a;
-    s[0] = group_scale<FMT>(a);
-  }
-}
-
 template <typename TIn, int FMT>
 __global__ __launch_bounds__(256) void tensor_quant_kernel(const TIn* __restrict__ x, int64_t R, int64_t C,
-                                                           int64_t ldx, const float* __restrict__ s,
-                                                           uint8_t* __restrict__ q, int64_t ldq) {
-  const float sc = s[0];
+                                                           int64_t ldx, TensorScaleArgs ta, uint8_t* __restrict__ q,
+                                                           int64_t ldq) {
+  const float sc = tensor_scale<FMT>(ta);
   const float rc = 1.0f / sc;
   for_tensor_chunks(x, R, C, ldx, [&](int64_t r, int64_t c, const float (&v)[8]) {
     float b[8];
@@ -556,7 +570,7 @@ static hipError_t launch_128x128_dual_t(const void* w, int64_t N, int64_t K, int
                                         float* s, int64_t lds, uint8_t* qt, int64_t ldqt, hipStream_t st) {
   dim3 grid((unsigned)(K / kGroup), (unsigned)(N / kGroup));
   hipLaunchKernelGGL((quant_128x128_dual_kernel<TIn, FMT>), grid, dim3(256), 0, st, (const TIn*)w, ldw, q, ldq, s,
-                     lds, qt, ldqt);
+                     lds, qt, ldqt, TensorScaleArgs{});
   return hipGetLastError();
 }
 
@@ -579,16 +593,16 @@ static hipError_t launch_tensor_t(const void* x, int64_t R, int64_t C, int64_t l
                                   uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s, float* partial,
                                   hipStream_t st) {
   const int nb = tensor_amax_blocks(R);
-  hipLaunchKernelGGL((tensor_amax_kernel<TIn>), dim3(nb), dim3(256), 0, st, (const TIn*)x, R, C, ldx, partial);
-  hipLaunchKernelGGL((tensor_scale_kernel<FMT>), dim3(1), dim3(256), 0, st, (const float*)partial, nb, amax, b1, b2,
-                     s);
+  hipLaunchKernelGGL((tensor_amax_kernel<TIn>), dim3(nb), dim3(256), 0, st, (const TIn*)x, R, C, ldx,
+                     (const float*)amax, partial);
+  const TensorScaleArgs ta{partial, nb, b1, b2, amax, s};
   if (qt) {
     dim3 grid((unsigned)(C / kGroup), (unsigned)(R / kGroup));
     hipLaunchKernelGGL((quant_128x128_dual_kernel<TIn, FMT, true>), grid, dim3(256), 0, st, (const TIn*)x, ldx, q,
-                       ldq, s, (int64_t)0, qt, ldqt);
+                       ldq, s, (int64_t)0, qt, ldqt, ta);
   } else {
-    hipLaunchKernelGGL((tensor_quant_kernel<TIn, FMT>), dim3(nb), dim3(256), 0, st, (const TIn*)x, R, C, ldx,
-                       (const float*)s, q, ldq);
+    hipLaunchKernelGGL((tensor_quant_kernel<TIn, FMT>), dim3(nb), dim3(256), 0, st, (const TIn*)x, R, C, ldx, ta, q,
+                       ldq);
   }
   return hipGetLastError();
 }

@@ -156,6 +156,33 @@ int validate_quant_tensor(const void* x, int xt, int64_t R, int64_t C, int64_t l
   return kOk;
 }
 
+static bool finite_nonneg(double v) { return v >= 0.0 && v <= 1.7976931348623157e308; }
+
+int validate_hyperball(const void* w, int64_t ldw, const void* g, int gt, int64_t ldg, int64_t R, int64_t C,
+                       double lr, double wd, double eps, double radius, const void* norms, const void* ws,
+                       size_t ws_bytes, size_t ws_needed, bool* empty) {
+  *empty = false;
+  if (in_esize(gt) == 0) return kErrDtype;
+  if (!finite_nonneg(lr) || !finite_nonneg(wd) || !finite_nonneg(radius) || !(finite_nonneg(eps) && eps > 0.0))
+    return kErrValue;
+  if (R < 0 || C < 0 || C % 8 != 0) return kErrShape;
+  if (R == 0 || C == 0) {
+    *empty = true;
+    return kOk;
+  }
+  if (w == nullptr || g == nullptr || ws == nullptr) return kErrNull;
+  const Mat mw{w, R, C, ldw, 4}, mg{g, R, C, ldg, in_esize(gt)};
+  int st;
+  if ((st = check_mat(mw, true)) != kOk) return st;
+  if ((st = check_mat(mg, true)) != kOk) return st;
+  if (!aligned16(ws) || (norms != nullptr && !aligned4(norms))) return kErrAlign;
+  if (ws_bytes < ws_needed) return kErrWorkspace;
+  const Mat mws{ws, 1, (int64_t)ws_needed, (int64_t)ws_needed, 1}, mn{norms, 1, 2, 2, 4};
+  if (overlaps(mw, mg) || overlaps(mws, mw) || overlaps(mws, mg)) return kErrOverlap;
+  if (norms != nullptr && (overlaps(mn, mw) || overlaps(mn, mg) || overlaps(mn, mws))) return kErrOverlap;
+  return kOk;
+}
+
 int validate_gemm(const GemmArgs& g, size_t ws_needed, bool* empty, bool* zero_fill) {
   *empty = false;
   *zero_fill = false;

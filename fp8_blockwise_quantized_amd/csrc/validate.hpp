@@ -54,6 +54,12 @@ int validate_quant_tensor(const void* x, int xt, int64_t R, int64_t C, int64_t l
                           double beta, const void* q, int64_t ldq, const void* qt, int64_t ldqt, const void* s,
                           const void* ws, size_t ws_bytes, size_t ws_needed, bool* empty);
 
+// Hyperball step: w [R, C] FP32, g [R, C] (BF16 or FP32), C % 8 == 0; lr >= 0, wd >= 0, eps > 0,
+// radius >= 0, all finite; norms NULL or two 4-byte-aligned floats; ws >= ws_needed bytes.
+int validate_hyperball(const void* w, int64_t ldw, const void* g, int gt, int64_t ldg, int64_t R, int64_t C,
+                       double lr, double wd, double eps, double radius, const void* norms, const void* ws,
+                       size_t ws_bytes, size_t ws_needed, bool* empty);
+
 // The three GEMMs share one validator: op selects the operand shapes.
 struct GemmArgs {
   int op;

@@ -61,7 +61,7 @@ typedef enum {
   FP8BQ_ERR_DEVICE = 8,    /* no current HIP device, or it is not gfx950 */
   FP8BQ_ERR_LAUNCH = 9,    /* the kernel launch itself failed */
   FP8BQ_ERR_OVERLAP = 10,  /* an output overlaps an input the same call reads */
-  FP8BQ_ERR_VALUE = 11     /* a scalar argument is out of range (beta outside [0, 1]) */
+  FP8BQ_ERR_VALUE = 11     /* a scalar argument is out of range or not finite */
 } fp8bq_status;
 
 /* OCP FP8 formats: E4M3 = float8_e4m3fn (bias 7, no Inf, max 448);
@@ -257,8 +257,9 @@ int fp8bq_gemm_wgrad(int64_t M, int64_t N, int64_t K,
  *   ws         at least fp8bq_quantize_tensor_workspace_size(R, C) bytes, 16-byte aligned
  *              (per-block partial maxima; its contents are not needed between calls).
  * Errors: FP8BQ_ERR_VALUE for beta outside [0, 1] (or NaN); FP8BQ_ERR_ALIGN for amax or s not
- * 4-byte aligned; otherwise as the blockwise quantizers.  Three kernels run on `stream` in order
- * (partial maxima, the running-amax update and scale, the codes).
+ * 4-byte aligned; otherwise as the blockwise quantizers.  Two kernels run on `stream` in order:
+ * the partial maxima, then the codes (every block derives the scale from the partials; the first
+ * also stores the new running amax and the scale).
  */
 size_t fp8bq_quantize_tensor_workspace_size(int64_t R, int64_t C);
 int fp8bq_quantize_tensor_delayed(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx, fp8bq_fp8 fmt,
@@ -281,6 +282,36 @@ int fp8bq_quantize_tensor_delayed(const void* x, fp8bq_in xt, int64_t R, int64_t
 int fp8bq_gemm_tensor(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_t ldqa, const float* sa,
                       fp8bq_fp8 fa, const uint8_t* qb, int64_t ldqb, const float* sb, fp8bq_fp8 fb, void* out,
                       fp8bq_out out_t, int64_t ldout, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Hyperball normalized update of one weight matrix, in place, with the optional fixed-radius
+ * projection.
+ * Defining passages: "用 RTX 5090 花 $7000 训练 2B 大模型：Puro-2B 低成本预训练技术解析", section
+ * "Hyperball 优化：让 FP8 训练不爆炸" (HyperballSGD: only the gradient's direction is used, with
+ * decoupled weight decay); "小团队也能预训练！普罗2B：RTX5090训练成本不到5090美元", MuonH paragraph, and
+ * "Puro-2B: Poor Lab's Qwen2-1.5B Trained on RTX 5090 within $5090", section "方法关键点" (MuonH:
+ * after the update the weight is projected back onto a fixed radius).
+ *
+ *   n = max(||g||_2, eps);  w <- fp32(w * fp32(1 - lr*wd)) + fp32(g * fp32(-lr / n));
+ *   if radius > 0 and ||w||_F > 0:  w <- fp32(w * fp32(radius / ||w||_F)).
+ * Norms are summed in fp64 over fixed per-block partials (deterministic).
+ *   w       [R, C] FP32 master weights (ldw >= C), read and written.
+ *   g       [R, C] gradient, BF16 or FP32 (gt), ldg >= C; for example dW from fp8bq_gemm_wgrad.
+ *   C % 8 == 0.  R == 0 or C == 0: nothing is enqueued.
+ *   lr >= 0, weight_decay >= 0, eps > 0, radius >= 0 (0: no projection), all finite; else
+ *           FP8BQ_ERR_VALUE.  The pages' defaults are lr 1e-4, weight_decay 0.1, eps 1e-8.
+ *   norms   NULL, or two device floats (4-byte aligned) that receive ||g||_2 (before the clamp) and
+ *           ||w||_F after the update and before the projection.
+ *   ws      at least fp8bq_hyperball_workspace_size(R, C) bytes, 16-byte aligned.
+ * w may not overlap g, ws or norms (FP8BQ_ERR_OVERLAP).  Two or three sweeps run on `stream` in
+ * order: the gradient's sums of squares; the update (each block reduces those to the step
+ * coefficient, and sums the new weights' squares when a radius or norms are asked for); then, with a
+ * radius, the scaling (each block reduces those to the projection factor).
+ */
+size_t fp8bq_hyperball_workspace_size(int64_t R, int64_t C);
+int fp8bq_hyperball_step(float* w, int64_t ldw, const void* g, fp8bq_in gt, int64_t ldg, int64_t R, int64_t C,
+                         double lr, double weight_decay, double eps, double radius, float* norms, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /* Workspace bytes the given GEMM needs at these sizes on the current device (0 if none).
  * Returns 0 for invalid arguments too; the GEMM call itself reports those. */

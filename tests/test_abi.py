@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fq.lib()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -226,13 +226,13 @@ def test_gemm_dgrad_wt_validation():
 
 
 def qtensor(x=P(0), xt=0, R=256, C=256, ldx=256, fmt=0, amax=P(1), beta=0.99, q=P(2), ldq=256, qt=P(3), ldqt=256,
-            s=ctypes.c_void_p(0x100000 * 2 + 64), ws=P(4), ws_bytes=4096):
+            s=ctypes.c_void_p(0x100000 * 2 + 64), ws=P(4), ws_bytes=8192):
     return fq.lib().fp8bq_quantize_tensor_delayed(x, xt, R, C, ldx, fmt, amax, beta, q, ldq, qt, ldqt, s, ws, ws_bytes,
                                                   S0)
 
 
 def test_quant_tensor_delayed_validation():
-    assert fq.fp8bq_quantize_tensor_workspace_size(256, 256) == 4096
+    assert 4096 < fq.fp8bq_quantize_tensor_workspace_size(256, 256) <= 8192
     assert fq.fp8bq_quantize_tensor_workspace_size(0, 256) == 0
     valid(lambda: qtensor(s=P(5)))
     valid(lambda: qtensor(s=P(5), qt=NUL, R=200))  # ragged rows without the transposed codes
@@ -265,3 +265,27 @@ def test_gemm_tensor_validation():
     assert gt(out=P(0)) == OVERLAP
     assert gt(M=0, qa=NUL, out=NUL) == OK
     assert fq.fp8bq_gemm_plan(fq.OP_TENSOR, 4096, 2048, 2048) == fq.fp8bq_gemm_plan(fq.OP_FPROP, 4096, 2048, 2048)
+
+
+def hb(w=P(0), ldw=256, g=P(1), gt=0, ldg=256, R=256, C=256, lr=1e-4, wd=0.1, eps=1e-8, radius=0.0, norms=P(2),
+       ws=P(3), ws_bytes=1 << 16):
+    return fq.lib().fp8bq_hyperball_step(w, ldw, g, gt, ldg, R, C, lr, wd, eps, radius, norms, ws, ws_bytes, S0)
+
+
+def test_hyperball_validation():
+    need = fq.fp8bq_hyperball_workspace_size(256, 256)
+    assert 16 * 1024 <= need <= 1 << 16 and fq.fp8bq_hyperball_workspace_size(0, 8) == 0
+    valid(lambda: hb())
+    valid(lambda: hb(norms=NUL, radius=3.0, C=264, ldw=264, ldg=264, R=7))
+    assert hb(R=0) == OK
+    assert hb(gt=2) == DTYPE
+    assert hb(C=100, ldw=256, ldg=256) == SHAPE
+    for bad in (dict(lr=-1.0), dict(wd=-0.1), dict(eps=0.0), dict(eps=float("inf")), dict(radius=-2.0),
+                dict(lr=float("nan")), dict(radius=float("inf"))):
+        assert hb(**bad) == VALUE, bad
+    assert hb(w=NUL) == NULL and hb(ws=NUL) == NULL
+    assert hb(ldw=100) == LD and hb(ldg=250) == LD
+    assert hb(norms=ctypes.c_void_p(0x300002)) == ALIGN
+    assert hb(ws_bytes=need - 1) == WORKSPACE
+    assert hb(g=P(0)) == OVERLAP  # gradient on top of the weights
+    assert hb(norms=ctypes.c_void_p(0x100000 + 64)) == OVERLAP  # norms inside w
