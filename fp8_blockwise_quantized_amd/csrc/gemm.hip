@@ -340,17 +340,21 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   constexpr int NIN = STREAM_B ? MI : NI;   // resident patches
   constexpr int NTILE = MI * NI;
   constexpr int LAG = 2;
-  constexpr int TAIL0 = (NOUT - 2) * NIN;  // first MFMA of the two-patch tail
-  constexpr int UB = TAIL0 + 1;            // step that ends with the stage barrier
+#ifndef FP8BQ_TAILN
+#define FP8BQ_TAILN 3
+#endif
+  constexpr int TAILN = (PERM && NOUT >= 6) ? FP8BQ_TAILN : 2;  // streamed patches in the tail
+  constexpr int TAIL0 = (NOUT - TAILN) * NIN;  // first MFMA of the tail
+  constexpr int UB = TAIL0 + TAILN - 1;        // step that ends with the stage barrier
   constexpr int NPOST = NTILE + LAG - UB - 1;  // steps after it
-  static_assert(NOUT >= 2 && NPOST >= 1, "tile too small for the pipelined order");
+  static_assert(NOUT >= TAILN && NPOST >= 1, "tile too small for the pipelined order");
   auto order = [&](int u, int& o, int& k) {
     if (u < TAIL0) {
       o = u / NIN;
       k = u % NIN;
     } else {
-      o = NOUT - 2 + (u - TAIL0) % 2;
-      k = (u - TAIL0) / 2;
+      o = NOUT - TAILN + (u - TAIL0) % TAILN;
+      k = (u - TAIL0) / TAILN;
     }
   };
   const PatchLane pl = patch_lane(lane);

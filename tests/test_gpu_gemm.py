@@ -312,13 +312,14 @@ def test_large_tile_ragged_edges(out_dtype):
     checked(run_dgrad(dY, Wd, out_dtype=out_dtype), "256x256 ragged dgrad", f32)
 
 
-@pytest.mark.parametrize("shape", [(4096, 4480, 2432), (16384, 2432, 1408)])
+@pytest.mark.parametrize("shape", [(4096, 4480, 2432), (16384, 2944, 1664)])
 def test_large_tile_wgrad(shape):
-    """wgrad on 256x256 tiles: ragged output columns (2432 = 9.5 tiles) without and with a split
-    contraction (FP32 partial sums)."""
+    """wgrad on 256x256 tiles: ragged output columns (2432 = 9.5 tiles) without a split, and ragged
+    rows and columns (2944 = 11.5, 1664 = 6.5 tiles) with a split contraction (FP32 partial sums)."""
     M, N, K = shape
     tm, tn, split = fq.fp8bq_gemm_plan(fq.OP_WGRAD, M, N, K)
     assert TILE_FORCED or (tm, tn) == (256, 256)
+    assert TILE_FORCED or (split > 1) == (M == 16384)
     dY = synth.random_bf16((M, N), seed=305 + N, std=1e-3)
     X = synth.random_bf16((M, K), seed=306 + K, outliers=True)
     checked(run_wgrad(dY, X, ncols=_sample(N, 160, 7), kcols=_sample(K, 160, 8)), f"256x256 wgrad {shape} split {split}")
