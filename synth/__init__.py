@@ -26,6 +26,10 @@ and 2 key/value heads of 128, SwiGLU intermediate 5632):
    for M in 512 .. 32768;
 5. heavy-tailed gradients, seed 4: dY[16384, 5632] Student-t(3) * 1e-3,
    X[16384, 2048] N(0,1) with outliers, W[5632, 2048] N(0,0.02).
+
+Tensors too large to draw on the host (the beyond-4-GiB tests) come from
+``device_normal_bf16``: torch's seeded generator on the device, N(0, s) in
+fp32 rounded to BF16.
 """
 
 import numpy as np
@@ -140,3 +144,15 @@ def random_bf16(shape, seed, std=1.0, outliers=False):
 def random_f32(shape, seed, std=1.0):
     rng = _streams(seed, 1)[0]
     return normal(rng, shape, std, torch.float32)
+
+
+def device_normal_bf16(shape, seed, device, std=1.0, chunk_rows=1 << 18):
+    """N(0, std) BF16 tensor drawn on `device` by torch's generator seeded with `seed`, one block of
+    rows at a time (for tensors of several GiB); the same seed gives the same tensor."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    for r0 in range(0, shape[0], chunk_rows):
+        r1 = min(shape[0], r0 + chunk_rows)
+        out[r0:r1] = (torch.randn((r1 - r0,) + tuple(shape[1:]), generator=g, device=device) * std).to(torch.bfloat16)
+    return out
