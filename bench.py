@@ -8,11 +8,15 @@ One step = the whole path for one synthetic 2B-class decoder block at M = 16384 
     quantize dY both ways in one pass, dgrad dX = dY W, wgrad dW = dY^T X
 i.e. 12 quantize passes and 12 GEMMs, all E4M3, BF16 in and out, inputs resident in HBM.
 
-    python bench.py [--steps K] [--warmup W] [--workload decoder|delayed|hyperball|linear|sweep] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload decoder|delayed|hyperball|linear|sweep|qerror]
+                    [--no-cpu-baseline]
 
 `--workload delayed` runs the same decoder-block step with per-tensor delayed scaling instead (one
 running amax and one scale per tensor, X / W / dY each quantized once with transposed codes, the
 three GEMMs with per-tensor scales): the pages' own alternative recipe, as a comparison point.
+`--workload qerror` is not a timing: on the heavy-tailed gradient workload it reports the relative
+Frobenius error of dgrad and wgrad against float64 products of the unquantized BF16 inputs, with dY
+in E5M2 and in E4M3 (sampled rows / columns).
 `--workload hyperball` times the Hyperball update (with the fixed-radius projection) of the decoder
 block's four FP32 master weights from BF16 gradients, and reports GB/s.
 
@@ -46,7 +50,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", choices=["decoder", "delayed", "hyperball", "linear", "sweep"], default="decoder")
+    p.add_argument("--workload", choices=["decoder", "delayed", "hyperball", "linear", "sweep", "qerror"],
+                   default="decoder")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=4096)
     p.add_argument("--calibrate", action="store_true",
@@ -88,6 +93,8 @@ def main():
         ops, bufs, desc = build_delayed(torch, fq, synth, dev)
     elif args.workload == "hyperball":
         return run_hyperball(args, torch, fq, synth, dev)
+    elif args.workload == "qerror":
+        return run_qerror(torch, fq, synth, dev)
     elif args.workload == "linear":
         ops, bufs, desc = build_linear(torch, fq, synth, dev)
     else:
@@ -370,6 +377,41 @@ def run_hyperball(args, torch, fq, synth, dev):
                       "config": {"workload": "decoder-block weights (QKV, O, gate+up, down), FP32 masters, "
                                              "BF16 gradients"},
                       "per_weight": per}), flush=True)
+
+
+def run_qerror(torch, fq, synth, dev):
+    """Quantization error of the heavy-tailed gradient workload (dY Student-t(3) * 1e-3 [16384, 5632],
+    X [16384, 2048] with outlier columns, W [5632, 2048]): relative Frobenius error of the FP8 dgrad
+    (dY . W) and wgrad (dY^T . X) against float64 products of the unquantized BF16 inputs, for dY in
+    E5M2 and in E4M3 (X and W in E4M3), on 256 sampled rows of dX and 128 x 128 sampled entries of dW."""
+    import numpy as np
+    c = synth.config5()
+    dY, X, W = c["dY"], c["X"], c["W"]
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(dY.shape[0], 256, replace=False))
+    ncols = np.sort(rng.choice(dY.shape[1], 128, replace=False))
+    kcols = np.sort(rng.choice(X.shape[1], 128, replace=False))
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    ref_dx = f64(dY[rows]) @ f64(W)
+    ref_dw = f64(dY[:, ncols]).T @ f64(X[:, kcols])
+    dYd, Xd, Wd = dY.to(dev), X.to(dev), W.to(dev)
+    qw, sw, qwt = fq.quantize_weight_dual(Wd, fq.E4M3)
+    qxt, sxt = fq.quantize_act_128x1(Xd, fq.E4M3)
+    out = {}
+    rel = lambda got, ref: float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    for name, fmt in (("e5m2", fq.E5M2), ("e4m3", fq.E4M3)):
+        q, s, qt, st = fq.quantize_act_dual(dYd, fmt, fmt)
+        dx = fq.gemm_dgrad_wt(q, s, qwt, sw, fmt, fq.E4M3, out_dtype=torch.float32)
+        dw = fq.gemm_wgrad(qt, st, qxt, sxt, fmt, fq.E4M3, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        got_dx = dx[torch.from_numpy(rows).to(dev)].double().cpu().numpy()
+        got_dw = dw.double().cpu().numpy()[np.ix_(ncols, kcols)]
+        out[name] = {"dgrad_rel_frobenius": rel(got_dx, ref_dx), "wgrad_rel_frobenius": rel(got_dw, ref_dw)}
+        log(name, out[name])
+    print(json.dumps({"report": "quantization error, heavy-tailed gradients (dY Student-t(3) * 1e-3), "
+                                "FP8 GEMM (FP32 out) vs float64 of the unquantized BF16 inputs",
+                      "dy_format": out, "x_w_format": "e4m3",
+                      "sample": "256 rows of dX [16384, 2048]; 128 x 128 entries of dW [5632, 2048]"}), flush=True)
 
 
 def build_linear(torch, fq, synth, dev):

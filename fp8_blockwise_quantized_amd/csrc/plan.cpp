@@ -24,7 +24,9 @@ static double block_us(int shape) { return shape == k256x256 ? 2.05 : 1.2; }
 
 // Cost model in microseconds: rounds of resident units x blocks per unit x block time, plus, for a
 // split, a pass that writes and re-reads split x rows x cols FP32 partials and writes the output
-// (~5 TB/s effective).  Splitting pays off only when the tiles alone leave workgroup slots idle.
+// (~5 TB/s effective) and costs a fixed ~6 us as a launch of its own (measured: a 512-token fprop
+// split in two took 18.9 us where 1024 tokens unsplit took 15.8).  Splitting pays off only when
+// the tiles alone leave workgroup slots idle.
 // A last round that fills only a fraction f of the slots runs faster than a full one (less
 // contention for memory and power): it is charged (1 + f) / 2 of a round, as measured on MI355X
 // (a half-full last round of 256x256 tiles took ~0.74 of a full one).
@@ -35,7 +37,7 @@ static double split_cost(int64_t rows, int64_t cols, int64_t nkb, int64_t slots,
   const double frac = (double)(units - full * slots) / (double)slots;
   const double rounds = (double)full + (frac > 0.0 ? 0.5 * (1.0 + frac) : 0.0);
   const double gemm_us = rounds * ((double)nkb / s) * block_us(shape);
-  const double red_us = s > 1 ? (8.0 * s + 4.0) * (double)rows * (double)cols / 5.0e6 : 0.0;
+  const double red_us = s > 1 ? 6.0 + (8.0 * s + 4.0) * (double)rows * (double)cols / 5.0e6 : 0.0;
   return gemm_us + red_us;
 }
 
