@@ -333,8 +333,8 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
 
   // The side with fewer 16-row patches stays in registers for the whole block ("resident"); the
   // other side is streamed one patch at a time.  MFMA order: streamed patch outer, except for the
-  // last two streamed patches, which alternate (resident patch outer) so that resident patch k is
-  // free after MFMA 2k+1 of that tail.
+  // last TAILN streamed patches (the tail), which alternate (resident patch outer) so that resident
+  // patch k is free after MFMA TAILN*k + TAILN-1 of the tail.
   constexpr bool STREAM_B = NI > MI;
   constexpr int NOUT = STREAM_B ? NI : MI;  // streamed patches
   constexpr int NIN = STREAM_B ? MI : NI;   // resident patches

@@ -1,5 +1,6 @@
-// Blockwise FP8 quantize kernels for gfx950: 1x128 (activations), 128x1 (token axis, transposed
-// output for wgrad) and 128x128 (weights).
+// FP8 quantize kernels for gfx950: blockwise 1x128 (activations), 128x1 (token axis, transposed
+// output for wgrad), both at once (dual), 128x128 (weights, optionally also transposed), and the
+// per-tensor delayed-scaling variant at the end of the file.
 //
 // Rule per group ("用 RTX 5090 花 $7000 训练 2B 大模型：Puro-2B 低成本预训练技术解析", section
 // "核心挑战：Scale Factor 管理", FP8Linear._quantize): amax = max|x|; s = max(RN(amax/fmt_max), 1e-12);
@@ -7,7 +8,7 @@
 // 128x128 tiles ("Puro-2B: Poor Lab's Qwen2-1.5B Trained on RTX 5090 within $5090", "方法关键点",
 // bullet "FP8 blockwise 混合精度").
 //
-// All three passes are HBM-bound (about 3 bytes moved per element from BF16).  Each reads its input
+// The blockwise passes are HBM-bound (about 3 bytes moved per element from BF16).  Each reads its input
 // once with 16-byte coalesced loads, keeps the group in registers, reduces amax with DPP row
 // rotations (1x128, 128x128) or through LDS (128x1, whose groups run down columns), and writes codes
 // with 8- or 16-byte stores.  The division x/s uses the exact reciprocal-and-residual form in
