@@ -289,3 +289,23 @@ def test_hyperball_validation():
     assert hb(ws_bytes=need - 1) == WORKSPACE
     assert hb(g=P(0)) == OVERLAP  # gradient on top of the weights
     assert hb(norms=ctypes.c_void_p(0x100000 + 64)) == OVERLAP  # norms inside w
+
+
+def test_planner_decisions_documented_for_the_decoder_block():
+    """Plans the design records (device of 256 compute units; no GPU here, or an MI355X): the step's
+    fprop/dgrad on 256x256 tiles unsplit (the QKV fprop's half-filled last round is charged half a
+    round, which moves it off 128x128); small-token fprops are not split (the reduction pass costs a
+    fixed launch); long-contraction wgrads with few output tiles are."""
+    if HAVE_GPU and torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("plans are recorded for 256 compute units")
+    M = 16384
+    for K, N in [(2048, 2560), (2048, 2048), (2048, 11264), (5632, 2048)]:
+        assert fq.fp8bq_gemm_plan(fq.OP_FPROP, M, N, K) == (256, 256, 1), (K, N)
+        assert fq.fp8bq_gemm_plan(fq.OP_DGRAD_WT, M, N, K) == (256, 256, 1), (K, N)
+    assert fq.fp8bq_gemm_plan(fq.OP_WGRAD, M, 2560, 2048) == (256, 256, 3)
+    assert fq.fp8bq_gemm_plan(fq.OP_WGRAD, M, 2048, 2048) == (128, 128, 2)
+    for tokens in (512, 1024, 2048, 4096):
+        assert fq.fp8bq_gemm_plan(fq.OP_FPROP, tokens, 2048, 2048)[2] == 1, tokens
+    # the plan is a pure function of its arguments
+    assert all(fq.fp8bq_gemm_plan(fq.OP_WGRAD, 8192, 4096, 1024) == fq.fp8bq_gemm_plan(fq.OP_WGRAD, 8192, 4096, 1024)
+               for _ in range(3))
