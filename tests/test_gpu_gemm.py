@@ -403,3 +403,23 @@ def test_wgrad_accumulate_paths_and_empty_sum():
                                    fq.OUT_F32_ACCUM, 256, None, 0, None)
     torch.cuda.synchronize()
     assert st == 0 and torch.all(out == 3.25)
+
+
+# ------------------------------------------------------------------------------------------
+# contractions shorter than the LDS ring on 256x256 tiles (1-3 blocks: the ring reloads the last
+# block into its free slot; the first unit's prologue already covers the whole contraction)
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K", [128, 256, 384])
+def test_short_contraction_on_large_tiles(K):
+    M, N = 4096, 4096
+    assert TILE_FORCED or fq.fp8bq_gemm_plan(fq.OP_FPROP, M, N, K)[:2] == (256, 256)
+    X = synth.random_bf16((M, K), seed=700 + K, outliers=True)
+    W = synth.random_bf16((N, K), seed=701 + K, std=0.02)
+    checked(run_fprop(X, W, rows=_sample(M, 96, K)), f"fprop K={K} on 256x256 tiles")
+    # wgrad over K tokens: dW [4096, 4096] from dY [K, 4096] and X [K, 4096]
+    assert TILE_FORCED or fq.fp8bq_gemm_plan(fq.OP_WGRAD, K, N, M)[:2] == (256, 256)
+    dY = synth.random_bf16((K, N), seed=702 + K, std=1e-3)
+    Xw = synth.random_bf16((K, M), seed=703 + K, outliers=True)
+    checked(run_wgrad(dY, Xw, ncols=_sample(N, 96, K + 1), kcols=_sample(M, 96, K + 2)),
+            f"wgrad over {K} tokens on 256x256 tiles")
