@@ -250,7 +250,7 @@ def build_decoder(torch, fq, synth, dev):
     log("generating the decoder-block inputs ...")
     ops, bufs = [], []
     for name, K, N in synth.DECODER_LINEARS:
-        c = synth.config3_linear(name)
+        c = synth.decoder_linear(name)
         X, W, dY = c["X"].to(dev), c["W"].to(dev), c["dY"].to(dev)
         o, b = linear_ops(torch, fq, name, X, W, dY, dev)
         ops += o
@@ -314,7 +314,7 @@ def build_delayed(torch, fq, synth, dev):
     log("generating the decoder-block inputs ...")
     ops, bufs = [], []
     for name, K, N in synth.DECODER_LINEARS:
-        c = synth.config3_linear(name)
+        c = synth.decoder_linear(name)
         X, W, dY = c["X"].to(dev), c["W"].to(dev), c["dY"].to(dev)
         o, b = delayed_linear_ops(torch, fq, name, X, W, dY, dev)
         ops += o
@@ -385,7 +385,7 @@ def run_qerror(torch, fq, synth, dev):
     (dY . W) and wgrad (dY^T . X) against float64 products of the unquantized BF16 inputs, for dY in
     E5M2 and in E4M3 (X and W in E4M3), on 256 sampled rows of dX and 128 x 128 sampled entries of dW."""
     import numpy as np
-    c = synth.config5()
+    c = synth.heavy_tailed()
     dY, X, W = c["dY"], c["X"], c["W"]
     rng = np.random.default_rng(11)
     rows = np.sort(rng.choice(dY.shape[0], 256, replace=False))
@@ -415,7 +415,7 @@ def run_qerror(torch, fq, synth, dev):
 
 
 def build_linear(torch, fq, synth, dev):
-    c = synth.config2()
+    c = synth.single_linear()
     X, W = c["X"].to(dev), c["W"].to(dev)
     ops, bufs = linear_ops(torch, fq, "linear", X, W, None, dev, with_backward=False)
     desc = {"workload": "single fprop linear X[8192,2048] W[8192,2048], E4M3 act 1x128 / weight 128x128",
@@ -424,10 +424,10 @@ def build_linear(torch, fq, synth, dev):
 
 
 def run_sweep(args, torch, fq, synth, dev):
-    W = synth.config4_weight().to(dev)
+    W = synth.sweep_weight().to(dev)
     res = []
     for M in synth.SWEEP_M:
-        X = synth.config4_x(M).to(dev)
+        X = synth.sweep_x(M).to(dev)
         ops, bufs = linear_ops(torch, fq, f"M{M}", X, W, None, dev, with_backward=False)
         g = ops[2]
         for _ in range(args.warmup):
@@ -561,7 +561,7 @@ def cpu_baseline(tokens, desc):
     flops = 0
     t_total = 0.0
     for name, K, N in synth.DECODER_LINEARS:
-        c = synth.config3_linear(name)
+        c = synth.decoder_linear(name)
         X = c["X"][:tokens].float().numpy()
         dY = c["dY"][:tokens].float().numpy()
         W = c["W"].float().numpy()

@@ -34,7 +34,7 @@ Sources (cited by page title and section; the pages are the authority):
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 values the pages fix, closed forms, invariants, library routines on special
-cases and brute force; none is "parity unpinned" except the config-5
+cases and brute force; none is "parity unpinned" except the heavy-tailed-gradient
 quantization-error report, which is reported and not graded.
 """
 

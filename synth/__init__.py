@@ -35,7 +35,7 @@ fp32 rounded to BF16.
 import numpy as np
 import torch
 
-SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4}
+SEEDS = {"tiny": 0, "single": 1, "decoder": 2, "sweep": 3, "heavy": 4}
 
 DECODER_LINEARS = (
     # name, K (in), N (out)
@@ -81,8 +81,8 @@ def student_t(rng, shape, nu, scale, dtype=torch.bfloat16):
     return _to_torch(a, dtype)
 
 
-def config1():
-    r = _streams(SEEDS[1], 3)
+def tiny_check():
+    r = _streams(SEEDS["tiny"], 3)
     return {
         "A": normal(r[0], (256, 256), 1.0, torch.float32),
         "W": normal(r[1], (256, 256), 0.02, torch.float32),
@@ -90,20 +90,20 @@ def config1():
     }
 
 
-def config2():
-    r = _streams(SEEDS[2], 2)
+def single_linear():
+    r = _streams(SEEDS["single"], 2)
     return {
         "X": normal_outliers(r[0], (8192, 2048), 1.0),
         "W": normal(r[1], (8192, 2048), 0.02),
     }
 
 
-def config3_linear(name, M=DECODER_M):
+def decoder_linear(name, M=DECODER_M):
     """X, W, dY of one linear of the decoder block (independent streams)."""
     names = [n for n, _, _ in DECODER_LINEARS]
     i = names.index(name)
     _, K, N = DECODER_LINEARS[i]
-    r = _streams(SEEDS[3], 3 * len(DECODER_LINEARS))[3 * i: 3 * i + 3]
+    r = _streams(SEEDS["decoder"], 3 * len(DECODER_LINEARS))[3 * i: 3 * i + 3]
     return {
         "X": normal(r[0], (M, K), 1.0),
         "W": normal(r[1], (N, K), 0.02),
@@ -111,21 +111,21 @@ def config3_linear(name, M=DECODER_M):
     }
 
 
-def config3(M=DECODER_M):
-    return {n: config3_linear(n, M) for n, _, _ in DECODER_LINEARS}
+def decoder_block(M=DECODER_M):
+    return {n: decoder_linear(n, M) for n, _, _ in DECODER_LINEARS}
 
 
-def config4_weight():
-    return normal(_streams(SEEDS[4], 1 + len(SWEEP_M))[0], (2048, 2048), 0.02)
+def sweep_weight():
+    return normal(_streams(SEEDS["sweep"], 1 + len(SWEEP_M))[0], (2048, 2048), 0.02)
 
 
-def config4_x(M):
+def sweep_x(M):
     i = SWEEP_M.index(M)
-    return normal(_streams(SEEDS[4], 1 + len(SWEEP_M))[1 + i], (M, 2048), 1.0)
+    return normal(_streams(SEEDS["sweep"], 1 + len(SWEEP_M))[1 + i], (M, 2048), 1.0)
 
 
-def config5():
-    r = _streams(SEEDS[5], 3)
+def heavy_tailed():
+    r = _streams(SEEDS["heavy"], 3)
     return {
         "dY": student_t(r[0], (16384, 5632), 3, 1e-3),
         "X": normal_outliers(r[1], (16384, 2048), 1.0),

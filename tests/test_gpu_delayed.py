@@ -90,7 +90,7 @@ def test_strided_input_and_empty():
 
 def test_activation_size_sampled():
     """A 16384 x 2048 activation: the running amax and scale exactly, codes on sampled rows."""
-    c = synth.config3_linear("qkv")
+    c = synth.decoder_linear("qkv")
     X = c["X"]
     amax = torch.ones(1, dtype=torch.float32, device=DEV)
     q, s, qt = fq.quantize_tensor_delayed(X.to(DEV), amax, 0.99, fq.E4M3, transpose=True)
@@ -160,7 +160,7 @@ def test_gemm_tensor_three_products():
 
 
 def test_gemm_tensor_full_size_sampled():
-    c = synth.config3_linear("gate_up")
+    c = synth.decoder_linear("gate_up")
     X, W = c["X"], c["W"]
     qa, sa, _ = _quant_both(X, E4)
     qb, sb, _ = _quant_both(W, E4)

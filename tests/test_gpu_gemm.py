@@ -94,7 +94,7 @@ def checked(res, what, out_f32=False):
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_tiny_workload_all_products(out_dtype):
-    c = synth.config1()
+    c = synth.tiny_check()
     f32 = out_dtype == torch.float32
     checked(run_fprop(c["A"], c["W"], out_dtype=out_dtype), "tiny fprop", f32)
     checked(run_dgrad(c["dY"], c["W"], E5, E4, out_dtype=out_dtype), "tiny dgrad e5m2", f32)
@@ -105,7 +105,7 @@ def test_tiny_workload_all_products(out_dtype):
 
 def test_gemm_on_oracle_codes():
     """The GEMM alone: the oracle's codes and scales are uploaded, so no GPU quantizer is involved."""
-    c = synth.config1()
+    c = synth.tiny_check()
     qx, sx = oracle.quant_act_1x128(c["A"].numpy(), E4)
     qw, sw = oracle.quant_weight_128x128(c["W"].numpy(), E4)
     tq = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
@@ -226,7 +226,7 @@ def test_deterministic():
 # ------------------------------------------------------------------------------------------
 
 def test_single_linear_fprop_full_size():
-    c = synth.config2()
+    c = synth.single_linear()
     rows = _sample(8192, 192, 1)
     checked(run_fprop(c["X"], c["W"], rows=rows), "8192x8192x2048 fprop (sampled rows)")
 
@@ -234,7 +234,7 @@ def test_single_linear_fprop_full_size():
 @pytest.mark.parametrize("name", [n for n, _, _ in synth.DECODER_LINEARS])
 def test_decoder_block_full_size(name):
     say(f"decoder block linear {name}")
-    c = synth.config3_linear(name)
+    c = synth.decoder_linear(name)
     M, K = c["X"].shape
     N = c["W"].shape[0]
     rows = _sample(M, 96, 2)
@@ -244,14 +244,14 @@ def test_decoder_block_full_size(name):
 
 
 def test_sweep_fprop_all_sizes():
-    W = synth.config4_weight()
+    W = synth.sweep_weight()
     for M in synth.SWEEP_M:
-        X = synth.config4_x(M)
+        X = synth.sweep_x(M)
         checked(run_fprop(X, W, rows=_sample(M, 64, M)), f"sweep fprop M={M}")
 
 
 def test_heavy_tailed_gradients_full_size():
-    c = synth.config5()
+    c = synth.heavy_tailed()
     rows = _sample(16384, 96, 5)
     checked(run_dgrad(c["dY"], c["W"], E5, E4, rows=rows), "heavy-tail dgrad e5m2 x e4m3")
     ncols, kcols = _sample(5632, 48, 6), _sample(2048, 48, 7)

@@ -89,7 +89,7 @@ def test_encoder_every_decision_point(fmt):
 # ------------------------------------------------------------------------------------------
 
 def test_tiny_workload_all_quantizers():
-    c = synth.config1()
+    c = synth.tiny_check()
     A, W, dY = c["A"], c["W"], c["dY"]
     same(gpu_1x128(A, oracle.E4M3), oracle.quant_act_1x128(A.numpy(), oracle.E4M3), "A 1x128")
     same(gpu_w(W, oracle.E4M3), oracle.quant_weight_128x128(W.numpy(), oracle.E4M3), "W 128x128")
@@ -198,7 +198,7 @@ def test_deterministic():
 # ------------------------------------------------------------------------------------------
 
 def test_single_linear_full():
-    c = synth.config2()
+    c = synth.single_linear()
     say("8192x2048 activation and weight, full comparison")
     same(gpu_1x128(c["X"], oracle.E4M3), oracle.quant_act_1x128(c["X"].float().numpy(), oracle.E4M3), "X 1x128")
     same(gpu_w(c["W"], oracle.E4M3), oracle.quant_weight_128x128(c["W"].float().numpy(), oracle.E4M3), "W")
@@ -229,7 +229,7 @@ def _check_act_sampled(x, fmt, what, seed):
 @pytest.mark.parametrize("name", [n for n, _, _ in synth.DECODER_LINEARS])
 def test_decoder_block_sampled(name):
     say(f"decoder block linear {name}")
-    c = synth.config3_linear(name)
+    c = synth.decoder_linear(name)
     _check_act_sampled(c["X"], oracle.E4M3, f"{name} X", 1)
     _check_act_sampled(c["dY"], oracle.E4M3, f"{name} dY", 2)
     same(gpu_w(c["W"], oracle.E4M3), oracle.quant_weight_128x128(c["W"].float().numpy(), oracle.E4M3), f"{name} W")
@@ -237,16 +237,16 @@ def test_decoder_block_sampled(name):
 
 def test_sweep_activations_sampled():
     for M in synth.SWEEP_M:
-        x = synth.config4_x(M)
+        x = synth.sweep_x(M)
         rows = _sample(M, 128, M)
         q, s = gpu_1x128(x, oracle.E4M3)
         same((q[rows], s[rows]), oracle.quant_act_1x128(x[rows].float().numpy(), oracle.E4M3), f"sweep M={M}")
-    w = synth.config4_weight()
+    w = synth.sweep_weight()
     same(gpu_w(w, oracle.E4M3), oracle.quant_weight_128x128(w.float().numpy(), oracle.E4M3), "sweep W")
 
 
 def test_heavy_tailed_gradients_sampled():
-    c = synth.config5()
+    c = synth.heavy_tailed()
     _check_act_sampled(c["dY"], oracle.E5M2, "dY E5M2", 3)
     _check_act_sampled(c["dY"], oracle.E4M3, "dY E4M3", 4)
     _check_act_sampled(c["X"], oracle.E4M3, "X", 5)
@@ -299,7 +299,7 @@ def test_dual_edge_values_and_strides():
 @pytest.mark.parametrize("name", ["gate_up", "down"])
 def test_dual_decoder_block_sampled(name):
     """Full-size decoder-block activations: rows and columns sampled as in the single-layout checks."""
-    c = synth.config3_linear(name)
+    c = synth.decoder_linear(name)
     for key, fr, fc, seed in [("X", oracle.E4M3, oracle.E4M3, 11), ("dY", oracle.E5M2, oracle.E4M3, 12)]:
         x = c[key]
         R, C = x.shape
@@ -330,7 +330,7 @@ def test_weight_dual_shapes(fmt, shape, dt):
 
 
 def test_weight_dual_full_size_and_edges():
-    c = synth.config3_linear("gate_up")
+    c = synth.decoder_linear("gate_up")
     W = c["W"]
     q, s, qt = fq.quantize_weight_dual(W.to(DEV), fq.E4M3)
     torch.cuda.synchronize()

@@ -167,15 +167,15 @@ def test_wgrad_exact_rational():
 
 
 # --------------------------------------------------------------------------
-# per-block form vs dequantize-then-matmul (config-1 sizes)
+# per-block form vs dequantize-then-matmul (the 256 x 256 tiny-check sizes)
 # --------------------------------------------------------------------------
 
 def _rel(a, b):
     return np.max(np.abs(a - b)) / np.max(np.abs(b))
 
 
-def test_blockloops_agree_config1():
-    c = synth.config1()
+def test_blockloops_agree_tiny_check():
+    c = synth.tiny_check()
     A, W, dY = c["A"].numpy(), c["W"].numpy(), c["dY"].numpy()
     qa, sa = quant_act_1x128(A, E4M3)
     qw, sw = quant_weight_128x128(W, E4M3)
