@@ -285,7 +285,7 @@ const char* fp8bq_status_string(int status) {
     case kOk: return "FP8BQ_OK";
     case kErrNull: return "FP8BQ_ERR_NULL: a required pointer is NULL";
     case kErrShape: return "FP8BQ_ERR_SHAPE: negative size or a grouped/contracted size not a multiple of 128";
-    case kErrLd: return "FP8BQ_ERR_LD: leading dimension too small or misaligned";
+    case kErrLd: return "FP8BQ_ERR_LD: leading dimension too small, misaligned, or too large for a code operand";
     case kErrAlign: return "FP8BQ_ERR_ALIGN: pointer not 16-byte aligned";
     case kErrDtype: return "FP8BQ_ERR_DTYPE: unknown element type";
     case kErrFormat: return "FP8BQ_ERR_FORMAT: unknown FP8 format";

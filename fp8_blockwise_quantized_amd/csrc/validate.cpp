@@ -243,6 +243,12 @@ int validate_gemm(const GemmArgs& g, size_t ws_needed, bool* empty, bool* zero_f
   if (g.qa == nullptr || g.sa == nullptr || g.qb == nullptr || g.sb == nullptr) return kErrNull;
   if ((st = check_mat(qa, true)) != kOk) return st;
   if ((st = check_mat(qb, true)) != kOk) return st;
+  // The kernels reach one tile of a code operand (at most 256 rows of the contraction) through a
+  // buffer range of 32 bits: 255 row strides plus one row must stay below 4 GiB.  (dgrad's W codes
+  // are first transposed into the workspace with rows of N bytes.)
+  const int64_t kSpan = (int64_t)1 << 32;
+  if (255 * qa.ld + contraction >= kSpan) return kErrLd;
+  if (g.op != 1 && 255 * qb.ld + contraction >= kSpan) return kErrLd;
   if (g.op == 4) {  // the two scales are single floats
     if (!aligned4(g.sa) || !aligned4(g.sb)) return kErrAlign;
   } else {

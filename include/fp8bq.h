@@ -53,7 +53,10 @@ typedef enum {
   FP8BQ_OK = 0,
   FP8BQ_ERR_NULL = 1,      /* a required pointer is NULL */
   FP8BQ_ERR_SHAPE = 2,     /* negative size, or a grouped/contracted size not a multiple of 128 */
-  FP8BQ_ERR_LD = 3,        /* leading dimension smaller than the row length, or misaligned */
+  FP8BQ_ERR_LD = 3,        /* leading dimension smaller than the row length, or misaligned; for the
+                              GEMMs' code operands also 255 * ld + contraction length >= 2^32 bytes
+                              (a 256-row tile is addressed through a 32-bit range: rows of codes
+                              up to about 16.8 MB) */
   FP8BQ_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
   FP8BQ_ERR_DTYPE = 5,     /* unknown input or output element type */
   FP8BQ_ERR_FORMAT = 6,    /* unknown FP8 format */

@@ -140,6 +140,13 @@ def test_gemm_validation():
     valid(lambda: gemm(w, M=0, qa=NUL, sa=NUL, qb=NUL, sb=NUL, ldsb=256, out_t=2))  # an empty sum
     assert gemm(w, M=200, ldqa=208, ldqb=208, ldsb=256) == SHAPE  # contraction must be a multiple of 128
     assert gemm(w, ldsb=2) == LD  # column scales are read as vectors
+    # a 256-row tile of codes is addressed through a 32-bit range: 2^24 tokens is one too many rows
+    big = 1 << 24
+    assert gemm(w, M=big, ldqa=big, ldqb=big, ldsa=256, ldsb=256) == LD
+    far = lambda i: ctypes.c_void_p((i + 1) << 36)  # fake buffers 64 GiB apart
+    valid(lambda: gemm(w, M=big - 128, ldqa=big - 128, ldqb=big - 128, ldsb=256, qa=far(0), sa=far(1), qb=far(2),
+                       sb=far(3), out=far(4), ws=far(5), ws_bytes=1 << 34))
+    assert gemm("fp8bq_gemm_fprop", ldqa=(1 << 32) // 255) == LD
     # dgrad needs a workspace for the transposed weight codes
     need = fq.fp8bq_gemm_workspace_size(fq.OP_DGRAD, 256, 256, 256)
     assert need >= 256 * 256
