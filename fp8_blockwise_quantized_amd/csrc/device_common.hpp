@@ -103,6 +103,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Tile (row, column) of a block of a 2-D tile grid launched in one dimension (up to 2^31 blocks; a
+// grid's second dimension is much shorter), column tiles fastest as a 2-D grid would dispatch them.
+struct TileRC {
+  int64_t row, col;
+};
+__device__ __forceinline__ TileRC tile_of_block(uint32_t ncols) {
+  const uint32_t b = blockIdx.x;
+  const uint32_t r = b / ncols;
+  return TileRC{(int64_t)r, (int64_t)(b - r * ncols)};
+}
+
 // fp32 value of the nearest BF16 number (ties to even).
 __device__ __forceinline__ float round_bf16(float v) { return bf16lo(pack_bf16x2(v, 0.0f)); }
 

@@ -631,10 +631,11 @@ __device__ __forceinline__ void transpose4x4(uint32_t d0, uint32_t d1, uint32_t 
 }
 
 __global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __restrict__ src, int64_t lds,
-                                                           uint8_t* __restrict__ dst, int64_t ldd) {
+                                                           uint8_t* __restrict__ dst, int64_t ldd, uint32_t ncb) {
   __shared__ uint32_t tileT[128 * kTrStride];
   const int t = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
+  const TileRC tile = tile_of_block(ncb);
+  const int64_t r0 = tile.row * 128, c0 = tile.col * 128;
   const int rq = t >> 3, cq = t & 7;
   uint4 d[4];
 #pragma unroll
@@ -661,8 +662,8 @@ __global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __rest
 
 hipError_t launch_transpose_u8(const uint8_t* src, int64_t lds, uint8_t* dst, int64_t ldd, int64_t R, int64_t C,
                                hipStream_t st) {
-  hipLaunchKernelGGL(transpose_u8_kernel, dim3((unsigned)(C / 128), (unsigned)(R / 128)), dim3(256), 0, st, src, lds,
-                     dst, ldd);
+  const uint32_t ncb = (uint32_t)(C / 128);
+  hipLaunchKernelGGL(transpose_u8_kernel, dim3((unsigned)(R / 128) * ncb), dim3(256), 0, st, src, lds, dst, ldd, ncb);
   return hipGetLastError();
 }
 

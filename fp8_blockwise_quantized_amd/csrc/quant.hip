@@ -123,7 +123,7 @@ constexpr int kQtStride = 34;  // dwords per staged column (32 + 2 pad; even for
 template <typename TIn, int FMT>
 __global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict__ x, int64_t C, int64_t ldx,
                                                           uint8_t* __restrict__ qt, int64_t ldqt,
-                                                          float* __restrict__ st, int64_t ldst) {
+                                                          float* __restrict__ st, int64_t ldst, uint32_t ncg) {
   __shared__ float red[16][kQtCols + 1];
   __shared__ float ssc[kQtCols];
   __shared__ float src[kQtCols];
@@ -132,8 +132,9 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict_
   const int t = threadIdx.x;
   const int cc = t & 15;
   const int rg = t >> 4;
-  const int64_t rb = blockIdx.y;
-  const int64_t c0 = (int64_t)blockIdx.x * kQtCols;
+  const TileRC tile = tile_of_block(ncg);
+  const int64_t rb = tile.row;
+  const int64_t c0 = tile.col * kQtCols;
   const int64_t col = c0 + 8 * cc;
   const bool cvalid = col < C;  // C % 8 == 0, so a chunk is all in or all out
 
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const TIn* __restrict__
                                                          uint8_t* __restrict__ q, int64_t ldq,
                                                          float* __restrict__ s, int64_t lds,
                                                          uint8_t* __restrict__ qt, int64_t ldqt,
-                                                         float* __restrict__ st, int64_t ldst) {
+                                                         float* __restrict__ st, int64_t ldst, uint32_t ncg) {
   __shared__ float red[16][kQtCols + 1];
   __shared__ float ssc[kQtCols];
   __shared__ float src[kQtCols];
@@ -209,8 +210,9 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const TIn* __restrict__
   const int t = threadIdx.x;
   const int cc = t & 15;
   const int rg = t >> 4;
-  const int64_t rb = blockIdx.y;
-  const int64_t g = blockIdx.x;  // 128-column group
+  const TileRC tile = tile_of_block(ncg);
+  const int64_t rb = tile.row;
+  const int64_t g = tile.col;  // 128-column group
   const int64_t c0 = g * kQtCols;
   const int64_t col = c0 + 8 * cc;
 
@@ -282,12 +284,13 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const TIn* __restrict__
 template <typename TIn, int FMT>
 __global__ __launch_bounds__(256) void quant_128x128_kernel(const TIn* __restrict__ w, int64_t ldw,
                                                             uint8_t* __restrict__ q, int64_t ldq,
-                                                            float* __restrict__ s, int64_t lds) {
+                                                            float* __restrict__ s, int64_t lds, uint32_t nkb) {
   __shared__ float wmax[4];
   const int t = threadIdx.x;
   const int l16 = t & 15;
   const int rsub = t >> 4;
-  const int64_t kb = blockIdx.x, nb = blockIdx.y;
+  const TileRC tile = tile_of_block(nkb);
+  const int64_t kb = tile.col, nb = tile.row;
   const int64_t col = kb * kGroup + 8 * l16;
 
   float v[8][8];
@@ -334,7 +337,7 @@ __device__ __forceinline__ float tensor_scale(const TensorScaleArgs& a) {
   const float cur = __builtin_fmaxf(__builtin_fmaxf(tmax[0], tmax[1]), __builtin_fmaxf(tmax[2], tmax[3]));
   const float am = __fadd_rn(__fmul_rn(a.partial[kTensorAmaxBlocks], a.b1), __fmul_rn(cur, a.b2));
   const float sc = group_scale<FMT>(am);
-  if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
     a.amax[0] = am;
     a.s[0] = sc;
   }
@@ -354,13 +357,14 @@ __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __re
                                                                  uint8_t* __restrict__ q, int64_t ldq,
                                                                  float* __restrict__ s, int64_t lds,
                                                                  uint8_t* __restrict__ qt, int64_t ldqt,
-                                                                 TensorScaleArgs ta) {
+                                                                 TensorScaleArgs ta, uint32_t nkb) {
   __shared__ float wmax[4];
   __shared__ __attribute__((aligned(8))) uint32_t tileT[kQtCols * kQtStride];
   const int t = threadIdx.x;
   const int cc = t & 15;
   const int rg = t >> 4;
-  const int64_t kb = blockIdx.x, nb = blockIdx.y;
+  const TileRC tile = tile_of_block(nkb);
+  const int64_t kb = tile.col, nb = tile.row;
   const int64_t col = kb * kGroup + 8 * cc;
 
   float v[8][8];
@@ -507,9 +511,9 @@ hipError_t launch_quant_1x128(const void* x, int xt, int64_t R, int64_t C, int64
 template <typename TIn, int FMT>
 static hipError_t launch_128x1_t(const void* x, int64_t R, int64_t C, int64_t ldx, uint8_t* qt, int64_t ldqt,
                                  float* st_, int64_t ldst, hipStream_t st) {
-  dim3 grid((unsigned)((C + kQtCols - 1) / kQtCols), (unsigned)(R / kGroup));
-  hipLaunchKernelGGL((quant_128x1_kernel<TIn, FMT>), grid, dim3(256), 0, st, (const TIn*)x, C, ldx, qt, ldqt, st_,
-                     ldst);
+  const uint32_t ncg = (uint32_t)((C + kQtCols - 1) / kQtCols);
+  hipLaunchKernelGGL((quant_128x1_kernel<TIn, FMT>), dim3((unsigned)(R / kGroup) * ncg), dim3(256), 0, st, (const TIn*)x,
+                     C, ldx, qt, ldqt, st_, ldst, ncg);
   return hipGetLastError();
 }
 
@@ -525,9 +529,9 @@ hipError_t launch_quant_128x1(const void* x, int xt, int64_t R, int64_t C, int64
 template <typename TIn, int FR, int FC>
 static hipError_t launch_dual_t(const void* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q, int64_t ldq, float* s,
                                 int64_t lds, uint8_t* qt, int64_t ldqt, float* st_, int64_t ldst, hipStream_t st) {
-  dim3 grid((unsigned)(C / kQtCols), (unsigned)(R / kGroup));
-  hipLaunchKernelGGL((quant_dual_kernel<TIn, FR, FC>), grid, dim3(256), 0, st, (const TIn*)x, ldx, q, ldq, s, lds, qt,
-                     ldqt, st_, ldst);
+  const uint32_t ncg = (uint32_t)(C / kQtCols);
+  hipLaunchKernelGGL((quant_dual_kernel<TIn, FR, FC>), dim3((unsigned)(R / kGroup) * ncg), dim3(256), 0, st,
+                     (const TIn*)x, ldx, q, ldq, s, lds, qt, ldqt, st_, ldst, ncg);
   return hipGetLastError();
 }
 
@@ -552,8 +556,9 @@ hipError_t launch_quant_dual(const void* x, int xt, int64_t R, int64_t C, int64_
 template <typename TIn, int FMT>
 static hipError_t launch_128x128_t(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, int64_t ldq,
                                    float* s, int64_t lds, hipStream_t st) {
-  dim3 grid((unsigned)(K / kGroup), (unsigned)(N / kGroup));
-  hipLaunchKernelGGL((quant_128x128_kernel<TIn, FMT>), grid, dim3(256), 0, st, (const TIn*)w, ldw, q, ldq, s, lds);
+  const uint32_t nkb = (uint32_t)(K / kGroup);
+  hipLaunchKernelGGL((quant_128x128_kernel<TIn, FMT>), dim3((unsigned)(N / kGroup) * nkb), dim3(256), 0, st,
+                     (const TIn*)w, ldw, q, ldq, s, lds, nkb);
   return hipGetLastError();
 }
 
@@ -569,9 +574,9 @@ hipError_t launch_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int
 template <typename TIn, int FMT>
 static hipError_t launch_128x128_dual_t(const void* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, int64_t ldq,
                                         float* s, int64_t lds, uint8_t* qt, int64_t ldqt, hipStream_t st) {
-  dim3 grid((unsigned)(K / kGroup), (unsigned)(N / kGroup));
-  hipLaunchKernelGGL((quant_128x128_dual_kernel<TIn, FMT>), grid, dim3(256), 0, st, (const TIn*)w, ldw, q, ldq, s,
-                     lds, qt, ldqt, TensorScaleArgs{});
+  const uint32_t nkb = (uint32_t)(K / kGroup);
+  hipLaunchKernelGGL((quant_128x128_dual_kernel<TIn, FMT>), dim3((unsigned)(N / kGroup) * nkb), dim3(256), 0, st,
+                     (const TIn*)w, ldw, q, ldq, s, lds, qt, ldqt, TensorScaleArgs{}, nkb);
   return hipGetLastError();
 }
 
@@ -598,9 +603,9 @@ static hipError_t launch_tensor_t(const void* x, int64_t R, int64_t C, int64_t l
                      (const float*)amax, partial);
   const TensorScaleArgs ta{partial, nb, b1, b2, amax, s};
   if (qt) {
-    dim3 grid((unsigned)(C / kGroup), (unsigned)(R / kGroup));
-    hipLaunchKernelGGL((quant_128x128_dual_kernel<TIn, FMT, true>), grid, dim3(256), 0, st, (const TIn*)x, ldx, q,
-                       ldq, s, (int64_t)0, qt, ldqt, ta);
+    const uint32_t ncg = (uint32_t)(C / kGroup);
+    hipLaunchKernelGGL((quant_128x128_dual_kernel<TIn, FMT, true>), dim3((unsigned)(R / kGroup) * ncg), dim3(256), 0,
+                       st, (const TIn*)x, ldx, q, ldq, s, (int64_t)0, qt, ldqt, ta, ncg);
   } else {
     hipLaunchKernelGGL((tensor_quant_kernel<TIn, FMT>), dim3(nb), dim3(256), 0, st, (const TIn*)x, R, C, ldx, ta, q,
                        ldq);

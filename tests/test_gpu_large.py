@@ -80,3 +80,43 @@ def test_dual_and_wgrad_beyond_4gib():
     worst, _ = check_gemm(got, a.T @ b, row_norms(a.T), row_norms(b.T), out_f32=True, what="wgrad M=2.2M")
     say(f"wgrad over {M} tokens (split {fq.fp8bq_gemm_plan(fq.OP_WGRAD, M, N, K)[2]}): "
         f"max|err|/(|a||b|) = {worst:.2e}")
+
+
+def test_more_than_65535_row_blocks():
+    """8,388,864 rows (65,538 blocks of 128): the quantizers' tile grids are one-dimensional, so a
+    row-block count past the short grid dimensions' limit is still covered exactly once."""
+    R, C = 8_388_864, 128
+    X = synth.device_normal_bf16((R, C), seed=905, device=DEV)
+    q, s, qt, st = fq.quantize_act_dual(X)
+    qw, sw, qwt = fq.quantize_weight_dual(X)
+    amax = torch.ones(1, dtype=torch.float32, device=DEV)
+    qd, sd, qdt = fq.quantize_tensor_delayed(X, amax, 0.99, fq.E4M3, transpose=True)
+    torch.cuda.synchronize()
+    # 1x128 codes of sampled rows, with rows of the last blocks
+    rows = np.unique(np.concatenate([[0, R - 1, R - 128, R - 129], np.random.default_rng(7).choice(R, 40, replace=False)]))
+    ridx = torch.from_numpy(rows).to(DEV)
+    xs = X[ridx].float().cpu().numpy()
+    oq, os_ = oracle.quant_act_1x128(xs, E4)
+    assert np.array_equal(q[ridx].cpu().numpy(), oq)
+    assert np.array_equal(f32_bits(s[:, ridx].cpu().numpy().T), f32_bits(os_))
+    # 128x1 codes of two whole columns (every row block)
+    for c in (0, C - 1):
+        col = X[:, c:c + 1].float().cpu().numpy()
+        oqc, osc = oracle.quant_act_128x1(col, E4)
+        assert np.array_equal(qt[c].cpu().numpy(), oqc[:, 0]), c
+        assert np.array_equal(f32_bits(st[:, c].cpu().numpy()), f32_bits(osc[:, 0])), c
+    # 128x128 weight codes of the first and last tiles, and their transpose
+    for r0 in (0, R - 128):
+        tile = X[r0:r0 + 128].float().cpu().numpy()
+        oqw, osw = oracle.quant_weight_128x128(tile, E4)
+        assert np.array_equal(qw[r0:r0 + 128].cpu().numpy(), oqw), r0
+        assert f32_bits(sw[r0 // 128].cpu().numpy())[0] == f32_bits(osw)[0, 0], r0
+        assert np.array_equal(qwt[:, r0:r0 + 128].cpu().numpy(), oqw.T), r0
+    # per-tensor codes and their transpose on the same rows
+    a = oracle.amax_ema_update(np.float32(1.0), X.float().abs().max().cpu().numpy().reshape(1), 0.99)
+    os_d = oracle.tensor_scale(a, E4)
+    assert f32_bits(sd.cpu().numpy())[0] == f32_bits(os_d)
+    oqd = oracle.quant_tensor(xs, os_d, E4)
+    assert np.array_equal(qd[ridx].cpu().numpy(), oqd)
+    assert np.array_equal(qdt[:, ridx].cpu().numpy(), oqd.T)
+    say(f"{R} rows ({R // 128} row blocks): 1x128, 128x1, 128x128 and per-tensor codes exact")
