@@ -150,9 +150,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "dtype": "fp8_e4m3",
         "data": "synthetic (seeded, shapes and distributions of the workload)",
-        "config": desc,
+        "config": dict(desc, accumulate="fp32", inputs_and_outputs="bf16"),
         "step_gemm_flops": step_flops,
         "step_quant_bytes": step_bytes,
         "pct_fp8_peak_step": round(100 * value / FP8_PEAK_TFLOPS, 2),
