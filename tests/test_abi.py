@@ -8,6 +8,8 @@ argument validation, or with FP8BQ_ERR_DEVICE on a machine without a gfx950 GPU.
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 import torch
@@ -316,3 +318,17 @@ def test_planner_decisions_documented_for_the_decoder_block():
     # the plan is a pure function of its arguments
     assert all(fq.fp8bq_gemm_plan(fq.OP_WGRAD, 8192, 4096, 1024) == fq.fp8bq_gemm_plan(fq.OP_WGRAD, 8192, 4096, 1024)
                for _ in range(3))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None or HAVE_GPU, reason="needs gcc; checks the no-device paths")
+def test_c99_caller(tmp_path):
+    """The header alone is a C99 interface: a C program (tests/csrc/abi_from_c.c) built with gcc
+    -std=c99 -pedantic links against the library and gets the documented status codes, plans and
+    workspace sizes without any HIP header."""
+    src = os.path.join(ROOT, "tests", "csrc", "abi_from_c.c")
+    libdir = os.path.dirname(fq.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    src, "-L", libdir, "-lfp8bq", f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
