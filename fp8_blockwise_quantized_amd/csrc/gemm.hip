@@ -82,9 +82,12 @@ __device__ __forceinline__ PatchLane patch_lane(int lane) {
 // is output column 8*(rho/4) + 32*(j/2) + 4*(j%2) + rho%4 of the wave's 64 columns.  Lane l then
 // holds, for patches 2t and 2t+1, the 8 consecutive columns 32*t + 8*(l/16) .. +7 of its output row,
 // so the four lanes of a row write 64 contiguous bytes per store.  B tile rows get their own chunk
-// swizzle, which for these row sets is conflict-free and the same for all four patches (their rows
-// differ by 32*(j/2) + 4*(j%2)): swzb(row) = 2 * ((row / 8) % 4) + (row / 2) % 2.
-__device__ __forceinline__ int swzb(int row) { return (((row >> 3) & 3) << 1) | ((row >> 1) & 1); }
+// swizzle: lane l's row 8*(rho/4) + rho%4 (rho = l % 16) takes the swizzle A-side row rho has, so
+// every lane of a B-patch read hits exactly the bank of the same lane's A-patch read, and the two
+// reads conflict alike on any grouping of lanes into LDS phases (A's pattern is conflict-free).  It
+// ignores row bit 2 and bits 5 and up, so it is the same for all four patches (their rows differ by
+// 32*(j/2) + 4*(j%2)) and for every wave column.
+__device__ __forceinline__ int swzb(int row) { return swz(4 * ((row >> 3) & 3) + (row & 3)); }
 __device__ __forceinline__ PatchLane b_patch_lane(int lane) {
   const int rho = lane & 15, r = 8 * (rho >> 2) + (rho & 3), s = swzb(r), c0 = 2 * (lane >> 4);
   return PatchLane{r * 128 + ((c0 ^ s) << 4), r * 128 + (((c0 + 1) ^ s) << 4)};
