@@ -118,16 +118,31 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const TIn* __restrict_
 // the token axis (128 contiguous bytes per column).
 // ---------------------------------------------------------------------------------------------
 constexpr int kQtCols = 128;
-constexpr int kQtStride = 34;  // dwords per staged column (32 + 2 pad; even for 8-byte stores)
+
+// LDS layouts of the 128-column tile kernels, chosen so that no access conflicts on LDS banks
+// (64 banks of 4 bytes; a thread's 8 columns are 8*cc .. 8*cc+7, cc = t % 16, and the 4 row groups
+// of a wave share them):
+// - per-column arrays (partial maxima, scales) put column c at c + 4*(c/64): columns c and c+64,
+//   which one instruction's lanes cc and cc+8 touch together, fall on different banks;
+// - the transposed codes: column c's 128 codes (one byte per row) at byte 128*c + 128*(c/64), its
+//   8-byte unit u (rows 8u .. 8u+7) at unit u ^ 2*((c ^ c/8) % 8).  The XOR value is even, so the
+//   16-byte read of units 2h, 2h+1 stays one aligned access.
+constexpr int kColPos = kQtCols + 4;   // entries per padded per-column array
+constexpr int kRedStride = kColPos + 1;  // partial-maxima row stride (133: row groups 4 banks apart)
+constexpr int kQtBytes = kQtCols * 128 + 128;
+__device__ __forceinline__ int col_pos(int c) { return c + ((c >> 6) << 2); }
+__device__ __forceinline__ int qt_off(int c, int u) {
+  return (c << 7) + ((c >> 6) << 7) + ((u ^ (((c ^ (c >> 3)) & 7) << 1)) << 3);
+}
 
 template <typename TIn, int FMT>
 __global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict__ x, int64_t C, int64_t ldx,
                                                           uint8_t* __restrict__ qt, int64_t ldqt,
                                                           float* __restrict__ st, int64_t ldst, uint32_t ncg) {
-  __shared__ float red[16][kQtCols + 1];
-  __shared__ float ssc[kQtCols];
-  __shared__ float src[kQtCols];
-  __shared__ __attribute__((aligned(8))) uint32_t tileT[kQtCols * kQtStride];
+  __shared__ float red[16][kRedStride];
+  __shared__ __attribute__((aligned(16))) float ssc[kColPos];
+  __shared__ __attribute__((aligned(16))) float src[kColPos];
+  __shared__ __attribute__((aligned(16))) uint8_t tileT[kQtBytes];
 
   const int t = threadIdx.x;
   const int cc = t & 15;
@@ -154,28 +169,28 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict_
     float m = __builtin_fabsf(v[0][i]);
 #pragma unroll
     for (int p = 1; p < 8; ++p) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
-    red[rg][8 * cc + i] = m;
+    red[rg][col_pos(8 * cc + i)] = m;
   }
   __syncthreads();
   if (t < kQtCols) {
     float m = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) m = __builtin_fmaxf(m, red[k][t]);
+    for (int k = 0; k < 16; ++k) m = __builtin_fmaxf(m, red[k][col_pos(t)]);
     const float sc = group_scale<FMT>(m);
-    ssc[t] = sc;
-    src[t] = 1.0f / sc;
+    ssc[col_pos(t)] = sc;
+    src[col_pos(t)] = 1.0f / sc;
     if (c0 + t < C) st[rb * ldst + c0 + t] = sc;
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = 8 * cc + i;
-    const float sc = ssc[c], rc = src[c];
+    const float sc = ssc[col_pos(c)], rc = src[col_pos(c)];
     float y[8];
 #pragma unroll
     for (int p = 0; p < 8; ++p) y[p] = clamp_fmt<FMT>(div_by_scale(v[p][i], sc, rc));
     const uint2 w = make_uint2(pack4<FMT>(y[0], y[1], y[2], y[3]), pack4<FMT>(y[4], y[5], y[6], y[7]));
-    *reinterpret_cast<uint2*>(tileT + c * kQtStride + 2 * rg) = w;
+    *reinterpret_cast<uint2*>(tileT + qt_off(c, rg)) = w;
   }
   __syncthreads();
 #pragma unroll
@@ -183,8 +198,8 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict_
     const int c = (t >> 3) + 32 * pass;
     const int ch = t & 7;
     if (c0 + c < C) {
-      const uint32_t* src4 = tileT + c * kQtStride + 4 * ch;
-      store_codes16(qt + (c0 + c) * ldqt + rb * kGroup + 16 * ch, make_uint4(src4[0], src4[1], src4[2], src4[3]));
+      const uint4 codes = *reinterpret_cast<const uint4*>(tileT + qt_off(c, 2 * ch));
+      store_codes16(qt + (c0 + c) * ldqt + rb * kGroup + 16 * ch, codes);
     }
   }
 }
@@ -192,9 +207,9 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict_
 // ---------------------------------------------------------------------------------------------
 // Both activation layouts from one read: grid (C/128, R/128), the 128x1 kernel's 128x128 tiles and
 // thread mapping.  The 16 threads that share a row patch are one DPP row, so each of a thread's 8
-// rows also gets its 1x128 group amax by DPP, and its 8 codes of that row go out as one 8-byte
-// store (16 threads write the row's 128 contiguous bytes).  Codes and scales are those of the two
-// separate kernels, bit for bit (same scale, division and conversion code).
+// rows also gets its 1x128 group amax by DPP, and its 8 codes of that row go out as one 8-byte store
+// (16 threads write the row's 128 contiguous bytes).  Codes and scales are those of the two separate
+// kernels, bit for bit (same scale, division and conversion code).
 // ---------------------------------------------------------------------------------------------
 template <typename TIn, int FR, int FC>
 __global__ __launch_bounds__(256) void quant_dual_kernel(const TIn* __restrict__ x, int64_t ldx,
@@ -202,10 +217,10 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const TIn* __restrict__
                                                          float* __restrict__ s, int64_t lds,
                                                          uint8_t* __restrict__ qt, int64_t ldqt,
                                                          float* __restrict__ st, int64_t ldst, uint32_t ncg) {
-  __shared__ float red[16][kQtCols + 1];
-  __shared__ float ssc[kQtCols];
-  __shared__ float src[kQtCols];
-  __shared__ __attribute__((aligned(8))) uint32_t tileT[kQtCols * kQtStride];
+  __shared__ float red[16][kRedStride];
+  __shared__ __attribute__((aligned(16))) float ssc[kColPos];
+  __shared__ __attribute__((aligned(16))) float src[kColPos];
+  __shared__ __attribute__((aligned(16))) uint8_t tileT[kQtBytes];
 
   const int t = threadIdx.x;
   const int cc = t & 15;
@@ -243,36 +258,36 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const TIn* __restrict__
     float m = __builtin_fabsf(v[0][i]);
 #pragma unroll
     for (int p = 1; p < 8; ++p) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
-    red[rg][8 * cc + i] = m;
+    red[rg][col_pos(8 * cc + i)] = m;
   }
   __syncthreads();
   if (t < kQtCols) {
     float m = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) m = __builtin_fmaxf(m, red[k][t]);
+    for (int k = 0; k < 16; ++k) m = __builtin_fmaxf(m, red[k][col_pos(t)]);
     const float sc = group_scale<FC>(m);
-    ssc[t] = sc;
-    src[t] = 1.0f / sc;
+    ssc[col_pos(t)] = sc;
+    src[col_pos(t)] = 1.0f / sc;
     st[rb * ldst + c0 + t] = sc;
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = 8 * cc + i;
-    const float sc = ssc[c], rc = src[c];
+    const float sc = ssc[col_pos(c)], rc = src[col_pos(c)];
     float y[8];
 #pragma unroll
     for (int p = 0; p < 8; ++p) y[p] = clamp_fmt<FC>(div_by_scale(v[p][i], sc, rc));
     const uint2 w = make_uint2(pack4<FC>(y[0], y[1], y[2], y[3]), pack4<FC>(y[4], y[5], y[6], y[7]));
-    *reinterpret_cast<uint2*>(tileT + c * kQtStride + 2 * rg) = w;
+    *reinterpret_cast<uint2*>(tileT + qt_off(c, rg)) = w;
   }
   __syncthreads();
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int c = (t >> 3) + 32 * pass;
     const int ch = t & 7;
-    const uint32_t* src4 = tileT + c * kQtStride + 4 * ch;
-    store_codes16(qt + (c0 + c) * ldqt + rb * kGroup + 16 * ch, make_uint4(src4[0], src4[1], src4[2], src4[3]));
+    const uint4 codes = *reinterpret_cast<const uint4*>(tileT + qt_off(c, 2 * ch));
+    store_codes16(qt + (c0 + c) * ldqt + rb * kGroup + 16 * ch, codes);
   }
 }
 
@@ -359,7 +374,7 @@ __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __re
                                                                  uint8_t* __restrict__ qt, int64_t ldqt,
                                                                  TensorScaleArgs ta, uint32_t nkb) {
   __shared__ float wmax[4];
-  __shared__ __attribute__((aligned(8))) uint32_t tileT[kQtCols * kQtStride];
+  __shared__ __attribute__((aligned(16))) uint8_t tileT[kQtBytes];
   const int t = threadIdx.x;
   const int cc = t & 15;
   const int rg = t >> 4;
@@ -411,7 +426,7 @@ __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __re
       lo |= (uint32_t)cb[p][i] << (8 * p);
       hi |= (uint32_t)cb[4 + p][i] << (8 * p);
     }
-    *reinterpret_cast<uint2*>(tileT + (8 * cc + i) * kQtStride + 2 * rg) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(tileT + qt_off(8 * cc + i, rg)) = make_uint2(lo, hi);
   }
   if (!TENSOR && t == 0) s[nb * lds + kb] = sc;
   __syncthreads();
@@ -419,8 +434,8 @@ __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __re
   for (int pass = 0; pass < 4; ++pass) {
     const int c = (t >> 3) + 32 * pass;
     const int ch = t & 7;
-    const uint32_t* src4 = tileT + c * kQtStride + 4 * ch;
-    store_codes16(qt + (kb * kGroup + c) * ldqt + nb * kGroup + 16 * ch, make_uint4(src4[0], src4[1], src4[2], src4[3]));
+    const uint4 codes = *reinterpret_cast<const uint4*>(tileT + qt_off(c, 2 * ch));
+    store_codes16(qt + (kb * kGroup + c) * ldqt + nb * kGroup + 16 * ch, codes);
   }
 }
 
