@@ -130,14 +130,11 @@ def main():
     for k in range(args.steps):
         step(ev[k])
     torch.cuda.synchronize()
-    dur = np.zeros(len(ops))
-    for k in range(args.steps):
-        for i in range(len(ops)):
-            dur[i] += ev[k][i][0].elapsed_time(ev[k][i][1])
-    dur_ms = dur / args.steps  # mean per launch
+    per = np.array([[ev[k][i][0].elapsed_time(ev[k][i][1]) for i in range(len(ops))] for k in range(args.steps)])
+    dur_ms = per.mean(axis=0)  # mean per launch
 
     value = step_flops / (ms_per_step * 1e-3) / 1e12
-    breakdown = summarize(ops, dur_ms)
+    breakdown = summarize(ops, dur_ms, np.median(per, axis=0), per.min(axis=0))
     roof = roofline(fq, ops, dur_ms, with_traffic=args.workload == "decoder")
     out = {
         "metric": METRIC,
@@ -450,7 +447,9 @@ def run_sweep(args, torch, fq, synth, dev):
 # reporting
 # -----------------------------------------------------------------------------------------------
 
-def summarize(ops, dur_ms):
+def summarize(ops, dur_ms, med_ms=None, min_ms=None):
+    """Per kind (quantize / fprop / dgrad / wgrad) sums of the mean launch durations, and per launch
+    the mean (`ms`, which all rates use), with the median and minimum over the steps beside it."""
     kinds = {}
     for o, d in zip(ops, dur_ms):
         k = kinds.setdefault(o["kind"], {"ms": 0.0, "flops": 0, "bytes": 0, "launches": 0})
@@ -468,10 +467,14 @@ def summarize(ops, dur_ms):
             gbs = k["bytes"] / (k["ms"] * 1e-3) / 1e9
             r.update(gbs=round(gbs, 1), pct_hbm_peak=round(100 * gbs / HBM_PEAK_GBS, 1))
         out[name] = r
-    out["per_launch"] = [{"op": o["name"], "ms": round(float(d), 5),
-                          **({"tflops": round(o["flops"] / (d * 1e-3) / 1e12, 1)} if o["flops"] else
-                             {"gbs": round(o["bytes"] / (d * 1e-3) / 1e9, 1)})}
-                         for o, d in zip(ops, dur_ms)]
+    out["per_launch"] = []
+    for i, (o, d) in enumerate(zip(ops, dur_ms)):
+        r = {"op": o["name"], "ms": round(float(d), 5)}
+        if med_ms is not None:
+            r.update(ms_median=round(float(med_ms[i]), 5), ms_min=round(float(min_ms[i]), 5))
+        r.update({"tflops": round(o["flops"] / (d * 1e-3) / 1e12, 1)} if o["flops"] else
+                 {"gbs": round(o["bytes"] / (d * 1e-3) / 1e9, 1)})
+        out["per_launch"].append(r)
     return out
 
 
@@ -508,7 +511,8 @@ def _traffic(kernel):
 
 
 def roofline(fq, ops, dur_ms, with_traffic=True):
-    """The dominant GEMM kernel among those whose every launch in the step is that kernel alone:
+    """The dominant GEMM kernel among those whose every launch in the step is that kernel alone, by
+    FLOPs per step (the first in step order on a tie, so the choice does not depend on timing noise):
     achieved = its algorithmic FLOPs per launch / its mean launch duration (HIP events on the launch
     stream, one pair per call), over all of its launches in the step."""
     groups = {}
@@ -519,10 +523,12 @@ def roofline(fq, ops, dur_ms, with_traffic=True):
         g = groups.setdefault(name, {"ok": True, "sel": []})
         g["ok"] &= isolated
         g["sel"].append((o, float(d)))
-    eligible = [(sum(d for _, d in g["sel"]), name, g["sel"]) for name, g in groups.items() if g["ok"]]
+    eligible = [(sum(o["flops"] for o, _ in g["sel"]), -i, name, g["sel"])
+                for i, (name, g) in enumerate(groups.items()) if g["ok"]]
     if not eligible:
         return None
-    t, name, sel = max(eligible)
+    _, _, name, sel = max(eligible, key=lambda e: (e[0], e[1]))
+    t = sum(d for _, d in sel)
     flops_per_launch = sum(o["flops"] for o, _ in sel) / len(sel)
     ms_per_launch = t / len(sel)
     achieved = flops_per_launch / (ms_per_launch * 1e-3) / 1e12
