@@ -193,9 +193,11 @@ def _qdual_bytes(R, C, in_bytes=2):
     return R * C * in_bytes + 2 * R * C + R * (C // 128) * 4 + (R // 128) * C * 4
 
 
-def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True):
+def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True, weight_jobs=None):
     """Closures for one linear's hot path; every output buffer is preallocated.  With the backward
-    pass, X and dY are each quantized both ways (1x128 and 128x1) in one pass."""
+    pass, X and dY are each quantized both ways (1x128 and 128x1) in one pass.  With weight_jobs (a
+    list), W's quantization (codes, scales, W^T codes) is appended there as a job of one batched launch
+    for all weights instead of being an op of this linear."""
     M, K = X.shape
     N = W.shape[0]
     E4 = fq.E4M3
@@ -218,9 +220,10 @@ def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True):
                        fn=lambda: fq.fp8bq_quantize_act_1x128(X, E4, qx, sx))
         quant_w = dict(name=f"{name}.quant_w_128x128", kind="quant_128x128", bytes=_qw_bytes(N, K), flops=0,
                        fn=lambda: fq.fp8bq_quantize_weight_128x128(W, E4, qw, sw))
-    ops = [
-        quant_x,
-        quant_w,
+    if weight_jobs is not None and with_backward:
+        weight_jobs.append((W, qw, sw, qwt))
+        quant_w = None
+    ops = [op for op in (quant_x, quant_w) if op is not None] + [
         dict(name=f"{name}.fprop", kind="fprop", bytes=0, flops=2 * M * N * K, plan=(fq.OP_FPROP, M, N, K), kid=(0, 0),
              fn=lambda: fq.fp8bq_gemm_fprop(qx, sx, E4, qw, sw, E4, y, ws_f)),
     ]
@@ -245,22 +248,27 @@ def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True):
 
 def build_decoder(torch, fq, synth, dev):
     log("generating the decoder-block inputs ...")
-    ops, bufs = [], []
+    ops, bufs, wjobs = [], [], []
     for name, K, N in synth.DECODER_LINEARS:
         c = synth.decoder_linear(name)
         X, W, dY = c["X"].to(dev), c["W"].to(dev), c["dY"].to(dev)
-        o, b = linear_ops(torch, fq, name, X, W, dY, dev)
+        o, b = linear_ops(torch, fq, name, X, W, dY, dev, weight_jobs=wjobs)
         ops += o
         bufs += b + [X, W, dY]
+    # all four weights are known when the step starts: one launch quantizes them (codes, scales, W^T codes)
+    wbytes = sum(_qw_bytes(*w.shape) + w.numel() for w, _, _, _ in wjobs)
+    ops.insert(0, dict(name="weights.quant_w_dual", kind="quant_w_dual", bytes=wbytes, flops=0,
+                       fn=lambda: fq.fp8bq_quantize_weights_dual(wjobs, fq.E4M3)))
     desc = {
         "workload": "decoder block fprop+dgrad+wgrad, M=16384 tokens, hidden 2048, GQA 16q/2kv x128 "
                     "(QKV 2048->2560, O 2048->2048), SwiGLU gate+up 2048->11264, down 5632->2048; "
                     "E4M3 act 1x128 / weight 128x128 / wgrad 128x1 (X and dY quantized both ways in one pass "
-                    "each); BF16 in/out",
+                    "each, the four weights with their W^T codes in one launch); BF16 in/out",
         "tokens": synth.DECODER_M,
         "linears": [[n, k, nn] for n, k, nn in synth.DECODER_LINEARS],
         "gemms_per_step": 12,
         "quant_passes_per_step": 12,
+        "quant_launches_per_step": 9,
     }
     return ops, bufs, desc
 

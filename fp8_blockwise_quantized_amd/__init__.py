@@ -12,6 +12,7 @@ Raw entry points (same names and argument order as the C ABI, tensors in place o
     fp8bq_quantize_act_dual(x, fmt_rows, q, s, fmt_cols, qt, st)
     fp8bq_quantize_weight_128x128(w, fmt, q, s)
     fp8bq_quantize_weight_dual(w, fmt, q, s, qt)
+    fp8bq_quantize_weights_dual(jobs, fmt)    jobs: up to 16 (w, q, s, qt) tuples, one launch
     fp8bq_gemm_fprop(qx, sx, fx, qw, sw, fw, y, ws=None)
     fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws=None)
     fp8bq_gemm_dgrad_wt(qdy, sdy, fdy, qwt, sw, fw, dx, ws=None)
@@ -26,6 +27,8 @@ Allocating helpers (outputs created with torch on the input's device):
     quantize_act_dual(x, fmt_rows, fmt_cols) -> (q, s, qt, st) of the two above, one pass over x
     quantize_weight_128x128(w, fmt) -> (q [N, K] uint8, s [N/128, K/128] float32)
     quantize_weight_dual(w, fmt) -> (q, s, qt [K, N]): the above plus the transposed codes
+    quantize_weights_dual(ws, fmt) -> [(q, s, qt), ...]: quantize_weight_dual of every weight in ws,
+        in one launch per 16 weights
     gemm_fprop(qx, sx, qw, sw, fx=E4M3, fw=E4M3, out_dtype=bf16) -> y [M, N]
     gemm_dgrad(qdy, sdy, qw, sw, fdy=E4M3, fw=E4M3, out_dtype=bf16) -> dx [M, K]
     gemm_dgrad_wt(qdy, sdy, qwt, sw, fdy=E4M3, fw=E4M3, out_dtype=bf16) -> dx [M, K] (qwt = W^T codes)
@@ -63,6 +66,16 @@ _c_int = ctypes.c_int
 _c_vp = ctypes.c_void_p
 _c_sz = ctypes.c_size_t
 
+
+class WeightJob(ctypes.Structure):
+    """fp8bq_weight_job of the C ABI: one weight of fp8bq_quantize_weights_dual."""
+    _fields_ = [("w", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("ldw", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("ldq", ctypes.c_int64), ("s", ctypes.c_void_p), ("lds", ctypes.c_int64),
+                ("qt", ctypes.c_void_p), ("ldqt", ctypes.c_int64)]
+
+
+MAX_WEIGHT_JOBS = 16
+
 _SIGS = {
     "fp8bq_quantize_act_1x128": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
     "fp8bq_quantize_act_128x1": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
@@ -70,6 +83,7 @@ _SIGS = {
                                 _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
     "fp8bq_quantize_weight_dual": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp,
                                    _c_i64, _c_vp],
+    "fp8bq_quantize_weights_dual": [ctypes.POINTER(WeightJob), _c_int, _c_int, _c_int, _c_vp],
     "fp8bq_quantize_weight_128x128": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
                                       _c_vp],
     "fp8bq_gemm_fprop": [_c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64,
@@ -136,6 +150,8 @@ def _stream(t):
 
 
 def _ld(t):
+    if t.dim() == 2 and t.numel() == 0:
+        return t.size(1)  # an empty matrix has no meaningful strides; the call does nothing with it
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError("expected a 2-D tensor with unit column stride")
     return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
@@ -188,6 +204,24 @@ def fp8bq_quantize_weight_dual(w, fmt, q, s, qt):
     N, K = w.shape
     _check(lib().fp8bq_quantize_weight_dual(_ptr(w), _in_type(w), N, K, _ld(w), fmt, _ptr(q), _ld(q), _ptr(s), _ld(s),
                                             _ptr(qt), _ld(qt), _stream(w)), "fp8bq_quantize_weight_dual")
+
+
+def fp8bq_quantize_weights_dual(jobs, fmt):
+    """jobs: (w, q, s, qt) per weight, as fp8bq_quantize_weight_dual takes them; every w of one dtype.
+    One launch on the current stream of the first weight's device."""
+    jobs = list(jobs)
+    arr = (WeightJob * max(len(jobs), 1))()
+    wt = IN_BF16
+    for i, (w, q, s, qt) in enumerate(jobs):
+        if i == 0:
+            wt = _in_type(w)
+        elif _in_type(w) != wt:
+            raise TypeError("all weights of one fp8bq_quantize_weights_dual call must share one dtype")
+        N, K = w.shape
+        arr[i] = WeightJob(w.data_ptr(), N, K, _ld(w), q.data_ptr(), _ld(q), s.data_ptr(), _ld(s), qt.data_ptr(),
+                           _ld(qt))
+    stream = _stream(jobs[0][0]) if jobs else ctypes.c_void_p(0)
+    _check(lib().fp8bq_quantize_weights_dual(arr, len(jobs), wt, fmt, stream), "fp8bq_quantize_weights_dual")
 
 
 def fp8bq_quantize_weight_128x128(w, fmt, q, s):
@@ -327,6 +361,21 @@ def quantize_weight_dual(w, fmt=E4M3):
     qt = torch.empty((K, N), dtype=torch.uint8, device=w.device)
     fp8bq_quantize_weight_dual(w, fmt, q, s, qt)
     return q, s, qt
+
+
+def quantize_weights_dual(ws, fmt=E4M3):
+    """quantize_weight_dual of every weight in ws (all of one dtype), one launch per MAX_WEIGHT_JOBS weights."""
+    outs = []
+    for w in ws:
+        N, K = w.shape
+        outs.append((torch.empty((N, K), dtype=torch.uint8, device=w.device),
+                     torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device),
+                     torch.empty((K, N), dtype=torch.uint8, device=w.device)))
+    ws = list(ws)
+    for i in range(0, len(ws), MAX_WEIGHT_JOBS):
+        fp8bq_quantize_weights_dual([(w,) + o for w, o in zip(ws[i:i + MAX_WEIGHT_JOBS], outs[i:i + MAX_WEIGHT_JOBS])],
+                                    fmt)
+    return outs
 
 
 def quantize_weight_128x128(w, fmt=E4M3):

@@ -179,6 +179,38 @@ int fp8bq_quantize_weight_dual(const void* w, fp8bq_in wt, int64_t N, int64_t K,
       launch_quant_128x128_dual(w, (int)wt, N, K, ldw, (int)fmt, q, ldq, s, lds, qt, ldqt, (hipStream_t)stream));
 }
 
+int fp8bq_quantize_weights_dual(const fp8bq_weight_job* jobs, int count, fp8bq_in wt, fp8bq_fp8 fmt,
+                                void* stream) {
+  static_assert(FP8BQ_MAX_WEIGHT_JOBS == kMaxWeightJobs, "job limit of the header and the launcher");
+  WeightJobArgs args[kMaxWeightJobs];
+  bool empty[kMaxWeightJobs];
+  const int n = (count >= 0 && count <= kMaxWeightJobs && jobs) ? count : 0;
+  for (int j = 0; j < n; ++j) {
+    const fp8bq_weight_job& a = jobs[j];
+    args[j] = WeightJobArgs{a.w, a.N, a.K, a.ldw, a.q, a.ldq, a.s, a.lds, a.qt, a.ldqt};
+  }
+  int st = validate_quant_weights_dual(n == count ? args : nullptr, count, kMaxWeightJobs, (int)wt, (int)fmt, empty);
+  if (st != kOk) return st;
+  // one block per 128x128 tile, jobs in order; the grid must stay within 2^31 - 1 blocks
+  WeightDualBatch b{};
+  uint64_t tiles = 0;
+  for (int j = 0; j < count; ++j) {
+    if (empty[j]) continue;
+    const fp8bq_weight_job& a = jobs[j];
+    const int i = b.count++;
+    b.w[i] = a.w; b.q[i] = a.q; b.s[i] = a.s; b.qt[i] = a.qt;
+    b.ldw[i] = a.ldw; b.ldq[i] = a.ldq; b.lds[i] = a.lds; b.ldqt[i] = a.ldqt;
+    b.nkb[i] = (uint32_t)(a.K / 128);
+    b.start[i] = (uint32_t)tiles;
+    tiles += (uint64_t)(a.N / 128) * (uint64_t)(a.K / 128);
+    if (tiles > 0x7fffffffull) return kErrShape;
+  }
+  b.start[b.count] = (uint32_t)tiles;
+  if (b.count == 0) return kOk;
+  if ((st = current_device(nullptr)) != kOk) return st;
+  return launched(launch_quant_weights_dual(b, (int)wt, (int)fmt, (hipStream_t)stream));
+}
+
 int fp8bq_quantize_weight_128x128(const void* w, fp8bq_in wt, int64_t N, int64_t K, int64_t ldw, fp8bq_fp8 fmt,
                                   uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
   bool empty = false;

@@ -24,6 +24,23 @@ hipError_t launch_quant_128x128_dual(const void* w, int wt, int64_t N, int64_t K
 hipError_t launch_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
                                 int64_t ldq, float* s, int64_t lds, hipStream_t st);
 
+// Several weights quantized as launch_quant_128x128_dual in one launch (all of one input type and
+// format).  Job j covers blocks start[j] .. start[j+1]-1 (nkb[j] = K_j / 128 tiles per tile row);
+// only jobs with at least one tile are listed, so start is strictly increasing and start[count] is
+// the grid size.  Passed to the kernel by value (about 1.2 KB of kernel arguments).
+constexpr int kMaxWeightJobs = 16;
+struct WeightDualBatch {
+  const void* w[kMaxWeightJobs];
+  uint8_t* q[kMaxWeightJobs];
+  float* s[kMaxWeightJobs];
+  uint8_t* qt[kMaxWeightJobs];
+  int64_t ldw[kMaxWeightJobs], ldq[kMaxWeightJobs], lds[kMaxWeightJobs], ldqt[kMaxWeightJobs];
+  uint32_t nkb[kMaxWeightJobs];
+  uint32_t start[kMaxWeightJobs + 1];
+  int count;
+};
+hipError_t launch_quant_weights_dual(const WeightDualBatch& b, int wt, int fmt, hipStream_t st);
+
 // Per-tensor delayed scaling: the running amax *amax is updated with max|x| (beta = EMA decay) and
 // gives the scale *s; q[R, C] gets the codes of x's BF16 copy, and qt[C, R] the same codes
 // transposed when qt is non-null (then R % 128 == 0).  ws holds kTensorAmaxBlocks partial maxima

@@ -367,19 +367,16 @@ __device__ __forceinline__ float tensor_scale(const TensorScaleArgs& a) {
 // TENSOR: the per-tensor scale comes from tensor_scale (the delayed-scaling rule below; s and lds
 // are unused) and the codes are those of the input's BF16 copy.
 // ---------------------------------------------------------------------------------------------
-template <typename TIn, int FMT, bool TENSOR = false>
-__global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __restrict__ w, int64_t ldw,
-                                                                 uint8_t* __restrict__ q, int64_t ldq,
-                                                                 float* __restrict__ s, int64_t lds,
-                                                                 uint8_t* __restrict__ qt, int64_t ldqt,
-                                                                 TensorScaleArgs ta, uint32_t nkb) {
+template <typename TIn, int FMT, bool TENSOR>
+__device__ __forceinline__ void weight_dual_tile(const TIn* __restrict__ w, int64_t ldw, uint8_t* __restrict__ q,
+                                                 int64_t ldq, float* __restrict__ s, int64_t lds,
+                                                 uint8_t* __restrict__ qt, int64_t ldqt, const TensorScaleArgs& ta,
+                                                 int64_t nb, int64_t kb) {
   __shared__ float wmax[4];
   __shared__ __attribute__((aligned(16))) uint8_t tileT[kQtBytes];
   const int t = threadIdx.x;
   const int cc = t & 15;
   const int rg = t >> 4;
-  const TileRC tile = tile_of_block(nkb);
-  const int64_t kb = tile.col, nb = tile.row;
   const int64_t col = kb * kGroup + 8 * cc;
 
   float v[8][8];
@@ -437,6 +434,32 @@ __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __re
     const uint4 codes = *reinterpret_cast<const uint4*>(tileT + qt_off(c, 2 * ch));
     store_codes16(qt + (kb * kGroup + c) * ldqt + nb * kGroup + 16 * ch, codes);
   }
+}
+
+template <typename TIn, int FMT, bool TENSOR = false>
+__global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __restrict__ w, int64_t ldw,
+                                                                 uint8_t* __restrict__ q, int64_t ldq,
+                                                                 float* __restrict__ s, int64_t lds,
+                                                                 uint8_t* __restrict__ qt, int64_t ldqt,
+                                                                 TensorScaleArgs ta, uint32_t nkb) {
+  const TileRC tile = tile_of_block(nkb);
+  weight_dual_tile<TIn, FMT, TENSOR>(w, ldw, q, ldq, s, lds, qt, ldqt, ta, tile.row, tile.col);
+}
+
+// Several weights in one launch: the tiles of job j are blocks start[j] .. start[j+1]-1, each job's
+// tiles in the single-weight kernel's order, so every job gets exactly that kernel's codes and scales.
+// Jobs with no tiles have start[j] == start[j+1] and are never selected.
+template <typename TIn, int FMT>
+__global__ __launch_bounds__(256) void quant_weights_dual_kernel(WeightDualBatch b) {
+  const uint32_t blk = blockIdx.x;
+  int j = 0;
+  while (j + 1 < b.count && blk >= b.start[j + 1]) ++j;
+  const uint32_t local = blk - b.start[j];
+  const uint32_t nkb = b.nkb[j];
+  const uint32_t r = __builtin_amdgcn_readfirstlane(local / nkb);
+  weight_dual_tile<TIn, FMT, false>(reinterpret_cast<const TIn*>(b.w[j]), b.ldw[j], b.q[j], b.ldq[j], b.s[j],
+                                    b.lds[j], b.qt[j], b.ldqt[j], TensorScaleArgs{}, (int64_t)r,
+                                    (int64_t)(local - r * nkb));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -602,6 +625,18 @@ hipError_t launch_quant_128x128_dual(const void* w, int wt, int64_t N, int64_t K
                         : launch_128x128_dual_t<uint16_t, kE5M2>(w, N, K, ldw, q, ldq, s, lds, qt, ldqt, st);
   return fmt == kE4M3 ? launch_128x128_dual_t<float, kE4M3>(w, N, K, ldw, q, ldq, s, lds, qt, ldqt, st)
                       : launch_128x128_dual_t<float, kE5M2>(w, N, K, ldw, q, ldq, s, lds, qt, ldqt, st);
+}
+
+template <typename TIn, int FMT>
+static hipError_t launch_weights_dual_t(const WeightDualBatch& b, hipStream_t st) {
+  hipLaunchKernelGGL((quant_weights_dual_kernel<TIn, FMT>), dim3(b.start[b.count]), dim3(256), 0, st, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weights_dual(const WeightDualBatch& b, int wt, int fmt, hipStream_t st) {
+  if (wt == 0)
+    return fmt == kE4M3 ? launch_weights_dual_t<uint16_t, kE4M3>(b, st) : launch_weights_dual_t<uint16_t, kE5M2>(b, st);
+  return fmt == kE4M3 ? launch_weights_dual_t<float, kE4M3>(b, st) : launch_weights_dual_t<float, kE5M2>(b, st);
 }
 
 int tensor_amax_blocks(int64_t R) {

@@ -120,6 +120,36 @@ int validate_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t 
                      false);
 }
 
+int validate_quant_weights_dual(const WeightJobArgs* jobs, int count, int max_jobs, int wt, int fmt, bool* empty) {
+  if (count < 0 || count > max_jobs) return kErrValue;
+  if (count > 0 && jobs == nullptr) return kErrNull;
+  int r;
+  for (int j = 0; j < count; ++j) {
+    const WeightJobArgs& a = jobs[j];
+    if ((r = validate_quant_128x128_dual(a.w, wt, a.N, a.K, a.ldw, fmt, a.q, a.ldq, a.s, a.lds, a.qt, a.ldqt,
+                                         &empty[j])) != kOk)
+      return r;
+  }
+  const int es = in_esize(wt);
+  for (int i = 0; i < count; ++i) {
+    if (empty[i]) continue;
+    const WeightJobArgs& a = jobs[i];
+    const Mat outs[3] = {{a.q, a.N, a.K, a.ldq, 1}, {a.s, a.N / 128, a.K / 128, a.lds, 4}, {a.qt, a.K, a.N, a.ldqt, 1}};
+    for (int j = 0; j < count; ++j) {
+      if (j == i || empty[j]) continue;
+      const WeightJobArgs& b = jobs[j];
+      const Mat theirs[4] = {{b.w, b.N, b.K, b.ldw, es},
+                             {b.q, b.N, b.K, b.ldq, 1},
+                             {b.s, b.N / 128, b.K / 128, b.lds, 4},
+                             {b.qt, b.K, b.N, b.ldqt, 1}};
+      for (const Mat& o : outs)
+        for (const Mat& t : theirs)
+          if (overlaps(o, t)) return kErrOverlap;
+    }
+  }
+  return kOk;
+}
+
 static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 int validate_quant_tensor(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, const void* amax,

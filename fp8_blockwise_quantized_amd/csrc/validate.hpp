@@ -47,6 +47,16 @@ int validate_quant_128x128_dual(const void* w, int wt, int64_t N, int64_t K, int
                                 int64_t ldq, const void* s, int64_t lds, const void* qt, int64_t ldqt, bool* empty);
 int validate_quant_128x128(const void* w, int wt, int64_t N, int64_t K, int64_t ldw, int fmt, const void* q,
                            int64_t ldq, const void* s, int64_t lds, bool* empty);
+// Several weights: count in [0, max_jobs]; each job as validate_quant_128x128_dual (empty[j] set per
+// job); no job's outputs may overlap another job's input or outputs.  Job fields are passed as
+// parallel arrays so this stays free of the public header's types.
+struct WeightJobArgs {
+  const void* w; int64_t N, K, ldw;
+  const void* q; int64_t ldq;
+  const void* s; int64_t lds;
+  const void* qt; int64_t ldqt;
+};
+int validate_quant_weights_dual(const WeightJobArgs* jobs, int count, int max_jobs, int wt, int fmt, bool* empty);
 
 // Per-tensor delayed scaling: x [R, C] (C % 128 == 0), running amax and scale one float each (4-byte
 // aligned), q [R, C], optional qt [C, R] (then R % 128 == 0), beta in [0, 1], ws >= ws_needed bytes.

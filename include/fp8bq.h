@@ -135,6 +135,36 @@ int fp8bq_quantize_weight_dual(const void* w, fp8bq_in wt, int64_t N, int64_t K,
                                uint8_t* q, int64_t ldq, float* s, int64_t lds, uint8_t* qt, int64_t ldqt,
                                void* stream);
 
+/* One weight of fp8bq_quantize_weights_dual: the arguments fp8bq_quantize_weight_dual takes for it. */
+typedef struct {
+  const void* w;   /* [N, K], row stride ldw */
+  int64_t N, K, ldw;
+  uint8_t* q;      /* [N, K] codes, row stride ldq */
+  int64_t ldq;
+  float* s;        /* [N/128][K/128] scales, row stride lds */
+  int64_t lds;
+  uint8_t* qt;     /* [K, N] transposed codes, row stride ldqt */
+  int64_t ldqt;
+} fp8bq_weight_job;
+
+#define FP8BQ_MAX_WEIGHT_JOBS 16
+
+/*
+ * Several weights quantized in one launch.  For each of the count jobs (jobs is a HOST array, read
+ * only during the call; 0 <= count <= FP8BQ_MAX_WEIGHT_JOBS, else FP8BQ_ERR_VALUE) the outputs are
+ * exactly those of fp8bq_quantize_weight_dual(job.w, wt, job.N, job.K, job.ldw, fmt, job.q, job.ldq,
+ * job.s, job.lds, job.qt, job.ldqt), bit for bit.  All weights share the input type wt and the format
+ * fmt.  Every job must pass that call's checks (a job with N or K equal to 0 is skipped); besides, no
+ * job's outputs may overlap another job's input or outputs (FP8BQ_ERR_OVERLAP), while inputs may be
+ * shared.  The jobs' 128x128 tiles together must number under 2^31 (FP8BQ_ERR_SHAPE).  On error the
+ * first failing check's status is returned and nothing is enqueued.
+ * In a training step every weight is known at its start; one launch for all of them keeps the GPU
+ * busy where one weight alone is too small to fill it.  Defining passages: as
+ * fp8bq_quantize_weight_128x128.
+ */
+int fp8bq_quantize_weights_dual(const fp8bq_weight_job* jobs, int count, fp8bq_in wt, fp8bq_fp8 fmt,
+                                void* stream);
+
 /*
  * Both activation layouts from one read of x: the outputs of
  *   fp8bq_quantize_act_1x128(x, xt, R, C, ldx, fmt_rows, q, ldq, s, lds) and

@@ -36,7 +36,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fq.lib()
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -223,6 +223,45 @@ def test_quant_weight_dual_validation():
     assert qwdual(ldqt=200) == LD  # ldqt >= N
     assert qwdual(ldqt=264) == LD  # 16-byte rows
     assert qwdual(qt=P(1)) == OVERLAP and qwdual(qt=P(0)) == OVERLAP
+
+
+def wjob(base, N=256, K=256, ldw=256, ldq=256, lds=2, ldqt=256, w=None, q=None, s=None, qt=None):
+    """A fake weight job whose four buffers sit at P(base) .. P(base + 3) unless given."""
+    pick = lambda v, i: (v if v is not None else P(base + i)).value or 0
+    return fq.WeightJob(pick(w, 0), N, K, ldw, pick(q, 1), ldq, pick(s, 2), lds, pick(qt, 3), ldqt)
+
+
+def qwbatch(jobs, wt=0, fmt=0, count=None):
+    arr = (fq.WeightJob * max(len(jobs), 1))(*jobs)
+    return fq.lib().fp8bq_quantize_weights_dual(arr, len(jobs) if count is None else count, wt, fmt, S0)
+
+
+def test_quant_weights_batch_validation():
+    lib = fq.lib()
+    assert lib.fp8bq_quantize_weights_dual(None, 0, 0, 0, S0) == OK  # nothing to do
+    assert lib.fp8bq_quantize_weights_dual(None, 2, 0, 0, S0) == NULL
+    assert qwbatch([wjob(0)], count=-1) == VALUE and qwbatch([wjob(0)], count=17) == VALUE
+    assert qwbatch([wjob(0, N=0), wjob(4, K=0)]) == OK  # only empty jobs: nothing enqueued
+    valid(lambda: qwbatch([wjob(0), wjob(4, N=384, K=128, ldw=128, ldq=128, lds=4, ldqt=384)]))
+    valid(lambda: qwbatch([wjob(4 * i) for i in range(16)]))
+    # each job gets the single-weight checks, in job order
+    assert qwbatch([wjob(0)], wt=3) == DTYPE and qwbatch([wjob(0)], fmt=5) == FORMAT
+    assert qwbatch([wjob(0), wjob(4, N=200)]) == SHAPE
+    assert qwbatch([wjob(0), wjob(4, qt=NUL)]) == NULL
+    assert qwbatch([wjob(0), wjob(4, ldqt=200)]) == LD
+    assert qwbatch([wjob(0), wjob(4, qt=P(5))]) == OVERLAP  # within one job
+    # across jobs: outputs may not touch another job's input or outputs; inputs may be shared
+    assert qwbatch([wjob(0), wjob(4, q=P(0))]) == OVERLAP  # job 1's codes over job 0's weight
+    assert qwbatch([wjob(0), wjob(4, qt=P(1))]) == OVERLAP  # job 1's W^T codes over job 0's codes
+    assert qwbatch([wjob(0), wjob(4, s=P(3))]) == OVERLAP  # job 1's scales in job 0's W^T codes
+    assert qwbatch([wjob(0, q=P(6)), wjob(4)]) == OVERLAP  # job 0's codes over job 1's scales
+    valid(lambda: qwbatch([wjob(0), wjob(4, w=P(0))]))  # both read one weight
+    valid(lambda: qwbatch([wjob(0), wjob(4, q=P(0), N=0)]))  # an empty job's buffers are never touched
+    # the tiles of all jobs together must fit one grid: 2^16 x 2^15 tiles in one (fake, disjoint) job
+    N, K = 1 << 23, 1 << 22
+    far = lambda e: ctypes.c_void_p(1 << e)
+    big = wjob(0, N=N, K=K, ldw=K, ldq=K, lds=K // 128, ldqt=N, w=far(47), q=far(48), s=far(49), qt=far(50))
+    assert qwbatch([big]) == SHAPE
 
 
 def test_gemm_dgrad_wt_validation():

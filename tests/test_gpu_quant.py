@@ -343,3 +343,78 @@ def test_weight_dual_full_size_and_edges():
     oq, os_ = oracle.quant_weight_128x128(x.float().numpy(), oracle.E5M2)
     same((q.cpu().numpy(), s.cpu().numpy()), (oq, os_), "edge weight dual")
     assert np.array_equal(qt.cpu().numpy(), oq.T)
+
+
+# ------------------------------------------------------------------------------------------
+# several weights in one launch
+# ------------------------------------------------------------------------------------------
+
+def _padded_job(w, fmt_pad=(16, 4, 32)):
+    """Outputs for w in padded layouts (row strides beyond the row length), as views."""
+    N, K = w.shape
+    pq, ps, pqt = fmt_pad
+    q = torch.empty((N, K + pq), dtype=torch.uint8, device=DEV)[:, :K]
+    s = torch.empty((N // 128, K // 128 + ps), dtype=torch.float32, device=DEV)[:, :K // 128]
+    qt = torch.empty((K, N + pqt), dtype=torch.uint8, device=DEV)[:, :N]
+    return q, s, qt
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_weights_batch_matches_single_and_oracle(fmt, dt):
+    """One launch over weights of mixed shapes (one empty, one a strided view, one with padded
+    outputs): every job's codes, scales and transposed codes equal the single-weight kernel's and
+    the oracle's, bit for bit."""
+    gen = (lambda shape, seed: synth.random_bf16(shape, seed=seed, std=0.02)) if dt == "bf16" else \
+        (lambda shape, seed: synth.random_f32(shape, seed=seed))
+    big = gen((256, 1024), 31).to(DEV)
+    ws = [gen((128, 128), 11).to(DEV), gen((384, 256), 12).to(DEV), gen((0, 256), 13).to(DEV),
+          big[:, 128:512], gen((256, 640), 14).to(DEV)]
+    outs = []
+    for i, w in enumerate(ws):
+        N, K = w.shape
+        if i == 4:
+            outs.append(_padded_job(w))
+        else:
+            outs.append((torch.empty((N, K), dtype=torch.uint8, device=DEV),
+                         torch.empty((N // 128, K // 128), dtype=torch.float32, device=DEV),
+                         torch.empty((K, N), dtype=torch.uint8, device=DEV)))
+    fq.fp8bq_quantize_weights_dual([(w,) + o for w, o in zip(ws, outs)], FP[fmt])
+    torch.cuda.synchronize()
+    for i, (w, (q, s, qt)) in enumerate(zip(ws, outs)):
+        if w.shape[0] == 0:
+            continue
+        q1, s1, qt1 = fq.quantize_weight_dual(w, FP[fmt])
+        torch.cuda.synchronize()
+        assert torch.equal(q, q1) and torch.equal(qt, qt1), f"job {i}: codes differ from the single-weight call"
+        assert np.array_equal(f32_bits(s.cpu().numpy()), f32_bits(s1.cpu().numpy())), f"job {i}: scales"
+        oq, os_ = oracle.quant_weight_128x128(w.float().cpu().numpy(), fmt)
+        same((q.cpu().numpy(), s.cpu().numpy()), (oq, os_), f"batched weight job {i} {tuple(w.shape)} {dt}")
+        assert np.array_equal(qt.cpu().numpy(), oq.T), f"job {i}: transposed codes"
+    say(f"batched weight quantization ({fmt}, {dt}): {len(ws)} jobs bit-identical to single calls and the oracle")
+
+
+def test_weights_batch_decoder_block_and_many():
+    """The decoder block's four weights in one launch (bit-identical to four single-weight launches,
+    and to the oracle for two of them); then 20 small weights, which the helper splits into two
+    launches of at most 16."""
+    ws = [synth.decoder_linear(n)["W"] for n, _, _ in synth.DECODER_LINEARS]
+    wd = [w.to(DEV) for w in ws]
+    outs = fq.quantize_weights_dual(wd, fq.E4M3)
+    singles = [fq.quantize_weight_dual(w, fq.E4M3) for w in wd]
+    torch.cuda.synchronize()
+    for (n, _, _), o, s1 in zip(synth.DECODER_LINEARS, outs, singles):
+        for a, b in zip(o, s1):
+            assert torch.equal(a, b), f"{n}: batched and single-weight outputs differ"
+    for i in (1, 3):
+        oq, os_ = oracle.quant_weight_128x128(ws[i].float().numpy(), oracle.E4M3)
+        same((outs[i][0].cpu().numpy(), outs[i][1].cpu().numpy()), (oq, os_), f"{synth.DECODER_LINEARS[i][0]} W")
+        assert np.array_equal(outs[i][2].cpu().numpy(), oq.T)
+    many = [synth.random_bf16((128 * (1 + i % 3), 128 * (1 + i % 2)), seed=900 + i, std=0.5).to(DEV)
+            for i in range(20)]
+    outs = fq.quantize_weights_dual(many, fq.E5M2)
+    torch.cuda.synchronize()
+    for i, (w, (q, s, qt)) in enumerate(zip(many, outs)):
+        oq, os_ = oracle.quant_weight_128x128(w.float().cpu().numpy(), oracle.E5M2)
+        same((q.cpu().numpy(), s.cpu().numpy()), (oq, os_), f"small weight {i}")
+        assert np.array_equal(qt.cpu().numpy(), oq.T)
