@@ -54,6 +54,18 @@ int main(void) {
   static float w[256 * 256];
   EXPECT(fp8bq_hyperball_step(w, 256, x, FP8BQ_IN_BF16, 256, 256, 256, 1e-4, 0.1, 0.0, 0.0, NULL, ws, sizeof ws,
                               NULL) == FP8BQ_ERR_VALUE);     /* eps must be > 0 */
+  /* several weights: a job array from C, checked job by job and across jobs */
+  static uint8_t qt[256 * 256], q2[256 * 256], qt2[256 * 256];
+  static float s2[4];
+  fp8bq_weight_job jobs[2] = {{x, 256, 256, 256, q, 256, s, 2, qt, 256}, {x, 256, 256, 256, q2, 256, s2, 2, qt2, 256}};
+  EXPECT(fp8bq_quantize_weights_dual(jobs, 0, FP8BQ_IN_BF16, FP8BQ_E4M3, NULL) == FP8BQ_OK);
+  EXPECT(fp8bq_quantize_weights_dual(jobs, FP8BQ_MAX_WEIGHT_JOBS + 1, FP8BQ_IN_BF16, FP8BQ_E4M3, NULL) ==
+         FP8BQ_ERR_VALUE);
+  jobs[1].q = q;                                             /* job 1 would overwrite job 0's codes */
+  EXPECT(fp8bq_quantize_weights_dual(jobs, 2, FP8BQ_IN_BF16, FP8BQ_E4M3, NULL) == FP8BQ_ERR_OVERLAP);
+  jobs[1].q = q2;
+  jobs[1].K = 200;
+  EXPECT(fp8bq_quantize_weights_dual(jobs, 2, FP8BQ_IN_BF16, FP8BQ_E4M3, NULL) == FP8BQ_ERR_SHAPE);
 
   if (failures) return 1;
   printf("ok\n");
