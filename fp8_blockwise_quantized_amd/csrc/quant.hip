@@ -1,6 +1,6 @@
 // FP8 quantize kernels for gfx950: blockwise 1x128 (activations), 128x1 (token axis, transposed
-// output for wgrad), both at once (dual), 128x128 (weights, optionally also transposed), and the
-// per-tensor delayed-scaling variant at the end of the file.
+// output for wgrad), both at once (dual), 128x128 (weights, optionally also transposed, one weight or
+// several per launch), and the per-tensor delayed-scaling variant at the end of the file.
 //
 // Rule per group ("用 RTX 5090 花 $7000 训练 2B 大模型：Puro-2B 低成本预训练技术解析", section
 // "核心挑战：Scale Factor 管理", FP8Linear._quantize): amax = max|x|; s = max(RN(amax/fmt_max), 1e-12);
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(256) void quant_128x128_dual_kernel(const TIn* __re
 
 // Several weights in one launch: the tiles of job j are blocks start[j] .. start[j+1]-1, each job's
 // tiles in the single-weight kernel's order, so every job gets exactly that kernel's codes and scales.
-// Jobs with no tiles have start[j] == start[j+1] and are never selected.
+// The host lists only jobs with tiles (start strictly increasing); the job search is a scalar scan.
 template <typename TIn, int FMT>
 __global__ __launch_bounds__(256) void quant_weights_dual_kernel(WeightDualBatch b) {
   const uint32_t blk = blockIdx.x;
