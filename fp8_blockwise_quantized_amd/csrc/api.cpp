@@ -196,9 +196,12 @@ int fp8bq_quantize_weights_dual(const fp8bq_weight_job* jobs, int count, fp8bq_i
   uint64_t tiles = 0;
   for (int j = 0; j < count; ++j) {
     if (empty[j]) continue;
-    const fp8bq_weight_job& a = jobs[j];
+    const WeightJobArgs& a = args[j];  // the validated copy, not the caller's array again
     const int i = b.count++;
-    b.w[i] = a.w; b.q[i] = a.q; b.s[i] = a.s; b.qt[i] = a.qt;
+    b.w[i] = a.w;
+    b.q[i] = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.q));
+    b.s[i] = const_cast<float*>(static_cast<const float*>(a.s));
+    b.qt[i] = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.qt));
     b.ldw[i] = a.ldw; b.ldq[i] = a.ldq; b.lds[i] = a.lds; b.ldqt[i] = a.ldqt;
     b.nkb[i] = (uint32_t)(a.K / 128);
     b.start[i] = (uint32_t)tiles;
