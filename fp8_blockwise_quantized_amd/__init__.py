@@ -217,6 +217,8 @@ def fp8bq_quantize_weights_dual(jobs, fmt):
             wt = _in_type(w)
         elif _in_type(w) != wt:
             raise TypeError("all weights of one fp8bq_quantize_weights_dual call must share one dtype")
+        if any(t.device != jobs[0][0].device for t in (w, q, s, qt)):
+            raise ValueError("all tensors of one fp8bq_quantize_weights_dual call must be on one device")
         N, K = w.shape
         arr[i] = WeightJob(w.data_ptr(), N, K, _ld(w), q.data_ptr(), _ld(q), s.data_ptr(), _ld(s), qt.data_ptr(),
                            _ld(qt))

@@ -371,3 +371,16 @@ def test_c99_caller(tmp_path):
                     src, "-L", libdir, "-lfp8bq", f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
+
+
+def test_weights_batch_binding_rejects_mixed_dtypes_and_devices():
+    """The binding's own checks, before the library is called (CPU tensors: no launch happens)."""
+    w1 = torch.zeros((128, 128), dtype=torch.bfloat16)
+    w2 = torch.zeros((128, 128), dtype=torch.float32)
+    out = lambda: (torch.empty((128, 128), dtype=torch.uint8), torch.empty((1, 1), dtype=torch.float32),
+                   torch.empty((128, 128), dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        fq.fp8bq_quantize_weights_dual([(w1,) + out(), (w2,) + out()], fq.E4M3)
+    q, s, qt = out()
+    with pytest.raises(ValueError):
+        fq.fp8bq_quantize_weights_dual([(w1, q, s, qt.to("meta"))], fq.E4M3)
