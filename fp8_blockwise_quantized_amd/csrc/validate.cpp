@@ -7,10 +7,16 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool fmt_ok(int f) { return f == 0 || f == 1; }
 static int in_esize(int t) { return t == 0 ? 2 : (t == 1 ? 4 : 0); }
 
+// No device allocation reaches 2^48 bytes; bounding every matrix's byte extent by that keeps the
+// extent and overlap arithmetic below free of overflow.
+constexpr int64_t kMaxExtentBytes = int64_t(1) << 48;
+
 int check_mat(const Mat& m, bool align_ld) {
   if (m.p == nullptr) return kErrNull;
   if (!aligned16(m.p)) return kErrAlign;
   if (m.ld < m.cols || m.ld < 1) return kErrLd;
+  const int64_t max_elems = kMaxExtentBytes / m.esize;
+  if (m.ld > max_elems || (m.rows > 1 && m.rows - 1 > (max_elems - m.cols) / m.ld)) return kErrShape;
   if (align_ld && ((m.ld * m.esize) % 16) != 0) return kErrLd;
   return kOk;
 }

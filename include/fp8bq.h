@@ -52,7 +52,8 @@ extern "C" {
 typedef enum {
   FP8BQ_OK = 0,
   FP8BQ_ERR_NULL = 1,      /* a required pointer is NULL */
-  FP8BQ_ERR_SHAPE = 2,     /* negative size, or a grouped/contracted size not a multiple of 128 */
+  FP8BQ_ERR_SHAPE = 2,     /* negative size, a grouped/contracted size not a multiple of 128, or a
+                              matrix spanning 2^48 bytes or more */
   FP8BQ_ERR_LD = 3,        /* leading dimension smaller than the row length, or misaligned; for the
                               GEMMs' code operands also 255 * ld + contraction length >= 2^32 bytes
                               (a 256-row tile is addressed through a 32-bit range: rows of codes

@@ -384,3 +384,12 @@ def test_weights_batch_binding_rejects_mixed_dtypes_and_devices():
     q, s, qt = out()
     with pytest.raises(ValueError):
         fq.fp8bq_quantize_weights_dual([(w1, q, s, qt.to("meta"))], fq.E4M3)
+
+
+def test_matrices_beyond_the_address_space_are_rejected():
+    """A matrix whose byte extent reaches 2^48 cannot exist on the device; the check also keeps the
+    overlap arithmetic free of overflow."""
+    assert q1x128(R=1 << 41) == SHAPE  # 2^41 rows of 512 bytes
+    assert q1x128(R=2, ldx=1 << 47) == SHAPE  # two rows 2^48 bytes apart
+    assert q1x128(R=1 << 62, ldx=1 << 62) == SHAPE  # the product would overflow 64 bits
+    valid(lambda: q1x128(R=1 << 20, ldx=1 << 20, q=P(1 << 22), ldq=256, s=P(1 << 23), lds=1 << 20))
