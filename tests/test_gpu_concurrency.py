@@ -62,3 +62,40 @@ def test_threads_on_separate_streams_match_serial():
         assert got is not None, f"thread {i} did not finish"
         for a, b in zip(got, want):
             assert torch.equal(a, b), f"thread {i}: results differ from the serial run"
+
+
+def test_batched_weight_quantization_threads_match_serial():
+    """Several host threads, each quantizing its own set of weights in one batched launch on its own
+    stream, get exactly the serial results (the launch keeps its job table in kernel arguments, so
+    concurrent calls share nothing)."""
+    sets = [[synth.random_bf16((128 * (1 + (i + j) % 4), 128 * (1 + j % 3)), seed=700 + 10 * i + j, std=0.3).to(DEV)
+             for j in range(5)] for i in range(4)]
+    serial = [fq.quantize_weights_dual(ws) for ws in sets]
+    torch.cuda.synchronize()
+    results, errors = [None] * len(sets), []
+    start = threading.Barrier(len(sets))
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                start.wait()
+                for _ in range(10):
+                    out = fq.quantize_weights_dual(sets[i])
+            s.synchronize()
+            results[i] = out
+        except Exception as e:  # surfaced in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(sets))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i, (got, want) in enumerate(zip(results, serial)):
+        assert got is not None, f"thread {i} did not finish"
+        for g, w in zip(got, want):
+            for a, b in zip(g, w):
+                assert torch.equal(a, b), f"thread {i}: batched results differ from the serial run"
