@@ -418,3 +418,25 @@ def test_weights_batch_decoder_block_and_many():
         oq, os_ = oracle.quant_weight_128x128(w.float().cpu().numpy(), oracle.E5M2)
         same((q.cpu().numpy(), s.cpu().numpy()), (oq, os_), f"small weight {i}")
         assert np.array_equal(qt.cpu().numpy(), oq.T)
+
+
+def test_weights_batch_error_enqueues_nothing():
+    """A batch with one bad job fails as a whole: the status is returned and no job's outputs are
+    written, the valid ones included."""
+    w0 = synth.random_bf16((256, 256), seed=41, std=0.1).to(DEV)
+    w1 = synth.random_bf16((128, 256), seed=42, std=0.1).to(DEV)
+    q0 = torch.full((256, 256), 0xA5, dtype=torch.uint8, device=DEV)
+    s0 = torch.full((2, 2), -1.0, dtype=torch.float32, device=DEV)
+    qt0 = torch.full((256, 256), 0x5A, dtype=torch.uint8, device=DEV)
+    q1 = torch.empty((128, 256), dtype=torch.uint8, device=DEV)
+    s1 = torch.empty((1, 2), dtype=torch.float32, device=DEV)
+    bad_qt1 = q0[:, :128]  # job 1's W^T codes [256, 128] would land on job 0's codes
+    with pytest.raises(fq.Fp8bqError) as e:
+        fq.fp8bq_quantize_weights_dual([(w0, q0, s0, qt0), (w1, q1, s1, bad_qt1)], fq.E4M3)
+    assert e.value.status == 10  # FP8BQ_ERR_OVERLAP
+    qt1 = torch.empty((200, 128), dtype=torch.uint8, device=DEV)
+    with pytest.raises(fq.Fp8bqError) as e:
+        fq.fp8bq_quantize_weights_dual([(w0, q0, s0, qt0), (w1[:, :200], q1[:, :200], s1, qt1)], fq.E4M3)
+    assert e.value.status == 2  # FP8BQ_ERR_SHAPE: K = 200
+    torch.cuda.synchronize()
+    assert bool((q0 == 0xA5).all()) and bool((qt0 == 0x5A).all()) and bool((s0 == -1.0).all())
