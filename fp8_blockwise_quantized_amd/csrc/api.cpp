@@ -54,6 +54,7 @@ static int run_gemm(const GemmArgs& g, void* stream) {
   bool empty = false, zero = false;
   int st = validate_gemm(g, plan.ws_total(), &empty, &zero);
   if (st != kOk || empty) return st;
+  if (!plan.fits) return kErrShape;
   if ((st = current_device(nullptr)) != kOk) return st;
   hipStream_t s = (hipStream_t)stream;
   const int oes = g.out_t == 0 ? 2 : 4;
@@ -309,6 +310,7 @@ int fp8bq_gemm_plan(fp8bq_op op, int64_t M, int64_t N, int64_t K, int32_t* tile_
   if (!tile_m || !tile_n || !split_k) return kErrNull;
   if ((int)op < 0 || (int)op > 4 || M < 0 || N < 0 || K < 0) return kErrShape;
   const GemmPlan p = plan_gemm((int)op, M, N, K, cu_count_or_default());
+  if (!p.fits) return kErrShape;
   *tile_m = p.tile_m;
   *tile_n = p.tile_n;
   *split_k = p.split_k;

@@ -15,7 +15,7 @@ static int forced_shape() {
   return v;
 }
 
-static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int64_t cdiv(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0); }  // a >= 0, b > 0
 
 // Time of one contraction block for one round of resident work units, in microseconds, measured
 // on MI355X: two 128x128 workgroups per CU take ~1.2 us per block, one 256x256 workgroup ~2.05 us
@@ -69,6 +69,16 @@ GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count) {
   }
   const int64_t cus = cu_count > 0 ? cu_count : 256;
   const int64_t nkb = contraction / 128;
+  // one launch addresses its work units with 32 bits: at most 2^31 - 1 units of any tile shape and
+  // split; sizes beyond that (far past any device memory) get an empty plan that the caller refuses
+  const int64_t kMaxTiles128 = ((int64_t)1 << 28) - 1;
+  const int64_t t128m = rows > 0 ? cdiv(rows, 128) : 0, t128n = cols > 0 ? cdiv(cols, 128) : 0;
+  if (t128m > kMaxTiles128 || t128n > kMaxTiles128 || (t128n > 0 && t128m > kMaxTiles128 / t128n) ||
+      nkb > ((int64_t)1 << 31) - 1 ||
+      (op == kOpDgrad && (double)N * (double)K >= 4.611686018427388e18)) {
+    p.fits = false;
+    return p;
+  }
   const bool work = rows > 0 && cols > 0 && nkb > 0;
   if (forced_shape() >= 0) {
     p.shape = forced_shape();
@@ -90,7 +100,7 @@ GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count) {
   p.units = p.tiles_m * p.tiles_n * p.split_k;
   // persistent grid: one workgroup per slot (a multiple of 8, so each workgroup stays on one XCD's
   // range of tiles), or one per unit when there are fewer units
-  int64_t g = slots - slots % 8;
+  int64_t g = slots >= 8 ? slots - slots % 8 : slots;  // (a device with fewer than 8 CUs: all of them)
   p.grid = p.units < g ? p.units : g;
   p.ws_gemm = p.split_k > 1 ? (size_t)p.split_k * (size_t)rows * (size_t)cols * 4 : 0;
   p.ws_transpose = (op == kOpDgrad) ? (size_t)N * (size_t)K : 0;

@@ -35,6 +35,9 @@ struct GemmPlan {
   int64_t grid = 0;   // persistent workgroups launched
   size_t ws_gemm = 0;       // workspace for split partial sums
   size_t ws_transpose = 0;  // workspace for dgrad's transposed weight codes
+  // false when the product is too large for one launch (more than 2^28 - 1 output tiles of
+  // 128x128, or a dgrad transpose buffer past 2^62 bytes); the plan is then empty
+  bool fits = true;
   size_t ws_total() const { return ws_transpose + ws_gemm; }
 };
 

@@ -52,8 +52,9 @@ extern "C" {
 typedef enum {
   FP8BQ_OK = 0,
   FP8BQ_ERR_NULL = 1,      /* a required pointer is NULL */
-  FP8BQ_ERR_SHAPE = 2,     /* negative size, a grouped/contracted size not a multiple of 128, or a
-                              matrix spanning 2^48 bytes or more */
+  FP8BQ_ERR_SHAPE = 2,     /* negative size, a grouped/contracted size not a multiple of 128, a
+                              matrix spanning 2^48 bytes or more, or a GEMM with 2^28 or more
+                              output tiles of 128x128 */
   FP8BQ_ERR_LD = 3,        /* leading dimension smaller than the row length, or misaligned; for the
                               GEMMs' code operands also 255 * ld + contraction length >= 2^32 bytes
                               (a 256-row tile is addressed through a 32-bit range: rows of codes
@@ -356,8 +357,8 @@ size_t fp8bq_gemm_workspace_size(fp8bq_op op, int64_t M, int64_t N, int64_t K);
  * dgrad [M, K], wgrad [N, K]) and the number of parts the contraction is split into (*split_k;
  * 1 = no split, > 1 = FP32 partial sums in the workspace followed by a reduction pass).  The
  * plan is a deterministic function of (op, M, N, K) and the device's compute-unit count.
- * Returns FP8BQ_ERR_NULL if an output pointer is NULL, FP8BQ_ERR_SHAPE for an unknown op or a
- * negative size; writes nothing then. */
+ * Returns FP8BQ_ERR_NULL if an output pointer is NULL, FP8BQ_ERR_SHAPE for an unknown op, a
+ * negative size or a product too large for one launch (see FP8BQ_ERR_SHAPE); writes nothing then. */
 int fp8bq_gemm_plan(fp8bq_op op, int64_t M, int64_t N, int64_t K, int32_t* tile_m, int32_t* tile_n,
                     int32_t* split_k);
 

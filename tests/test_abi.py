@@ -393,3 +393,39 @@ def test_matrices_beyond_the_address_space_are_rejected():
     assert q1x128(R=2, ldx=1 << 47) == SHAPE  # two rows 2^48 bytes apart
     assert q1x128(R=1 << 62, ldx=1 << 62) == SHAPE  # the product would overflow 64 bits
     valid(lambda: q1x128(R=1 << 20, ldx=1 << 20, q=P(1 << 22), ldq=256, s=P(1 << 23), lds=1 << 20))
+
+
+def test_gemm_too_large_for_one_launch_is_refused():
+    """2^22 x 2^22 outputs are 2^30 tiles of 128x128, more than one launch addresses: FP8BQ_ERR_SHAPE
+    from the call and from fp8bq_gemm_plan, with buffers placed far apart so that no other check
+    fires first."""
+    M = N = 1 << 22
+    far = lambda e: ctypes.c_void_p(1 << e)
+    st = gemm("fp8bq_gemm_fprop", M=M, N=N, K=128, qa=far(40), ldqa=128, sa=far(41), ldsa=M, qb=far(42), ldqb=128,
+              sb=far(43), ldsb=1, out=far(45), ldout=N, ws=far(44), ws_bytes=1 << 20)
+    assert st == SHAPE
+    tm, tn, sk = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    assert fq.lib().fp8bq_gemm_plan(fq.OP_FPROP, M, N, 128, ctypes.byref(tm), ctypes.byref(tn),
+                                    ctypes.byref(sk)) == SHAPE
+    assert fq.fp8bq_gemm_workspace_size(fq.OP_FPROP, M, N, 128) == 0
+
+
+def test_host_code_under_sanitizers():
+    """The validation and the planner (pure host C++) built with g++ and the address and
+    undefined-behaviour sanitizers, driven by tests/csrc/host_checks.cpp over random and extreme
+    arguments: no undefined behaviour, only documented statuses, consistent plans."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    csrc = os.path.join(ROOT, "fp8_blockwise_quantized_amd", "csrc")
+    exe = os.path.join(os.environ.get("TMPDIR", "/tmp"), f"fp8bq_host_checks_{os.getpid()}")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-I", csrc,
+           os.path.join(ROOT, "tests", "csrc", "host_checks.cpp"), os.path.join(csrc, "validate.cpp"),
+           os.path.join(csrc, "plan.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+    finally:
+        os.remove(exe)
