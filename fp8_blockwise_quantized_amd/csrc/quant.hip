@@ -331,8 +331,10 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const TIn* __restric
 
 // Per-tensor scale of the delayed-scaling rule (below), computed by every block of the code pass
 // from the amax pass's partial maxima and the running amax it saved: cur = max of the partials;
-// a = fp32(fp32(a_old * b1) + fp32(cur * b2)); s = max(fp32(a / fmt_max), 1e-12).  The first block
-// stores the new running amax and the scale.  b1 = fp32(beta), b2 = fp32(1 - beta).
+// fresh = fp32(cur * b2), rounded to BF16 when the tensor is BF16 (the listing weights the current
+// amax in the tensor's own type); a = fp32(fp32(a_old * b1) + fresh); s = max(fp32(a / fmt_max),
+// 1e-12).  The first block stores the new running amax and the scale.  b1 = fp32(beta),
+// b2 = fp32(1 - beta).
 struct TensorScaleArgs {
   const float* partial;  // n partial maxima, then the running amax as it was before this call
   int n;
@@ -341,7 +343,7 @@ struct TensorScaleArgs {
   float* s;
 };
 
-template <int FMT>
+template <typename TIn, int FMT>
 __device__ __forceinline__ float tensor_scale(const TensorScaleArgs& a) {
   __shared__ float tmax[4];
   float m = 0.0f;
@@ -350,7 +352,9 @@ __device__ __forceinline__ float tensor_scale(const TensorScaleArgs& a) {
   if ((threadIdx.x & 63) == 0) tmax[threadIdx.x >> 6] = m;
   __syncthreads();
   const float cur = __builtin_fmaxf(__builtin_fmaxf(tmax[0], tmax[1]), __builtin_fmaxf(tmax[2], tmax[3]));
-  const float am = __fadd_rn(__fmul_rn(a.partial[kTensorAmaxBlocks], a.b1), __fmul_rn(cur, a.b2));
+  float fresh = __fmul_rn(cur, a.b2);
+  if constexpr (sizeof(TIn) == 2) fresh = round_bf16(fresh);
+  const float am = __fadd_rn(__fmul_rn(a.partial[kTensorAmaxBlocks], a.b1), fresh);
   const float sc = group_scale<FMT>(am);
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     a.amax[0] = am;
@@ -384,7 +388,7 @@ __device__ __forceinline__ void weight_dual_tile(const TIn* __restrict__ w, int6
   for (int p = 0; p < 8; ++p) Load8<TIn>::run(w + (nb * kGroup + 8 * rg + p) * ldw + col, v[p]);
   float sc;
   if constexpr (TENSOR) {
-    sc = tensor_scale<FMT>(ta);
+    sc = tensor_scale<TIn, FMT>(ta);
     if constexpr (sizeof(TIn) == 4) {
 #pragma unroll
       for (int p = 0; p < 8; ++p)
@@ -466,8 +470,9 @@ __global__ __launch_bounds__(256) void quant_weights_dual_kernel(WeightDualBatch
 // Per-tensor delayed scaling ("用 RTX 5090 花 $7000 训练 2B 大模型：Puro-2B 低成本预训练技术解析",
 // section "核心挑战：Scale Factor 管理", FP8Linear: _update_amax, _quantize, forward).  One scale per
 // tensor from a running amax: the tensor's current max|x| (of the values as given) updates the
-// running value, a = fp32(fp32(a * beta) + fp32(cur * (1 - beta))), and the tensor's BF16 copy is
-// quantized with s = max(fp32(a / fmt_max), 1e-12).  The global max needs the whole tensor before
+// running value, a = fp32(fp32(a * beta) + fresh) with fresh = cur * (1 - beta) in the tensor's
+// type (fp32, or fp32 rounded to BF16 for a BF16 tensor), and the tensor's BF16 copy is quantized
+// with s = max(fp32(a / fmt_max), 1e-12).  The global max needs the whole tensor before
 // any code can be written, so it takes two passes:
 //   tensor_amax_kernel    per-block partial maxima (grid-stride over rows, 16-byte loads); block 0
 //                         also saves the running amax as it was;
@@ -516,7 +521,7 @@ template <typename TIn, int FMT>
 __global__ __launch_bounds__(256) void tensor_quant_kernel(const TIn* __restrict__ x, int64_t R, int64_t C,
                                                            int64_t ldx, TensorScaleArgs ta, uint8_t* __restrict__ q,
                                                            int64_t ldq) {
-  const float sc = tensor_scale<FMT>(ta);
+  const float sc = tensor_scale<TIn, FMT>(ta);
   const float rc = 1.0f / sc;
   for_tensor_chunks(x, R, C, ldx, [&](int64_t r, int64_t c, const float (&v)[8]) {
     float b[8];

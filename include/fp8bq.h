@@ -279,8 +279,10 @@ int fp8bq_gemm_wgrad(int64_t M, int64_t N, int64_t K,
  *
  * fp8bq_quantize_tensor_delayed, for x [R, C] (row-major, ldx >= C):
  *   1. cur = max |x| over the whole tensor, of the values as given (BF16 or FP32);
- *   2. *amax = fp32(fp32(*amax * fp32(beta)) + fp32(cur * fp32(1 - beta))), 1 - beta formed in
- *      double; the listing uses beta = 0.99 and starts the running amax at 1.0;
+ *   2. fresh = fp32(cur * fp32(1 - beta)), 1 - beta formed in double, and for a BF16 tensor
+ *      rounded to BF16 (nearest, ties to even): the listing weights the current amax in the
+ *      tensor's own type;  *amax = fp32(fp32(*amax * fp32(beta)) + fresh).  The listing uses
+ *      beta = 0.99 and starts the running amax at 1.0;
  *   3. *s = max(fp32(*amax / fmt_max), fp32(1e-12));
  *   4. q[r, c] = RNE code of clamp(fp32(bf16(x[r, c]) / *s), +-fmt_max): the codes of x's BF16
  *      copy (identical to x for BF16 input); and, if qt is not NULL, qt[c, r] = q[r, c] (the

@@ -14,6 +14,13 @@ buffer:
   beta and 1 - beta enter as fp32 constants (1 - beta is formed in Python
   double first).  The listing's default beta is 0.99 and its buffers start
   at 1.0.
+* the type of the weighted current amax: the listing takes max |x| of the
+  tensor as given and multiplies it by (1 - beta) before adding it to the
+  buffer, so that product has the tensor's own type.  For an FP32 tensor it
+  is fp32(cur * (1 - beta)); for a BF16 tensor torch forms the product in
+  fp32 and rounds it to BF16 (ties to even), and the fp32 buffer then adds
+  that BF16 value.  The oracle follows the listing literally: callers state
+  the tensor's type (``in_dtype`` "bf16" or "f32").
 * order (``forward``): both running amaxes are updated first, and each
   tensor is then quantized with its updated amax.  The current amax is taken
   from the tensor as given, while the quantized values are those of its
@@ -44,8 +51,16 @@ def ema_constants(beta):
     return np.float32(beta), np.float32(1.0 - float(beta))
 
 
-def amax_ema_update(amax, x, beta):
-    """New running amax after seeing tensor x: fp32(fp32(amax * beta) + fp32(max|x| * (1 - beta)))."""
+IN_DTYPES = ("bf16", "f32")
+
+
+def amax_ema_update(amax, x, beta, in_dtype):
+    """New running amax after seeing tensor x (its values as fp32 numbers; in_dtype is the type
+    the tensor has, "bf16" or "f32"):
+        fresh = fp32(max|x| * (1 - beta)), rounded to BF16 when the tensor is BF16;
+        amax' = fp32(fp32(amax * beta) + fresh)."""
+    if in_dtype not in IN_DTYPES:
+        raise ValueError(f"in_dtype must be one of {IN_DTYPES}")
     x = np.asarray(x, dtype=np.float32)
     if x.size == 0:
         raise ValueError("the running amax is not updated by an empty tensor")
@@ -53,6 +68,8 @@ def amax_ema_update(amax, x, beta):
     b1, b2 = ema_constants(beta)
     decayed = np.float32(np.float32(amax) * b1)
     fresh = np.float32(cur * b2)
+    if in_dtype == "bf16":
+        fresh = np.float32(to_bf16_rne(np.array([fresh], np.float32))[0])
     return np.float32(decayed + fresh)
 
 
@@ -71,12 +88,13 @@ def quant_tensor(x, s, fmt):
     return encode(y, fmt)
 
 
-def quant_tensor_delayed(x, amax, beta, fmt):
-    """One step of the listing for one tensor: update the running amax with x, then quantize x.
+def quant_tensor_delayed(x, amax, beta, fmt, in_dtype):
+    """One step of the listing for one tensor of type in_dtype ("bf16" or "f32"): update the
+    running amax with x, then quantize x.
 
     Returns (codes uint8 like x, scale float32, new running amax float32).
     """
-    a = amax_ema_update(amax, x, beta)
+    a = amax_ema_update(amax, x, beta, in_dtype)
     s = tensor_scale(a, fmt)
     return quant_tensor(x, s, fmt), s, a
 

@@ -33,7 +33,8 @@ def _steps(shape, dtype, fmt, transpose, beta=0.99, mags=(1.0, 40.0, 0.05), seed
         x = _input(shape, seed + 17 * step + shape[0], dtype, mag)
         q, s, qt = fq.quantize_tensor_delayed(x.to(DEV), amax_d, beta, FP[fmt], transpose)
         torch.cuda.synchronize()
-        oq, os_, a = oracle.quant_tensor_delayed(x.float().numpy(), a, beta, fmt)
+        oq, os_, a = oracle.quant_tensor_delayed(x.float().numpy(), a, beta, fmt,
+                                                 "bf16" if dtype == torch.bfloat16 else "f32")
         assert f32_bits(amax_d.cpu().numpy())[0] == f32_bits(a), f"step {step}: running amax"
         assert f32_bits(s.cpu().numpy())[0] == f32_bits(os_), f"step {step}: scale"
         got = q.cpu().numpy()
@@ -76,7 +77,7 @@ def test_strided_input_and_empty():
     amax = torch.full((1,), 5.0, dtype=torch.float32, device=DEV)
     q, s, qt = fq.quantize_tensor_delayed(x, amax, 0.99, fq.E4M3, transpose=True)
     torch.cuda.synchronize()
-    oq, os_, a = oracle.quant_tensor_delayed(x.float().cpu().numpy(), np.float32(5.0), 0.99, E4)
+    oq, os_, a = oracle.quant_tensor_delayed(x.float().cpu().numpy(), np.float32(5.0), 0.99, E4, "bf16")
     assert np.array_equal(q.cpu().numpy(), oq) and f32_bits(s.cpu().numpy())[0] == f32_bits(os_)
     # no rows: nothing is enqueued, the running amax and the scale keep their values
     s0 = torch.full((1,), 7.0, dtype=torch.float32, device=DEV)
@@ -96,7 +97,7 @@ def test_activation_size_sampled():
     q, s, qt = fq.quantize_tensor_delayed(X.to(DEV), amax, 0.99, fq.E4M3, transpose=True)
     torch.cuda.synchronize()
     xf = X.float().numpy()
-    a = oracle.amax_ema_update(np.float32(1.0), xf, 0.99)
+    a = oracle.amax_ema_update(np.float32(1.0), xf, 0.99, "bf16")
     os_ = oracle.tensor_scale(a, E4)
     assert f32_bits(amax.cpu().numpy())[0] == f32_bits(a)
     assert f32_bits(s.cpu().numpy())[0] == f32_bits(os_)

@@ -113,7 +113,7 @@ def test_more_than_65535_row_blocks():
         assert f32_bits(sw[r0 // 128].cpu().numpy())[0] == f32_bits(osw)[0, 0], r0
         assert np.array_equal(qwt[:, r0:r0 + 128].cpu().numpy(), oqw.T), r0
     # per-tensor codes and their transpose on the same rows
-    a = oracle.amax_ema_update(np.float32(1.0), X.float().abs().max().cpu().numpy().reshape(1), 0.99)
+    a = oracle.amax_ema_update(np.float32(1.0), X.float().abs().max().cpu().numpy().reshape(1), 0.99, "bf16")
     os_d = oracle.tensor_scale(a, E4)
     assert f32_bits(sd.cpu().numpy())[0] == f32_bits(os_d)
     oqd = oracle.quant_tensor(xs, os_d, E4)

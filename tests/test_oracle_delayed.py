@@ -4,13 +4,17 @@ What pins them, independent of the code under test:
 * the fp32 bit patterns of the update's two multipliers for the listing's beta = 0.99
   (0.99 -> 0x3F7D70A4; 1 - 0.99 formed in double -> 0x3C23D70A, not fp32(1 - fp32(0.99)));
 * an exact-rational recomputation (Python Fractions) of the update with one fp32 rounding per
-  product and one for the sum;
+  product and one for the sum, and for a BF16 tensor one more rounding of the weighted current
+  amax to BF16 (the product has the tensor's type in the listing);
 * the closed form of the recurrence under a constant input, c + (a0 - c) beta^n;
 * the special cases beta = 0 (the running amax is the current amax, so the per-tensor rule is the
   blockwise rule with the whole tensor as one group) and beta = 1 (the amax never moves);
 * a hand-computed double-rounding case that only the BF16 copy of the input produces;
-* the pages' listing run in CPU PyTorch (in-place decay and add on a one-element fp32 buffer,
-  amax / fmt_max, clamp(min=1e-12), BF16 copy, divide, clamp, cast), step by step;
+* the pages' listing run verbatim in CPU PyTorch on FP32 and on BF16 tensors (current amax of the
+  tensor as given, in-place decay and add on a one-element fp32 buffer, amax / fmt_max,
+  clamp(min=1e-12), BF16 copy, divide, clamp, cast), step by step;
+* that the BF16 rounding of the weighted current amax matters: on BF16 tensors the update without
+  it disagrees with the listing;
 * for the GEMM: equality with the blockwise oracle GEMM under uniform scales, a hand-computable
   product and exact linearity in the scales.
 """
@@ -46,8 +50,9 @@ def bits(v):
     return int(np.asarray(v, dtype=np.float32).view(np.uint32))
 
 
-def _rn_f32(fr: Fraction) -> Fraction:
-    """Round an exact rational to the nearest fp32 value (ties to even), normal range only."""
+def _rn_f32(fr: Fraction, mant: int = 23) -> Fraction:
+    """Round an exact rational to the nearest binary value with `mant` fraction bits (fp32: 23,
+    BF16: 7), ties to even, normal range only."""
     if fr == 0:
         return Fraction(0)
     sign = -1 if fr < 0 else 1
@@ -57,7 +62,7 @@ def _rn_f32(fr: Fraction) -> Fraction:
         e -= 1
     while Fraction(2) ** (e + 1) <= a:
         e += 1
-    quantum = Fraction(2) ** (e - 23)
+    quantum = Fraction(2) ** (e - mant)
     fl = a // quantum
     rem = a / quantum - fl
     if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
@@ -71,16 +76,22 @@ def test_multipliers_for_the_listing_beta():
     assert bits(b2) == 0x3C23D70A  # fp32(0.010000000000000009), the double 1 - 0.99 rounded once
 
 
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("beta", [0.99, 0.9, 0.5])
-def test_update_matches_exact_rational(beta):
+def test_update_matches_exact_rational(beta, in_dtype):
     rng = np.random.default_rng(3)
     b1, b2 = (Fraction(float(c)) for c in ema_constants(beta))
     for _ in range(200):
         a0 = np.float32(rng.uniform(0.01, 100.0))
         x = (rng.standard_normal(64) * rng.uniform(0.01, 50.0)).astype(np.float32)
+        if in_dtype == "bf16":  # BF16-valued elements (truncate to 8 significant bits: exact)
+            x = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
         cur = max(abs(Fraction(float(v))) for v in x)
-        want = _rn_f32(_rn_f32(Fraction(float(a0)) * b1) + _rn_f32(cur * b2))
-        assert Fraction(float(amax_ema_update(a0, x, beta))) == want
+        fresh = _rn_f32(cur * b2)
+        if in_dtype == "bf16":
+            fresh = _rn_f32(fresh, 7)
+        want = _rn_f32(_rn_f32(Fraction(float(a0)) * b1) + fresh)
+        assert Fraction(float(amax_ema_update(a0, x, beta, in_dtype))) == want
 
 
 @pytest.mark.parametrize("a0,c", [(1.0, 448.0), (1000.0, 3.5), (2.0, 2.0)])
@@ -89,7 +100,7 @@ def test_constant_input_follows_the_closed_form(a0, c):
     a = np.float32(a0)
     x = np.array([c, -c / 2], np.float32)
     for n in range(1, 501):
-        a = amax_ema_update(a, x, beta)
+        a = amax_ema_update(a, x, beta, "f32")
         exact = c + (a0 - c) * beta ** n
         # each step adds at most 1.5 fp32 ulps, and beta shrinks earlier errors: <= 150 ulps in all
         assert abs(float(a) - exact) <= 150 * 2.0 ** -23 * max(a0, c), (n, float(a), exact)
@@ -98,7 +109,7 @@ def test_constant_input_follows_the_closed_form(a0, c):
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 def test_beta_zero_is_the_rule_with_one_group(fmt):
     x = synth.random_bf16((64, 256), seed=21, outliers=True).float().numpy()
-    q, s, a = quant_tensor_delayed(x, np.float32(7.0), 0.0, fmt)
+    q, s, a = quant_tensor_delayed(x, np.float32(7.0), 0.0, fmt, "bf16")
     qg, sg = quantize_group_rows(x.reshape(1, -1), fmt)
     assert bits(a) == bits(np.max(np.abs(x)))
     assert bits(s) == bits(sg[0])
@@ -106,14 +117,15 @@ def test_beta_zero_is_the_rule_with_one_group(fmt):
     # and it agrees with the blockwise quantizers on a single 128x128 tile
     t = x[:, :128].copy()
     t = np.concatenate([t, t], axis=0)  # 128 x 128
-    qt, st, _ = quant_tensor_delayed(t, np.float32(1.0), 0.0, fmt)
+    qt, st, _ = quant_tensor_delayed(t, np.float32(1.0), 0.0, fmt, "bf16")
     qw, sw = quant_weight_128x128(t, fmt)
     assert np.array_equal(qt, qw) and bits(st) == bits(sw[0, 0])
 
 
 def test_beta_one_keeps_the_running_amax():
     x = np.array([[3.0, -900.0]], np.float32)
-    assert bits(amax_ema_update(np.float32(12.5), x, 1.0)) == bits(12.5)
+    assert bits(amax_ema_update(np.float32(12.5), x, 1.0, "f32")) == bits(12.5)
+    assert bits(amax_ema_update(np.float32(12.5), x, 1.0, "bf16")) == bits(12.5)
 
 
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
@@ -136,37 +148,65 @@ def test_bf16_copy_decides_a_tie():
     copy is 1 + 2^-4 exactly: the midpoint, which goes to the even code 1.0 (0x38).  The element 448
     fixes amax = 448 and s = 1 with beta = 0."""
     x = np.array([[448.0, 1 + 2.0 ** -4 + 2.0 ** -9]], np.float32)
-    q, s, a = quant_tensor_delayed(x, np.float32(1.0), 0.0, E4M3)
+    q, s, a = quant_tensor_delayed(x, np.float32(1.0), 0.0, E4M3, "f32")
     assert bits(s) == bits(1.0) and bits(a) == bits(448.0)
     assert q.tolist() == [[0x7E, 0x38]]  # without the BF16 copy the second code would be 0x39
+
+
+def _listing_steps(xs, fmt, beta=0.99):
+    """The listing's _update_amax and _quantize, verbatim in CPU torch, over the tensors xs (one
+    running amax buffer, initialized to one as the listing registers it).  Yields (buffer, scale,
+    codes) after each tensor."""
+    fm = fmt_max(fmt)
+    buf = torch.ones(1)
+    for xt in xs:
+        current_amax = xt.abs().max().detach()
+        buf.mul_(beta).add_(current_amax * (1 - beta))
+        scale = (buf / fm).clamp(min=1e-12)
+        codes = (xt.bfloat16() / scale).clamp(-fm, fm).to(TORCH_DT[fmt]).view(torch.uint8).numpy()
+        yield buf.numpy()[0].copy(), scale.numpy()[0].copy(), codes
+
+
+def _listing_inputs(src_dtype, n=3, shape=(32, 256), mags=(1.0, 40.0, 0.05)):
+    return [(torch.from_numpy(np.random.default_rng(step).standard_normal(shape).astype(np.float32))
+             * mags[step % len(mags)]).to(src_dtype) for step in range(n)]
 
 
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 @pytest.mark.parametrize("src_dtype", [torch.float32, torch.bfloat16])
 def test_matches_the_listing_in_torch(fmt, src_dtype):
-    """Three steps of the listing's running-amax update and quantization, in CPU PyTorch."""
-    fm = fmt_max(fmt)
-    buf = torch.ones(1, dtype=torch.float32)  # the listing's buffer, initialized to one
+    """Three steps of the listing's running-amax update and quantization, verbatim in CPU PyTorch
+    on an FP32 or a BF16 tensor, against the oracle told the tensor's type."""
+    xs = _listing_inputs(src_dtype)
+    in_dtype = "bf16" if src_dtype == torch.bfloat16 else "f32"
     a = np.float32(1.0)
-    for step, mag in enumerate([1.0, 40.0, 0.05]):
-        xt = (torch.from_numpy(np.random.default_rng(step).standard_normal((32, 256)).astype(np.float32)) * mag)
-        xt = xt.to(src_dtype)
-        # torch: decay and add in place on the fp32 buffer, then scale, BF16 copy, divide, clamp, cast
-        cur = xt.float().abs().max()
-        buf.mul_(0.99).add_(cur * (1 - 0.99))
-        scale = (buf / fm).clamp(min=1e-12)
-        codes = (xt.bfloat16() / scale).clamp(-fm, fm).to(TORCH_DT[fmt]).view(torch.uint8).numpy()
-        q, s, a = quant_tensor_delayed(xt.float().numpy(), a, 0.99, fmt)
-        assert bits(a) == bits(buf.numpy()[0]), step
-        assert bits(s) == bits(scale.numpy()[0]), step
+    for step, (xt, (buf, scale, codes)) in enumerate(zip(xs, _listing_steps(xs, fmt))):
+        q, s, a = quant_tensor_delayed(xt.float().numpy(), a, 0.99, fmt, in_dtype)
+        assert bits(a) == bits(buf), step
+        assert bits(s) == bits(scale), step
         assert np.array_equal(q, codes), step
+
+
+def test_bf16_rounding_of_the_weighted_amax_matters():
+    """Over 200 BF16 tensors the listing's running amax equals the oracle's BF16 reading at every
+    step, while an update that keeps the weighted current amax in fp32 departs from it."""
+    xs = _listing_inputs(torch.bfloat16, n=200, shape=(8, 128), mags=(1.0, 3.0, 0.3, 17.0, 0.02))
+    a_bf16 = a_f32 = np.float32(1.0)
+    departs = 0
+    for step, (xt, (buf, _, _)) in enumerate(zip(xs, _listing_steps(xs, E4M3))):
+        xf = xt.float().numpy()
+        a_bf16 = amax_ema_update(a_bf16, xf, 0.99, "bf16")
+        assert bits(a_bf16) == bits(buf), step
+        a_f32 = amax_ema_update(a_f32, xf, 0.99, "f32")
+        departs += bits(a_f32) != bits(buf)
+    assert departs > 100
 
 
 def test_gemm_equals_blockwise_gemm_with_uniform_scales():
     X = synth.random_bf16((96, 256), seed=31, outliers=True).float().numpy()
     W = synth.random_bf16((128, 256), seed=32, std=0.02).float().numpy()
-    qx, sx, _ = quant_tensor_delayed(X, np.float32(1.0), 0.5, E4M3)
-    qw, sw, _ = quant_tensor_delayed(W, np.float32(1.0), 0.5, E4M3)
+    qx, sx, _ = quant_tensor_delayed(X, np.float32(1.0), 0.5, E4M3, "bf16")
+    qw, sw, _ = quant_tensor_delayed(W, np.float32(1.0), 0.5, E4M3, "bf16")
     y = gemm_tensor(qx, sx, E4M3, qw, sw, E4M3)
     yb = gemm_fprop(qx, np.full((96, 2), sx, np.float32), E4M3, qw, np.full((1, 2), sw, np.float32), E4M3)
     assert np.array_equal(y, yb)
