@@ -19,6 +19,8 @@ Raw entry points (same names and argument order as the C ABI, tensors in place o
     fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None)
     fp8bq_gemm_workspace_size(op, M, N, K)
     fp8bq_gemm_plan(op, M, N, K) -> (tile_m, tile_n, split_k)
+    fp8bq_quantize_tensor_delayed(x, fmt, amax, beta, q, qt, s, ws)
+    fp8bq_quantize_tensor_delayed_noalloc(x, fmt, amax, beta, q, qt, s)   (the library's own scratch)
 
 Allocating helpers (outputs created with torch on the input's device):
 
@@ -99,6 +101,8 @@ _SIGS = {
     "fp8bq_quantize_tensor_workspace_size": [_c_i64, _c_i64],
     "fp8bq_quantize_tensor_delayed": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, ctypes.c_double, _c_vp,
                                       _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_sz, _c_vp],
+    "fp8bq_quantize_tensor_delayed_noalloc": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, ctypes.c_double,
+                                              _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp],
     "fp8bq_hyperball_workspace_size": [_c_i64, _c_i64],
     "fp8bq_hyperball_step": [_c_vp, _c_i64, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, ctypes.c_double, ctypes.c_double,
                              ctypes.c_double, ctypes.c_double, _c_vp, _c_vp, _c_sz, _c_vp],
@@ -297,6 +301,13 @@ def fp8bq_quantize_tensor_delayed(x, fmt, amax, beta, q, qt, s, ws):
     _check(lib().fp8bq_quantize_tensor_delayed(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(amax), float(beta), _ptr(q),
                                                _ld(q), _ptr(qt), _ld(qt) if qt is not None else 0, _ptr(s), wsp, wsb,
                                                _stream(x)), "fp8bq_quantize_tensor_delayed")
+
+
+def fp8bq_quantize_tensor_delayed_noalloc(x, fmt, amax, beta, q, qt, s):
+    R, C = x.shape
+    _check(lib().fp8bq_quantize_tensor_delayed_noalloc(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(amax), float(beta),
+                                                       _ptr(q), _ld(q), _ptr(qt), _ld(qt) if qt is not None else 0,
+                                                       _ptr(s), _stream(x)), "fp8bq_quantize_tensor_delayed_noalloc")
 
 
 def fp8bq_gemm_tensor(qa, sa, fa, qb, sb, fb, out, ws=None):

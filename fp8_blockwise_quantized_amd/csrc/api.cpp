@@ -18,8 +18,9 @@ constexpr int kMaxDevices = 64;
 static std::atomic<int> g_dev_state[kMaxDevices];
 static std::atomic<int> g_dev_cus[kMaxDevices];
 
-// Returns kOk if the current device is a gfx950; fills *cus with its compute-unit count.
-static int current_device(int* cus) {
+// Returns kOk if the current device is a gfx950; fills *cus with its compute-unit count and *index
+// with its index (each if not null).
+static int current_device(int* cus, int* index = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
@@ -37,6 +38,7 @@ static int current_device(int* cus) {
     g_dev_state[dev].store(state, std::memory_order_relaxed);
   }
   if (cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+  if (index) *index = dev;
   return state == 1 ? kOk : kErrDevice;
 }
 
@@ -280,6 +282,24 @@ int fp8bq_quantize_tensor_delayed(const void* x, fp8bq_in xt, int64_t R, int64_t
   if (st != kOk || empty) return st;
   if ((st = current_device(nullptr)) != kOk) return st;
   return launched(launch_quant_tensor_delayed(x, (int)xt, R, C, ldx, (int)fmt, amax, beta, q, ldq, qt, ldqt, s, ws,
+                                              (hipStream_t)stream));
+}
+
+int fp8bq_quantize_tensor_delayed_noalloc(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx,
+                                          fp8bq_fp8 fmt, float* amax, double beta, uint8_t* q, int64_t ldq,
+                                          uint8_t* qt, int64_t ldqt, float* s, void* stream) {
+  bool empty = false;
+  int st = validate_quant_tensor(x, (int)xt, R, C, ldx, (int)fmt, amax, beta, q, ldq, qt, ldqt, s, nullptr, 0, 0,
+                                 &empty);
+  if (st != kOk || empty) return st;
+  int dev = -1;
+  if ((st = current_device(nullptr, &dev)) != kOk) return st;
+  float* scr = nullptr;
+  if (tensor_scratch(dev, &scr) != hipSuccess) {
+    (void)hipGetLastError();
+    return kErrDevice;
+  }
+  return launched(launch_quant_tensor_delayed(x, (int)xt, R, C, ldx, (int)fmt, amax, beta, q, ldq, qt, ldqt, s, scr,
                                               (hipStream_t)stream));
 }
 

@@ -48,6 +48,9 @@ hipError_t launch_quant_weights_dual(const WeightDualBatch& b, int wt, int fmt, 
 constexpr int kTensorAmaxBlocks = 1024;
 constexpr size_t kTensorWorkspace = (kTensorAmaxBlocks + 64) * sizeof(float);
 int tensor_amax_blocks(int64_t R);
+// Device address of the library's own scratch for the delayed quantizer on device dev (the current
+// device; looked up on its first use there, then cached).
+hipError_t tensor_scratch(int dev, float** out);
 hipError_t launch_quant_tensor_delayed(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, float* amax,
                                        double beta, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s,
                                        void* ws, hipStream_t st);

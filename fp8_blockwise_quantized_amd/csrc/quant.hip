@@ -15,6 +15,8 @@
 // div_by_scale (3 VALU ops instead of an IEEE divide sequence), which returns the IEEE quotient bit
 // for bit wherever it can change a code.
 
+#include <atomic>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -642,6 +644,33 @@ hipError_t launch_quant_weights_dual(const WeightDualBatch& b, int wt, int fmt, 
   if (wt == 0)
     return fmt == kE4M3 ? launch_weights_dual_t<uint16_t, kE4M3>(b, st) : launch_weights_dual_t<uint16_t, kE5M2>(b, st);
   return fmt == kE4M3 ? launch_weights_dual_t<float, kE4M3>(b, st) : launch_weights_dual_t<float, kE5M2>(b, st);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Scratch for callers that cannot allocate (fp8bq_quantize_tensor_delayed_noalloc): the delayed
+// quantizer's workspace (partial maxima and the saved running amax, kTensorWorkspace bytes) as a
+// file-scope device array.  Each GPU holds its own copy for the life of the process, at its own
+// address; host code uses that address, looked up once per device with the device current.  Nothing
+// in it has to start at zero: every launch writes the parts it reads.  Calls that overlap on one GPU
+// share it and race.
+// ---------------------------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[kTensorWorkspace / sizeof(float)];
+
+constexpr int kMaxScratchDevices = 64;
+static std::atomic<float*> g_scratch[kMaxScratchDevices];
+
+hipError_t tensor_scratch(int dev, float** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    p = static_cast<float*>(a);
+    g_scratch[dev].store(p, std::memory_order_release);  // (racing first calls store the same address)
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 int tensor_amax_blocks(int64_t R) {

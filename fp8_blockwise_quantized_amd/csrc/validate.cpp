@@ -170,25 +170,27 @@ int validate_quant_tensor(const void* x, int xt, int64_t R, int64_t C, int64_t l
     *empty = true;
     return kOk;
   }
-  if (x == nullptr || q == nullptr || amax == nullptr || s == nullptr || ws == nullptr) return kErrNull;
+  // ws_needed == 0: the caller passes no workspace (the kernels use the library's own scratch)
+  const bool has_ws = ws_needed > 0;
+  if (x == nullptr || q == nullptr || amax == nullptr || s == nullptr || (has_ws && ws == nullptr)) return kErrNull;
   int st;
   const Mat mx{x, R, C, ldx, in_esize(xt)}, mq{q, R, C, ldq, 1}, mqt{qt, C, R, ldqt, 1};
   const Mat ma{amax, 1, 1, 1, 4}, ms{s, 1, 1, 1, 4};
   if ((st = check_mat(mx, true)) != kOk) return st;
   if ((st = check_mat(mq, true)) != kOk) return st;
   if (qt != nullptr && (st = check_mat(mqt, true)) != kOk) return st;
-  if (!aligned4(amax) || !aligned4(s) || !aligned16(ws)) return kErrAlign;
+  if (!aligned4(amax) || !aligned4(s) || (has_ws && !aligned16(ws))) return kErrAlign;
   if (ws_bytes < ws_needed) return kErrWorkspace;
-  const Mat mw{ws, 1, (int64_t)ws_needed, (int64_t)ws_needed, 1};
+  const Mat mw{has_ws ? ws : nullptr, 1, (int64_t)ws_needed, (int64_t)ws_needed, 1};
   const Mat outs[4] = {mq, mqt, ma, ms};
   const int nout = 4;
   for (int i = 0; i < nout; ++i) {
     if (outs[i].p == nullptr) continue;
-    if (overlaps(outs[i], mx) || overlaps(outs[i], mw)) return kErrOverlap;
+    if (overlaps(outs[i], mx) || (has_ws && overlaps(outs[i], mw))) return kErrOverlap;
     for (int j = i + 1; j < nout; ++j)
       if (outs[j].p != nullptr && overlaps(outs[i], outs[j])) return kErrOverlap;
   }
-  if (overlaps(mw, mx)) return kErrOverlap;
+  if (has_ws && overlaps(mw, mx)) return kErrOverlap;
   return kOk;
 }
 

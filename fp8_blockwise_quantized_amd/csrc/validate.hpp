@@ -60,6 +60,7 @@ int validate_quant_weights_dual(const WeightJobArgs* jobs, int count, int max_jo
 
 // Per-tensor delayed scaling: x [R, C] (C % 128 == 0), running amax and scale one float each (4-byte
 // aligned), q [R, C], optional qt [C, R] (then R % 128 == 0), beta in [0, 1], ws >= ws_needed bytes.
+// ws_needed == 0 validates a call that takes no workspace (ws and ws_bytes are then ignored).
 int validate_quant_tensor(const void* x, int xt, int64_t R, int64_t C, int64_t ldx, int fmt, const void* amax,
                           double beta, const void* q, int64_t ldq, const void* qt, int64_t ldqt, const void* s,
                           const void* ws, size_t ws_bytes, size_t ws_needed, bool* empty);

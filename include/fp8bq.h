@@ -304,6 +304,22 @@ int fp8bq_quantize_tensor_delayed(const void* x, fp8bq_in xt, int64_t R, int64_t
                                   float* s, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fp8bq_quantize_tensor_delayed without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Outputs, running-amax update and errors are exactly those of
+ * fp8bq_quantize_tensor_delayed (minus FP8BQ_ERR_WORKSPACE); the kernels use the library's own
+ * scratch instead: a fixed fp8bq_quantize_tensor_workspace_size() bytes (4352) of device memory per
+ * GPU, held from the first call on that GPU until the process ends, enough for any R and C.  The
+ * call allocates nothing.  Every call on one GPU shares that scratch, so calls that may overlap on
+ * one GPU (other streams, other host threads) race: order them (one stream, or events).  Nothing in
+ * the scratch needs clearing between calls.  FP8BQ_ERR_DEVICE also if the scratch's device address
+ * cannot be obtained.
+ */
+int fp8bq_quantize_tensor_delayed_noalloc(const void* x, fp8bq_in xt, int64_t R, int64_t C, int64_t ldx,
+                                          fp8bq_fp8 fmt, float* amax, double beta, uint8_t* q, int64_t ldq,
+                                          uint8_t* qt, int64_t ldqt, float* s, void* stream);
+
+/*
  * GEMM of two per-tensor-scaled operands, both contiguous along the contraction ("TN"):
  *   out[m, n] = (*sa) * (*sb) * sum_k dec(qa[m, k]) * dec(qb[n, k]),  FP32 accumulation.
  * Defining passage: as fp8bq_quantize_tensor_delayed (the listing's forward dequantizes both

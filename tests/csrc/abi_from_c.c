@@ -51,6 +51,10 @@ int main(void) {
   static uint8_t ws[8192];
   EXPECT(fp8bq_quantize_tensor_delayed(x, FP8BQ_IN_BF16, 256, 256, 256, FP8BQ_E4M3, &amax, 1.5, q, 256, NULL, 0,
                                        &scale, ws, sizeof ws, NULL) == FP8BQ_ERR_VALUE);
+  EXPECT(fp8bq_quantize_tensor_delayed_noalloc(x, FP8BQ_IN_BF16, 256, 256, 256, FP8BQ_E4M3, &amax, 1.5, q, 256,
+                                               NULL, 0, &scale, NULL) == FP8BQ_ERR_VALUE);
+  EXPECT(fp8bq_quantize_tensor_delayed_noalloc(x, FP8BQ_IN_BF16, 0, 256, 256, FP8BQ_E4M3, &amax, 0.5, q, 256, NULL,
+                                               0, &scale, NULL) == FP8BQ_OK);  /* empty: nothing to do */
   static float w[256 * 256];
   EXPECT(fp8bq_hyperball_step(w, 256, x, FP8BQ_IN_BF16, 256, 256, 256, 1e-4, 0.1, 0.0, 0.0, NULL, ws, sizeof ws,
                               NULL) == FP8BQ_ERR_VALUE);     /* eps must be > 0 */

@@ -36,7 +36,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fq.lib()
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
 
