@@ -181,24 +181,62 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+_HI = (torch.bfloat16, torch.float32)
+
+
+def _expect_all(checks, ws=None):
+    """Refuse, before any launch, tensors the C call would misread: the C ABI sees only pointers and
+    leading dimensions, so it cannot check a buffer's extent, element type or device.  checks:
+    (tensor or None, name, shape, dtypes); every tensor's dtype and shape first, then that all (and
+    the workspace ws, if any) are on the first tensor's device, a CUDA (HIP) device."""
+    for t, name, shape, dtypes in checks:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if t.dtype not in dtypes:
+            raise TypeError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+        if tuple(t.shape) != tuple(int(v) for v in shape):
+            raise ValueError(f"{name} must have shape {tuple(int(v) for v in shape)}, not {tuple(t.shape)}")
+    device = checks[0][0].device
+    if device.type != "cuda":
+        raise ValueError(f"{checks[0][1]} must be on a CUDA (HIP) device, not {device}")
+    for t, name, _, _ in checks[1:]:
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the call's tensors on {device}")
+    if ws is not None:
+        if not isinstance(ws, torch.Tensor):
+            raise TypeError("ws must be a torch tensor or None")
+        if not ws.is_contiguous():
+            raise ValueError("ws must be contiguous")
+        if ws.device != device:
+            raise ValueError(f"ws is on {ws.device}, the call's tensors on {device}")
+
+
 # ---------------------------------------------------------------------------------------------
 # raw entry points
 # ---------------------------------------------------------------------------------------------
 
 def fp8bq_quantize_act_1x128(x, fmt, q, s):
     R, C = x.shape
+    _expect_all([(x, "x", (R, C), _HI), (q, "q", (R, C), _U8), (s, "s", (C // 128, R), _F32)])
     _check(lib().fp8bq_quantize_act_1x128(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(q), _ld(q), _ptr(s), _ld(s),
                                           _stream(x)), "fp8bq_quantize_act_1x128")
 
 
 def fp8bq_quantize_act_128x1(x, fmt, qt, st):
     R, C = x.shape
+    _expect_all([(x, "x", (R, C), _HI), (qt, "qt", (C, R), _U8), (st, "st", (R // 128, C), _F32)])
     _check(lib().fp8bq_quantize_act_128x1(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(qt), _ld(qt), _ptr(st),
                                           _ld(st), _stream(x)), "fp8bq_quantize_act_128x1")
 
 
 def fp8bq_quantize_act_dual(x, fmt_rows, q, s, fmt_cols, qt, st):
     R, C = x.shape
+    _expect_all([(x, "x", (R, C), _HI), (q, "q", (R, C), _U8), (s, "s", (C // 128, R), _F32),
+                 (qt, "qt", (C, R), _U8), (st, "st", (R // 128, C), _F32)])
     _check(lib().fp8bq_quantize_act_dual(_ptr(x), _in_type(x), R, C, _ld(x), fmt_rows, _ptr(q), _ld(q), _ptr(s),
                                          _ld(s), fmt_cols, _ptr(qt), _ld(qt), _ptr(st), _ld(st), _stream(x)),
            "fp8bq_quantize_act_dual")
@@ -206,6 +244,8 @@ def fp8bq_quantize_act_dual(x, fmt_rows, q, s, fmt_cols, qt, st):
 
 def fp8bq_quantize_weight_dual(w, fmt, q, s, qt):
     N, K = w.shape
+    _expect_all([(w, "w", (N, K), _HI), (q, "q", (N, K), _U8),
+                 (s, "s", (N // 128, K // 128), _F32), (qt, "qt", (K, N), _U8)])
     _check(lib().fp8bq_quantize_weight_dual(_ptr(w), _in_type(w), N, K, _ld(w), fmt, _ptr(q), _ld(q), _ptr(s), _ld(s),
                                             _ptr(qt), _ld(qt), _stream(w)), "fp8bq_quantize_weight_dual")
 
@@ -215,15 +255,14 @@ def fp8bq_quantize_weights_dual(jobs, fmt):
     One launch on the current stream of the first weight's device."""
     jobs = list(jobs)
     arr = (WeightJob * max(len(jobs), 1))()
-    wt = IN_BF16
+    wt = _in_type(jobs[0][0]) if jobs else IN_BF16
+    if any(_in_type(job[0]) != wt for job in jobs):
+        raise TypeError("all weights of one fp8bq_quantize_weights_dual call must share one dtype")
     for i, (w, q, s, qt) in enumerate(jobs):
-        if i == 0:
-            wt = _in_type(w)
-        elif _in_type(w) != wt:
-            raise TypeError("all weights of one fp8bq_quantize_weights_dual call must share one dtype")
-        if any(t.device != jobs[0][0].device for t in (w, q, s, qt)):
-            raise ValueError("all tensors of one fp8bq_quantize_weights_dual call must be on one device")
         N, K = w.shape
+        _expect_all([(jobs[0][0], "jobs[0].w", jobs[0][0].shape, _HI), (w, f"jobs[{i}].w", (N, K), _HI),
+                     (q, f"jobs[{i}].q", (N, K), _U8), (s, f"jobs[{i}].s", (N // 128, K // 128), _F32),
+                     (qt, f"jobs[{i}].qt", (K, N), _U8)])
         arr[i] = WeightJob(w.data_ptr(), N, K, _ld(w), q.data_ptr(), _ld(q), s.data_ptr(), _ld(s), qt.data_ptr(),
                            _ld(qt))
     stream = _stream(jobs[0][0]) if jobs else ctypes.c_void_p(0)
@@ -232,6 +271,8 @@ def fp8bq_quantize_weights_dual(jobs, fmt):
 
 def fp8bq_quantize_weight_128x128(w, fmt, q, s):
     N, K = w.shape
+    _expect_all([(w, "w", (N, K), _HI), (q, "q", (N, K), _U8),
+                 (s, "s", (N // 128, K // 128), _F32)])
     _check(lib().fp8bq_quantize_weight_128x128(_ptr(w), _in_type(w), N, K, _ld(w), fmt, _ptr(q), _ld(q), _ptr(s),
                                                _ld(s), _stream(w)), "fp8bq_quantize_weight_128x128")
 
@@ -257,6 +298,8 @@ def _ws_args(ws):
 def fp8bq_gemm_fprop(qx, sx, fx, qw, sw, fw, y, ws=None):
     M, K = qx.shape
     N = qw.shape[0]
+    _expect_all([(qx, "qx", (M, K), _U8), (sx, "sx", (K // 128, M), _F32), (qw, "qw", (N, K), _U8),
+                 (sw, "sw", (N // 128, K // 128), _F32), (y, "y", (M, N), _HI)], ws)
     wsp, wsb = _ws_args(ws)
     _check(lib().fp8bq_gemm_fprop(M, N, K, _ptr(qx), _ld(qx), _ptr(sx), _ld(sx), fx, _ptr(qw), _ld(qw), _ptr(sw),
                                   _ld(sw), fw, _ptr(y), _out_type(y), _ld(y), wsp, wsb, _stream(y)),
@@ -266,6 +309,8 @@ def fp8bq_gemm_fprop(qx, sx, fx, qw, sw, fw, y, ws=None):
 def fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws=None):
     M, N = qdy.shape
     K = qw.shape[1]
+    _expect_all([(qdy, "qdy", (M, N), _U8), (sdy, "sdy", (N // 128, M), _F32), (qw, "qw", (N, K), _U8),
+                 (sw, "sw", (N // 128, K // 128), _F32), (dx, "dx", (M, K), _HI)], ws)
     wsp, wsb = _ws_args(ws)
     _check(lib().fp8bq_gemm_dgrad(M, N, K, _ptr(qdy), _ld(qdy), _ptr(sdy), _ld(sdy), fdy, _ptr(qw), _ld(qw),
                                   _ptr(sw), _ld(sw), fw, _ptr(dx), _out_type(dx), _ld(dx), wsp, wsb, _stream(dx)),
@@ -275,6 +320,8 @@ def fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws=None):
 def fp8bq_gemm_dgrad_wt(qdy, sdy, fdy, qwt, sw, fw, dx, ws=None):
     M, N = qdy.shape
     K = qwt.shape[0]
+    _expect_all([(qdy, "qdy", (M, N), _U8), (sdy, "sdy", (N // 128, M), _F32), (qwt, "qwt", (K, N), _U8),
+                 (sw, "sw", (N // 128, K // 128), _F32), (dx, "dx", (M, K), _HI)], ws)
     wsp, wsb = _ws_args(ws)
     _check(lib().fp8bq_gemm_dgrad_wt(M, N, K, _ptr(qdy), _ld(qdy), _ptr(sdy), _ld(sdy), fdy, _ptr(qwt), _ld(qwt),
                                      _ptr(sw), _ld(sw), fw, _ptr(dx), _out_type(dx), _ld(dx), wsp, wsb, _stream(dx)),
@@ -284,6 +331,8 @@ def fp8bq_gemm_dgrad_wt(qdy, sdy, fdy, qwt, sw, fw, dx, ws=None):
 def fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None, accumulate=False):
     N, M = qdyt.shape
     K = qxt.shape[0]
+    _expect_all([(qdyt, "qdyt", (N, M), _U8), (sdyt, "sdyt", (M // 128, N), _F32), (qxt, "qxt", (K, M), _U8),
+                 (sxt, "sxt", (M // 128, K), _F32), (dw, "dw", (N, K), _F32 if accumulate else _HI)], ws)
     wsp, wsb = _ws_args(ws)
     ot = OUT_F32_ACCUM if accumulate else _out_type(dw)
     _check(lib().fp8bq_gemm_wgrad(M, N, K, _ptr(qdyt), _ld(qdyt), _ptr(sdyt), _ld(sdyt), fdy, _ptr(qxt), _ld(qxt),
@@ -297,6 +346,8 @@ def fp8bq_quantize_tensor_workspace_size(R, C):
 
 def fp8bq_quantize_tensor_delayed(x, fmt, amax, beta, q, qt, s, ws):
     R, C = x.shape
+    _expect_all([(x, "x", (R, C), _HI), (amax, "amax", (1,), _F32), (q, "q", (R, C), _U8),
+                 (qt, "qt", (C, R), _U8), (s, "s", (1,), _F32)], ws)
     wsp, wsb = _ws_args(ws)
     _check(lib().fp8bq_quantize_tensor_delayed(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(amax), float(beta), _ptr(q),
                                                _ld(q), _ptr(qt), _ld(qt) if qt is not None else 0, _ptr(s), wsp, wsb,
@@ -305,6 +356,8 @@ def fp8bq_quantize_tensor_delayed(x, fmt, amax, beta, q, qt, s, ws):
 
 def fp8bq_quantize_tensor_delayed_noalloc(x, fmt, amax, beta, q, qt, s):
     R, C = x.shape
+    _expect_all([(x, "x", (R, C), _HI), (amax, "amax", (1,), _F32), (q, "q", (R, C), _U8),
+                 (qt, "qt", (C, R), _U8), (s, "s", (1,), _F32)])
     _check(lib().fp8bq_quantize_tensor_delayed_noalloc(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(amax), float(beta),
                                                        _ptr(q), _ld(q), _ptr(qt), _ld(qt) if qt is not None else 0,
                                                        _ptr(s), _stream(x)), "fp8bq_quantize_tensor_delayed_noalloc")
@@ -313,6 +366,8 @@ def fp8bq_quantize_tensor_delayed_noalloc(x, fmt, amax, beta, q, qt, s):
 def fp8bq_gemm_tensor(qa, sa, fa, qb, sb, fb, out, ws=None):
     M, K = qa.shape
     N = qb.shape[0]
+    _expect_all([(qa, "qa", (M, K), _U8), (sa, "sa", (1,), _F32), (qb, "qb", (N, K), _U8), (sb, "sb", (1,), _F32),
+                 (out, "out", (M, N), _HI)], ws)
     wsp, wsb = _ws_args(ws)
     _check(lib().fp8bq_gemm_tensor(M, N, K, _ptr(qa), _ld(qa), _ptr(sa), fa, _ptr(qb), _ld(qb), _ptr(sb), fb,
                                    _ptr(out), _out_type(out), _ld(out), wsp, wsb, _stream(out)), "fp8bq_gemm_tensor")
@@ -324,6 +379,7 @@ def fp8bq_hyperball_workspace_size(R, C):
 
 def fp8bq_hyperball_step(w, g, lr, weight_decay, eps, radius, norms, ws):
     R, C = w.shape
+    _expect_all([(w, "w", (R, C), _F32), (g, "g", (R, C), _HI), (norms, "norms", (2,), _F32)], ws)
     wsp, wsb = _ws_args(ws)
     _check(lib().fp8bq_hyperball_step(_ptr(w), _ld(w), _ptr(g), _in_type(g), _ld(g), R, C, float(lr),
                                       float(weight_decay), float(eps), float(radius), _ptr(norms), wsp, wsb,

@@ -63,3 +63,22 @@ def test_quantizer_errors_enqueue_nothing():
     torch.cuda.synchronize()
     assert bool((q == 0x77).all()) and bool((s == 5.0).all())
     assert bool((qt == 0x66).all()) and bool((s2 == 5.0).all()) and bool((st == 6.0).all())
+
+
+def test_binding_refuses_mismatched_tensors_on_the_device():
+    """The binding's own checks on device tensors: an output with too few rows, scales of another
+    element type, a scale array left on the host, a workspace on the host.  Nothing runs."""
+    M, N, K = 384, 512, 1024
+    q, s, qw, sw, qd, sd = _operands(M, N, K)
+    y = torch.full((M, N), -2.0, dtype=torch.bfloat16, device=DEV)
+    short = torch.full((M - 128, N), -2.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        fq.fp8bq_gemm_fprop(q, s, fq.E4M3, qw, sw, fq.E4M3, short)
+    with pytest.raises(TypeError):
+        fq.fp8bq_gemm_fprop(q, s.to(torch.bfloat16), fq.E4M3, qw, sw, fq.E4M3, y)
+    with pytest.raises(ValueError):
+        fq.fp8bq_gemm_fprop(q, s.cpu(), fq.E4M3, qw, sw, fq.E4M3, y)
+    with pytest.raises(ValueError):
+        fq.fp8bq_gemm_fprop(q, s, fq.E4M3, qw, sw, fq.E4M3, y, torch.zeros(1 << 20, dtype=torch.uint8))
+    torch.cuda.synchronize()
+    assert bool((y == -2.0).all()) and bool((short == -2.0).all())
