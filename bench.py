@@ -338,8 +338,9 @@ def build_delayed(torch, fq, synth, dev):
 
 def run_hyperball(args, torch, fq, synth, dev):
     """Hyperball update with projection of the four decoder weights (FP32 masters, BF16 gradients).
-    Algorithmic bytes per element: gradient read 2 + weight read and write 8 + the projection's second
-    weight read and write 8 (it needs the whole updated tensor's norm first) = 18."""
+    Algorithmic bytes per element: the norms (of g, of w and of their product) must be known before
+    any element is written, so g and w are read once for them (2 + 4) and then read again and w
+    written in one update pass (2 + 4 + 4) = 16."""
     import numpy as np
     items = []
     for name, K, N in synth.DECODER_LINEARS:
@@ -348,7 +349,7 @@ def run_hyperball(args, torch, fq, synth, dev):
         radius = float(torch.linalg.vector_norm(w.double()).item())
         norms = torch.empty(2, dtype=torch.float32, device=dev)
         ws = torch.empty(fq.fp8bq_hyperball_workspace_size(N, K), dtype=torch.uint8, device=dev)
-        items.append((name, w, g, radius, norms, ws, 18 * N * K))
+        items.append((name, w, g, radius, norms, ws, 16 * N * K))
 
     def step():
         for _, w, g, radius, norms, ws, _ in items:
@@ -376,7 +377,7 @@ def run_hyperball(args, torch, fq, synth, dev):
         t = e0.elapsed_time(e1) / args.steps
         per.append({"weight": name, "shape": list(w.shape), "ms": round(t, 5),
                     "gbs": round(nbytes / (t * 1e-3) / 1e9, 1)})
-    print(json.dumps({"metric": "Hyperball update with fixed-radius projection, GB/s (18 B per weight element)",
+    print(json.dumps({"metric": "Hyperball update with fixed-radius projection, GB/s (16 B per weight element)",
                       "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(ms, 4),
                       "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "steps": args.steps,
                       "config": {"workload": "decoder-block weights (QKV, O, gate+up, down), FP32 masters, "

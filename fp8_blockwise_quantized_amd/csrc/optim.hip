@@ -9,12 +9,18 @@
 // weight stays zero).  The gradient norm is also reported (the pages' debugging advice, section
 // "调试 FP8 训练的关键步骤", is to watch it).
 //
-// All passes are HBM-bound elementwise sweeps.  A global norm is needed before any element can be
-// updated, so the step is: partial sums of squares of g (fp64, per block) -> the update, whose
-// blocks each first reduce those partials to the step coefficient and which also sums the squares
-// of the new weights -> (with a radius) the scaling pass, whose blocks each reduce those to the
-// projection factor.  Every block combines the partials in the same fixed order, so all blocks use
-// the same coefficient and results are deterministic.
+// Both passes are HBM-bound elementwise sweeps.  Global norms gate every element, so the step reads
+// first and writes once:
+//   1. per-block fp64 partial sums of g*g and, when the projection or the norms need them, of w*w
+//      and w*g (reads g, and w);
+//   2. the update, whose blocks each reduce those partials (fixed order: every block gets the same
+//      values) to the step coefficient c = fp32(-lr / n) and, with d = fp32(1 - lr * wd), to the
+//      updated weight's norm from the expansion ||w d + g c||^2 = d^2 sum w^2 + 2 d c sum wg +
+//      c^2 sum g^2, then to the projection factor; it reads w and g and writes w once.
+// That is 16 bytes per element (BF16 g) against 20 for a third sweep over the updated weight.  The
+// expansion is evaluated in fp64 over exact fp64 products of fp32 values; it differs from the norm
+// of the rounded FP32 weights by about 2^-24 relative, well inside the FP32 update's own error.
+// Results are deterministic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -64,151 +70,132 @@ __device__ __forceinline__ void for_rows(int64_t R, int64_t C, F&& f) {
     for (int64_t c8 = threadIdx.x; c8 < chunks; c8 += blockDim.x) f(r0, 8 * c8);
 }
 
-template <typename TG>
-__global__ __launch_bounds__(256) void sumsq_kernel(const TG* __restrict__ g, int64_t R, int64_t C, int64_t ldg,
-                                                    double* __restrict__ partial) {
+// Pass 1: the block's fp64 sums of g*g and, with WITH_W, of w*w and w*g, into partial[b],
+// partial[kHyperballBlocks + b] and partial[2 * kHyperballBlocks + b].
+template <typename TG, bool WITH_W>
+__global__ __launch_bounds__(256) void hyperball_sums_kernel(const float* __restrict__ w, int64_t ldw,
+                                                             const TG* __restrict__ g, int64_t ldg, int64_t R,
+                                                             int64_t C, double* __restrict__ partial) {
   __shared__ double red[4];
-  double s = 0.0;
+  double sgg = 0.0, sww = 0.0, swg = 0.0;
   for_rows(R, C, [&](int64_t r0, int64_t c) {
-    float v[kRowsPerIter][8];
-#pragma unroll
-    for (int i = 0; i < kRowsPerIter; ++i)
-      if (r0 + i < R) load8(g + (r0 + i) * ldg + c, v[i]);
+    float gv[kRowsPerIter][8], wv[kRowsPerIter][8];
 #pragma unroll
     for (int i = 0; i < kRowsPerIter; ++i)
       if (r0 + i < R) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) s = __builtin_fma((double)v[i][k], (double)v[i][k], s);
-      }
-  });
-  const double t = block_sum(s, red);
-  if (threadIdx.x == 0) partial[blockIdx.x] = t;
-}
-
-// Fixed-order sum of n partials by one block of 256 threads.
-__device__ __forceinline__ double sum_partials(const double* partial, int n, double* red) {
-  double s = 0.0;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) s += partial[i];
-  return block_sum(s, red);
-}
-
-// coef = fp32(-lr / max(||g||, eps)) (0 for an all-zero gradient, whose move is zero whatever eps
-// is), from the gradient's partial sums; block 0 reports ||g|| if asked.
-__device__ __forceinline__ float grad_coef(const double* partial, int n, double lr, double eps, float* norms,
-                                           double* red) {
-  __shared__ double bc;
-  const double s = sum_partials(partial, n, red);
-  if (threadIdx.x == 0) {
-    bc = s;
-    if (norms && blockIdx.x == 0) norms[0] = (float)__builtin_sqrt(s);
-  }
-  __syncthreads();
-  const double gn = __builtin_sqrt(bc);
-  const double d = gn > eps ? gn : eps;
-  __syncthreads();  // red is reused by the caller
-  return gn > 0.0 ? (float)(-lr / d) : 0.0f;
-}
-
-// w <- w * decay + g * coef (three fp32 roundings); with PROJ also the block's sum of squares of
-// the new weights.
-template <typename TG, bool PROJ>
-__global__ __launch_bounds__(256) void hyperball_update_kernel(float* __restrict__ w, int64_t ldw,
-                                                               const TG* __restrict__ g, int64_t ldg, int64_t R,
-                                                               int64_t C, float decay, const double* __restrict__ pg,
-                                                               int npg, double lr, double eps,
-                                                               float* __restrict__ norms,
-                                                               double* __restrict__ partial) {
-  __shared__ double red[4];
-  const float coef = grad_coef(pg, npg, lr, eps, norms, red);
-  double s = 0.0;
-  for_rows(R, C, [&](int64_t r0, int64_t c) {
-    float wv[kRowsPerIter][8], gv[kRowsPerIter][8];
-#pragma unroll
-    for (int i = 0; i < kRowsPerIter; ++i)
-      if (r0 + i < R) {
-        load8(w + (r0 + i) * ldw + c, wv[i]);
         load8(g + (r0 + i) * ldg + c, gv[i]);
+        if constexpr (WITH_W) load8(w + (r0 + i) * ldw + c, wv[i]);
       }
 #pragma unroll
     for (int i = 0; i < kRowsPerIter; ++i)
       if (r0 + i < R) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          wv[i][k] = __fadd_rn(__fmul_rn(wv[i][k], decay), __fmul_rn(gv[i][k], coef));
-          if constexpr (PROJ) s = __builtin_fma((double)wv[i][k], (double)wv[i][k], s);
+          const double gd = gv[i][k];
+          sgg = __builtin_fma(gd, gd, sgg);
+          if constexpr (WITH_W) {
+            const double wd = wv[i][k];
+            sww = __builtin_fma(wd, wd, sww);
+            swg = __builtin_fma(wd, gd, swg);
+          }
         }
-        store8(w + (r0 + i) * ldw + c, wv[i]);
       }
   });
-  if constexpr (PROJ) {
-    const double t = block_sum(s, red);
-    if (threadIdx.x == 0) partial[blockIdx.x] = t;
+  double t = block_sum(sgg, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = t;
+  if constexpr (WITH_W) {
+    __syncthreads();
+    t = block_sum(sww, red);
+    if (threadIdx.x == 0) partial[kHyperballBlocks + blockIdx.x] = t;
+    __syncthreads();
+    t = block_sum(swg, red);
+    if (threadIdx.x == 0) partial[2 * kHyperballBlocks + blockIdx.x] = t;
   }
 }
 
-// ||w|| after the update, from its partial sums (the same value in every block); block 0 reports it
-// if asked.
-__device__ __forceinline__ double weight_norm(const double* partial, int n, float* norms, double* red) {
+// Fixed-order sum of n partials by one block of 256 threads; every thread gets the result.
+__device__ __forceinline__ double sum_partials(const double* partial, int n, double* red) {
   __shared__ double bc;
-  const double s = sum_partials(partial, n, red);
-  if (threadIdx.x == 0) {
-    bc = s;
-    if (norms && blockIdx.x == 0) norms[1] = (float)__builtin_sqrt(s);
-  }
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) s += partial[i];
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) bc = s;
   __syncthreads();
-  return __builtin_sqrt(bc);
+  s = bc;
+  __syncthreads();  // red and bc are reused
+  return s;
 }
 
-// Only the norm, for a step without a projection that reports it.
-__global__ __launch_bounds__(256) void weight_norm_kernel(const double* __restrict__ partial, int n,
-                                                          float* __restrict__ norms) {
+// Pass 2: w <- fp32(fp32(w * d) + fp32(g * c)), times fp32(radius / ||w d + g c||) with PROJ.
+// c = fp32(-lr / max(||g||, eps)), 0 for an all-zero gradient (whose move is zero whatever eps is).
+// With WITH_W the updated weight's norm comes from the sums of pass 1; block 0 reports ||g|| and
+// that norm if asked.
+template <typename TG, bool WITH_W, bool PROJ>
+__global__ __launch_bounds__(256) void hyperball_update_kernel(float* __restrict__ w, int64_t ldw,
+                                                               const TG* __restrict__ g, int64_t ldg, int64_t R,
+                                                               int64_t C, float d, const double* __restrict__ partial,
+                                                               int np, double lr, double eps, double radius,
+                                                               float* __restrict__ norms) {
   __shared__ double red[4];
-  weight_norm(partial, n, norms, red);
-}
-
-// w <- w * fp32(radius / ||w||) (a zero weight is left as it is).
-__global__ __launch_bounds__(256) void scale_kernel(float* __restrict__ w, int64_t ldw, int64_t R, int64_t C,
-                                                    const double* __restrict__ pw, int npw, double radius,
-                                                    float* __restrict__ norms) {
-  __shared__ double red[4];
-  const double wn = weight_norm(pw, npw, norms, red);
-  const float f = wn > 0.0 ? (float)(radius / wn) : 1.0f;
-  for_rows(R, C, [&](int64_t r0, int64_t c) {
-    float wv[kRowsPerIter][8];
+  const double sgg = sum_partials(partial, np, red);
+  const double gn = __builtin_sqrt(sgg);
+  const double n = gn > eps ? gn : eps;
+  const float c = gn > 0.0 ? (float)(-lr / n) : 0.0f;
+  float f = 1.0f;
+  if constexpr (WITH_W) {
+    const double sww = sum_partials(partial + kHyperballBlocks, np, red);
+    const double swg = sum_partials(partial + 2 * kHyperballBlocks, np, red);
+    const double dd = d, cd = c;
+    double wn2 = dd * dd * sww + 2.0 * dd * cd * swg + cd * cd * sgg;
+    wn2 = wn2 > 0.0 ? wn2 : 0.0;  // (rounding can only push an exactly zero weight below zero)
+    const double wn = __builtin_sqrt(wn2);
+    if (PROJ && wn > 0.0) f = (float)(radius / wn);
+    if (norms && blockIdx.x == 0 && threadIdx.x == 0) norms[1] = (float)wn;
+  }
+  if (norms && blockIdx.x == 0 && threadIdx.x == 0) norms[0] = (float)gn;
+  for_rows(R, C, [&](int64_t r0, int64_t col) {
+    float wv[kRowsPerIter][8], gv[kRowsPerIter][8];
 #pragma unroll
     for (int i = 0; i < kRowsPerIter; ++i)
-      if (r0 + i < R) load8(w + (r0 + i) * ldw + c, wv[i]);
+      if (r0 + i < R) {
+        load8(w + (r0 + i) * ldw + col, wv[i]);
+        load8(g + (r0 + i) * ldg + col, gv[i]);
+      }
 #pragma unroll
     for (int i = 0; i < kRowsPerIter; ++i)
       if (r0 + i < R) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) wv[i][k] = __fmul_rn(wv[i][k], f);
-        store8(w + (r0 + i) * ldw + c, wv[i]);
+        for (int k = 0; k < 8; ++k) {
+          wv[i][k] = __fadd_rn(__fmul_rn(wv[i][k], d), __fmul_rn(gv[i][k], c));
+          if constexpr (PROJ) wv[i][k] = __fmul_rn(wv[i][k], f);
+        }
+        store8(w + (r0 + i) * ldw + col, wv[i]);
       }
   });
+}
+
+template <typename TG, bool WITH_W, bool PROJ>
+hipError_t launch_pair(float* w, int64_t ldw, const TG* g, int64_t ldg, int64_t R, int64_t C, float d, double lr,
+                       double eps, double radius, float* norms, double* partial, int nb, hipStream_t st) {
+  hipLaunchKernelGGL((hyperball_sums_kernel<TG, WITH_W>), dim3(nb), dim3(256), 0, st, (const float*)w, ldw, g, ldg, R,
+                     C, partial);
+  const hipError_t e = hipGetLastError();  // a failed launch stops the call before the update
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((hyperball_update_kernel<TG, WITH_W, PROJ>), dim3(nb), dim3(256), 0, st, w, ldw, g, ldg, R, C, d,
+                     (const double*)partial, nb, lr, eps, radius, norms);
+  return hipGetLastError();
 }
 
 template <typename TG>
 hipError_t launch_t(float* w, int64_t ldw, const void* g, int64_t ldg, int64_t R, int64_t C, double lr, double wd,
                     double eps, double radius, float* norms, void* ws, hipStream_t st) {
   const int nb = hyperball_blocks(R);
-  double* pg = reinterpret_cast<double*>(ws);
-  double* pw = pg + kHyperballBlocks;
-  const float decay = (float)(1.0 - lr * wd);
-  hipLaunchKernelGGL((sumsq_kernel<TG>), dim3(nb), dim3(256), 0, st, (const TG*)g, R, C, ldg, pg);
-  if (radius > 0.0 || norms) {
-    hipLaunchKernelGGL((hyperball_update_kernel<TG, true>), dim3(nb), dim3(256), 0, st, w, ldw, (const TG*)g, ldg, R,
-                       C, decay, (const double*)pg, nb, lr, eps, norms, pw);
-    if (radius > 0.0)
-      hipLaunchKernelGGL(scale_kernel, dim3(nb), dim3(256), 0, st, w, ldw, R, C, (const double*)pw, nb, radius,
-                         norms);
-    else
-      hipLaunchKernelGGL(weight_norm_kernel, dim3(1), dim3(256), 0, st, (const double*)pw, nb, norms);
-  } else {
-    hipLaunchKernelGGL((hyperball_update_kernel<TG, false>), dim3(nb), dim3(256), 0, st, w, ldw, (const TG*)g, ldg,
-                       R, C, decay, (const double*)pg, nb, lr, eps, norms, pw);
-  }
-  return hipGetLastError();
+  double* partial = reinterpret_cast<double*>(ws);
+  const float d = (float)(1.0 - lr * wd);
+  const TG* gt = (const TG*)g;
+  if (radius > 0.0) return launch_pair<TG, true, true>(w, ldw, gt, ldg, R, C, d, lr, eps, radius, norms, partial, nb, st);
+  if (norms) return launch_pair<TG, true, false>(w, ldw, gt, ldg, R, C, d, lr, eps, radius, norms, partial, nb, st);
+  return launch_pair<TG, false, false>(w, ldw, gt, ldg, R, C, d, lr, eps, radius, norms, partial, nb, st);
 }
 
 }  // namespace

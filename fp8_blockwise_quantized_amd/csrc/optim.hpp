@@ -7,9 +7,9 @@
 
 namespace fp8bq {
 
-constexpr int kHyperballBlocks = 1024;  // most blocks of the sweeps (one fp64 partial each)
-// workspace: fp64 partial sums of g and of the new w
-constexpr size_t kHyperballWorkspace = 2 * kHyperballBlocks * sizeof(double);
+constexpr int kHyperballBlocks = 1024;  // most blocks of the sweeps (fp64 partials of each)
+// workspace: per-block fp64 partial sums of g*g, w*w and w*g
+constexpr size_t kHyperballWorkspace = 3 * kHyperballBlocks * sizeof(double);
 
 int hyperball_blocks(int64_t R);
 

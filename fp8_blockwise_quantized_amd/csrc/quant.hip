@@ -685,6 +685,8 @@ static hipError_t launch_tensor_t(const void* x, int64_t R, int64_t C, int64_t l
   const int nb = tensor_amax_blocks(R);
   hipLaunchKernelGGL((tensor_amax_kernel<TIn>), dim3(nb), dim3(256), 0, st, (const TIn*)x, R, C, ldx,
                      (const float*)amax, partial);
+  const hipError_t e = hipGetLastError();  // a failed launch stops the call before its second kernel
+  if (e != hipSuccess) return e;
   const TensorScaleArgs ta{partial, nb, b1, b2, amax, s};
   if (qt) {
     const uint32_t ncg = (uint32_t)(C / kGroup);

@@ -18,11 +18,17 @@
  * - Every tensor pointer is a DEVICE pointer owned by the caller.  The library never frees,
  *   retains or allocates caller memory; callers provide any workspace.
  * - Matrices are row-major.  Sizes and leading dimensions (ld*) are in ELEMENTS.
- * - Each call validates all arguments first; on any error it returns a nonzero fp8bq_status
- *   and enqueues nothing.  On success it enqueues its kernels on `stream` (a hipStream_t;
- *   NULL means the default stream) and returns FP8BQ_OK without synchronizing.  Faults on the
- *   device surface at the caller's next synchronization, as usual for HIP.
- * - Outputs are fully overwritten (no accumulation into existing contents).
+ * - Each call validates all arguments first; on any argument error it returns a nonzero
+ *   fp8bq_status and enqueues nothing.  On success it enqueues its kernels on `stream` (a
+ *   hipStream_t; NULL means the default stream) and returns FP8BQ_OK without synchronizing.  Faults
+ *   on the device surface at the caller's next synchronization, as usual for HIP.  A call that
+ *   launches several kernels checks each launch (hipGetLastError, which also clears the thread's
+ *   last HIP error) and stops at the first that fails, returning FP8BQ_ERR_LAUNCH: the kernels
+ *   launched before it stay enqueued.
+ * - Outputs are fully overwritten, with three documented exceptions that update caller memory in
+ *   place: FP8BQ_OUT_F32_ACCUM (fp8bq_gemm_wgrad adds its result to the FP32 output), the running
+ *   amax of fp8bq_quantize_tensor_delayed[_noalloc] (read and updated), and the weight of
+ *   fp8bq_hyperball_step (read and updated).
  * - Calls are thread-safe and re-entrant; there is no mutable global state besides a per-device
  *   cache of the device's architecture check.  Calls that write overlapping outputs on the same
  *   device must be ordered by the caller (same stream or events).
@@ -356,10 +362,11 @@ int fp8bq_gemm_tensor(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_
  *   norms   NULL, or two device floats (4-byte aligned) that receive ||g||_2 (before the clamp) and
  *           ||w||_F after the update and before the projection.
  *   ws      at least fp8bq_hyperball_workspace_size(R, C) bytes, 16-byte aligned.
- * w may not overlap g, ws or norms (FP8BQ_ERR_OVERLAP).  Two or three sweeps run on `stream` in
- * order: the gradient's sums of squares; the update (each block reduces those to the step
- * coefficient, and sums the new weights' squares when a radius or norms are asked for); then, with a
- * radius, the scaling (each block reduces those to the projection factor).
+ * w may not overlap g, ws or norms (FP8BQ_ERR_OVERLAP).  Two sweeps run on `stream` in order: the
+ * sums of g*g (and, with a radius or norms, of w*w and w*g); then the update, which writes w once:
+ * each block reduces those sums to the step coefficient and, with a radius, to the projection
+ * factor, ||w'||^2 being d^2 sum w^2 + 2 d c sum wg + c^2 sum g^2 for the FP32 factors
+ * d = fp32(1 - lr*wd) and c = fp32(-lr/n) that the update applies.
  */
 size_t fp8bq_hyperball_workspace_size(int64_t R, int64_t C);
 int fp8bq_hyperball_step(float* w, int64_t ldw, const void* g, fp8bq_in gt, int64_t ldg, int64_t R, int64_t C,
