@@ -22,8 +22,13 @@ block's four FP32 master weights from BF16 gradients, and reports GB/s.
 
 Prints ONE JSON line on stdout.  `value` = GEMM FLOPs of the step / wall time of the step (the
 quantize passes are inside the timed step).  `breakdown` holds per-product TFLOP/s and per-pass GB/s
-from HIP events recorded on the launch stream; `roofline` is for the dominant GEMM kernel;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same path (first 4096 tokens).
+from HIP events recorded on the launch stream.  `roofline` is for the GEMM kernel with the most time
+per step, with `by_kind` entries for fprop, dgrad, wgrad (each against the FP8 peak) and the quantize
+passes (against HBM, beside the same run's plain-copy bandwidth).  After the timed steps, `configs`
+times the other workloads: the single 8192 x 8192 x 2048 linear, the token sweep K = N = 2048 with its
+knee, and the heavy-tailed gradients (dgrad / wgrad with dY in E5M2 and E4M3, and their quantization
+error).  `cpu_baseline` times the CPU oracle on a bounded sample of the same path (first 4096 tokens)
+and, per workload and operation, quantize GB/s and GEMM GFLOP/s on samples.
 """
 
 import argparse
@@ -53,6 +58,8 @@ def parse():
     p.add_argument("--workload", choices=["decoder", "delayed", "hyperball", "linear", "sweep", "qerror"],
                    default="decoder")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the single-linear, token-sweep and heavy-tailed workloads after the decoder step")
     p.add_argument("--cpu-tokens", type=int, default=4096)
     p.add_argument("--calibrate", action="store_true",
                    help="first run one plain elementwise kernel over 256 MiB in / 256 MiB out, so a "
@@ -135,7 +142,8 @@ def main():
 
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     breakdown = summarize(ops, dur_ms, np.median(per, axis=0), per.min(axis=0))
-    roof = roofline(fq, ops, dur_ms, with_traffic=args.workload == "decoder")
+    copy_gbs = copy_ceiling(torch, dev) if args.workload == "decoder" else None
+    roof = roofline(fq, ops, dur_ms, with_traffic=args.workload == "decoder", copy_gbs=copy_gbs)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -158,6 +166,8 @@ def main():
         "cpu_baseline": None,
     }
     del bufs
+    if args.workload == "decoder" and not args.no_configs:
+        out["configs"] = run_configs(torch, fq, synth, dev, steps=min(args.steps, 20))
     if not args.no_cpu_baseline and args.workload == "decoder":
         out["cpu_baseline"] = cpu_baseline(args.cpu_tokens, desc)
     print(json.dumps(out), flush=True)
@@ -212,20 +222,20 @@ def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True, weight_jobs=N
         qwt = torch.empty((K, N), dtype=torch.uint8, device=dev)
         bufs += [qxt, sxt, qwt]
         quant_x = dict(name=f"{name}.quant_x_dual", kind="quant_dual", bytes=_qdual_bytes(M, K), flops=0,
-                       fn=lambda: fq.fp8bq_quantize_act_dual(X, E4, qx, sx, E4, qxt, sxt))
+                       fn=fq.prepare(fq.fp8bq_quantize_act_dual, X, E4, qx, sx, E4, qxt, sxt))
         quant_w = dict(name=f"{name}.quant_w_dual", kind="quant_w_dual", bytes=_qw_bytes(N, K) + N * K, flops=0,
-                       fn=lambda: fq.fp8bq_quantize_weight_dual(W, E4, qw, sw, qwt))
+                       fn=fq.prepare(fq.fp8bq_quantize_weight_dual, W, E4, qw, sw, qwt))
     else:
         quant_x = dict(name=f"{name}.quant_x_1x128", kind="quant_1x128", bytes=_q1x128_bytes(M, K), flops=0,
-                       fn=lambda: fq.fp8bq_quantize_act_1x128(X, E4, qx, sx))
+                       fn=fq.prepare(fq.fp8bq_quantize_act_1x128, X, E4, qx, sx))
         quant_w = dict(name=f"{name}.quant_w_128x128", kind="quant_128x128", bytes=_qw_bytes(N, K), flops=0,
-                       fn=lambda: fq.fp8bq_quantize_weight_128x128(W, E4, qw, sw))
+                       fn=fq.prepare(fq.fp8bq_quantize_weight_128x128, W, E4, qw, sw))
     if weight_jobs is not None and with_backward:
         weight_jobs.append((W, qw, sw, qwt))
         quant_w = None
     ops = [op for op in (quant_x, quant_w) if op is not None] + [
         dict(name=f"{name}.fprop", kind="fprop", bytes=0, flops=2 * M * N * K, plan=(fq.OP_FPROP, M, N, K), kid=(0, 0),
-             fn=lambda: fq.fp8bq_gemm_fprop(qx, sx, E4, qw, sw, E4, y, ws_f)),
+             fn=fq.prepare(fq.fp8bq_gemm_fprop, qx, sx, E4, qw, sw, E4, y, ws_f)),
     ]
     if with_backward:
         qdy, sdy = _alloc_1x128(torch, M, N, dev)
@@ -236,11 +246,11 @@ def linear_ops(torch, fq, name, X, W, dY, dev, with_backward=True, weight_jobs=N
         ws_w = fq._workspace(fq.OP_WGRAD, M, N, K, dev)
         ops += [
             dict(name=f"{name}.quant_dy_dual", kind="quant_dual", bytes=_qdual_bytes(M, N), flops=0,
-                 fn=lambda: fq.fp8bq_quantize_act_dual(dY, E4, qdy, sdy, E4, qdyt, sdyt)),
+                 fn=fq.prepare(fq.fp8bq_quantize_act_dual, dY, E4, qdy, sdy, E4, qdyt, sdyt)),
             dict(name=f"{name}.dgrad", kind="dgrad", bytes=0, flops=2 * M * N * K, plan=(fq.OP_DGRAD_WT, M, N, K),
-                 kid=(1, 0), fn=lambda: fq.fp8bq_gemm_dgrad_wt(qdy, sdy, E4, qwt, sw, E4, dx, ws_d)),
+                 kid=(1, 0), fn=fq.prepare(fq.fp8bq_gemm_dgrad_wt, qdy, sdy, E4, qwt, sw, E4, dx, ws_d)),
             dict(name=f"{name}.wgrad", kind="wgrad", bytes=0, flops=2 * M * N * K, plan=(fq.OP_WGRAD, M, N, K),
-                 kid=(2, 1), fn=lambda: fq.fp8bq_gemm_wgrad(qdyt, sdyt, E4, qxt, sxt, E4, dw, ws_w)),
+                 kid=(2, 1), fn=fq.prepare(fq.fp8bq_gemm_wgrad, qdyt, sdyt, E4, qxt, sxt, E4, dw, ws_w)),
         ]
         bufs += [qdy, sdy, dx, qdyt, sdyt, dw, ws_d, ws_w]
     return ops, bufs
@@ -258,7 +268,7 @@ def build_decoder(torch, fq, synth, dev):
     # all four weights are known when the step starts: one launch quantizes them (codes, scales, W^T codes)
     wbytes = sum(_qw_bytes(*w.shape) + w.numel() for w, _, _, _ in wjobs)
     ops.insert(0, dict(name="weights.quant_w_dual", kind="quant_w_dual", bytes=wbytes, flops=0,
-                       fn=lambda: fq.fp8bq_quantize_weights_dual(wjobs, fq.E4M3)))
+                       fn=fq.prepare(fq.fp8bq_quantize_weights_dual, wjobs, fq.E4M3)))
     desc = {
         "workload": "decoder block fprop+dgrad+wgrad, M=16384 tokens, hidden 2048, GQA 16q/2kv x128 "
                     "(QKV 2048->2560, O 2048->2048), SwiGLU gate+up 2048->11264, down 5632->2048; "
@@ -299,17 +309,17 @@ def delayed_linear_ops(torch, fq, name, X, W, dY, dev):
     ws_w = fq._workspace(fq.OP_TENSOR, N, K, M, dev)
     ops = [
         dict(name=f"{name}.quant_x_tensor", kind="quant_tensor", bytes=_qtensor_bytes(M, K, True), flops=0,
-             fn=lambda: fq.fp8bq_quantize_tensor_delayed(X, E4, ax, 0.99, qx, qxt, sx, wsq)),
+             fn=fq.prepare(fq.fp8bq_quantize_tensor_delayed, X, E4, ax, 0.99, qx, qxt, sx, wsq)),
         dict(name=f"{name}.quant_w_tensor", kind="quant_tensor", bytes=_qtensor_bytes(N, K, True), flops=0,
-             fn=lambda: fq.fp8bq_quantize_tensor_delayed(W, E4, aw, 0.99, qw, qwt, sw, wsq)),
+             fn=fq.prepare(fq.fp8bq_quantize_tensor_delayed, W, E4, aw, 0.99, qw, qwt, sw, wsq)),
         dict(name=f"{name}.fprop", kind="fprop", bytes=0, flops=2 * M * N * K, plan=(fq.OP_TENSOR, M, N, K),
-             kid=(0, 0), fn=lambda: fq.fp8bq_gemm_tensor(qx, sx, E4, qw, sw, E4, y, ws_f)),
+             kid=(0, 0), fn=fq.prepare(fq.fp8bq_gemm_tensor, qx, sx, E4, qw, sw, E4, y, ws_f)),
         dict(name=f"{name}.quant_dy_tensor", kind="quant_tensor", bytes=_qtensor_bytes(M, N, True), flops=0,
-             fn=lambda: fq.fp8bq_quantize_tensor_delayed(dY, E4, ady, 0.99, qdy, qdyt, sdy, wsq)),
+             fn=fq.prepare(fq.fp8bq_quantize_tensor_delayed, dY, E4, ady, 0.99, qdy, qdyt, sdy, wsq)),
         dict(name=f"{name}.dgrad", kind="dgrad", bytes=0, flops=2 * M * N * K, plan=(fq.OP_TENSOR, M, K, N),
-             kid=(0, 0), fn=lambda: fq.fp8bq_gemm_tensor(qdy, sdy, E4, qwt, sw, E4, dx, ws_d)),
+             kid=(0, 0), fn=fq.prepare(fq.fp8bq_gemm_tensor, qdy, sdy, E4, qwt, sw, E4, dx, ws_d)),
         dict(name=f"{name}.wgrad", kind="wgrad", bytes=0, flops=2 * M * N * K, plan=(fq.OP_TENSOR, N, K, M),
-             kid=(0, 0), fn=lambda: fq.fp8bq_gemm_tensor(qdyt, sdy, E4, qxt, sx, E4, dw, ws_w)),
+             kid=(0, 0), fn=fq.prepare(fq.fp8bq_gemm_tensor, qdyt, sdy, E4, qxt, sx, E4, dw, ws_w)),
     ]
     bufs = [qx, qxt, qw, qwt, qdy, qdyt, ax, aw, ady, sx, sw, sdy, wsq, y, dx, dw, ws_f, ws_d, ws_w]
     return ops, bufs
@@ -351,9 +361,12 @@ def run_hyperball(args, torch, fq, synth, dev):
         ws = torch.empty(fq.fp8bq_hyperball_workspace_size(N, K), dtype=torch.uint8, device=dev)
         items.append((name, w, g, radius, norms, ws, 16 * N * K))
 
+    calls = [fq.prepare(fq.fp8bq_hyperball_step, w, g, 1e-4, 0.1, 1e-8, radius, norms, ws)
+             for _, w, g, radius, norms, ws, _ in items]
+
     def step():
-        for _, w, g, radius, norms, ws, _ in items:
-            fq.fp8bq_hyperball_step(w, g, 1e-4, 0.1, 1e-8, radius, norms, ws)
+        for c in calls:
+            c()
 
     for _ in range(args.warmup):
         step()
@@ -367,11 +380,11 @@ def run_hyperball(args, torch, fq, synth, dev):
     gbs = total / (ms * 1e-3) / 1e9
     stream = torch.cuda.current_stream(dev)
     per = []
-    for name, w, g, radius, norms, ws, nbytes in items:
+    for (name, w, g, radius, norms, ws, nbytes), call in zip(items, calls):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
-            fq.fp8bq_hyperball_step(w, g, 1e-4, 0.1, 1e-8, radius, norms, ws)
+            call()
         e1.record(stream)
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / args.steps
@@ -385,13 +398,97 @@ def run_hyperball(args, torch, fq, synth, dev):
                       "per_weight": per}), flush=True)
 
 
-def run_qerror(torch, fq, synth, dev):
-    """Quantization error of the heavy-tailed gradient workload (dY Student-t(3) * 1e-3 [16384, 5632],
-    X [16384, 2048] with outlier columns, W [5632, 2048]): relative Frobenius error of the FP8 dgrad
-    (dY . W) and wgrad (dY^T . X) against float64 products of the unquantized BF16 inputs, for dY in
-    E5M2 and in E4M3 (X and W in E4M3), on 256 sampled rows of dX and 128 x 128 sampled entries of dW."""
+def time_calls(torch, fns, steps, warmup=3):
+    """Mean ms per call of each function, HIP events around every call on the launch stream."""
     import numpy as np
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(steps)]
+    for k in range(steps):
+        for (e0, e1), f in zip(ev[k], fns):
+            e0.record(stream)
+            f()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    return [float(np.mean([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(steps)])) for i in range(len(fns))]
+
+
+def _rate(flops_or_bytes, ms, scale):
+    return round(flops_or_bytes / (ms * 1e-3) / scale, 1)
+
+
+def run_configs(torch, fq, synth, dev, steps):
+    """The other workloads, timed after the decoder step (not part of `value`):
+    single_linear  X[8192, 2048] (outlier columns) and W[8192, 2048]: quantize X 1x128, W 128x128, fprop;
+    token_sweep    fprop with K = N = 2048 for M = 512 .. 32768 (TFLOP/s against M, and the knee: the
+                   smallest M within 10% of the best rate);
+    heavy_tailed   dY[16384, 5632] Student-t(3) * 1e-3, X[16384, 2048], W[5632, 2048]: dgrad and wgrad with
+                   dY in E5M2 and in E4M3, and the quantization-error report of each."""
+    E4, E5 = fq.E4M3, fq.E5M2
+    out = {}
+    log("configs: single linear ...")
+    c = synth.single_linear()
+    X, W = c["X"].to(dev), c["W"].to(dev)
+    ops, bufs = linear_ops(torch, fq, "linear", X, W, None, dev, with_backward=False)
+    ms = time_calls(torch, [o["fn"] for o in ops], steps)
+    out["single_linear"] = {
+        "workload": "X[8192, 2048] BF16 N(0,1), 1% outlier columns x50; W[8192, 2048] N(0,0.02); E4M3",
+        "fprop_tflops": _rate(ops[2]["flops"], ms[2], 1e12), "fprop_ms": round(ms[2], 5),
+        "fprop_pct_fp8_peak": round(100 * ops[2]["flops"] / (ms[2] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 1),
+        "quant_x_1x128_gbs": _rate(ops[0]["bytes"], ms[0], 1e9), "quant_w_128x128_gbs": _rate(ops[1]["bytes"], ms[1], 1e9),
+        "plan": list(fq.fp8bq_gemm_plan(fq.OP_FPROP, 8192, 8192, 2048)),
+    }
+    del ops, bufs, X, W, c
+
+    log("configs: token sweep ...")
+    Wd = synth.sweep_weight().to(dev)
+    pts = []
+    for M in synth.SWEEP_M:
+        Xd = synth.sweep_x(M).to(dev)
+        ops, bufs = linear_ops(torch, fq, f"M{M}", Xd, Wd, None, dev, with_backward=False)
+        ms = time_calls(torch, [ops[2]["fn"]], max(steps, 20))[0]
+        pts.append({"M": M, "us": round(1e3 * ms, 2), "tflops": _rate(ops[2]["flops"], ms, 1e12),
+                    "plan": list(fq.fp8bq_gemm_plan(fq.OP_FPROP, M, 2048, 2048))})
+        del ops, bufs, Xd
+    best = max(p["tflops"] for p in pts)
+    out["token_sweep"] = {"workload": "fprop, K = N = 2048, X[M, 2048] N(0,1), W N(0,0.02)", "points": pts,
+                          "knee_M": next(p["M"] for p in pts if p["tflops"] >= 0.9 * best)}
+    del Wd
+
+    log("configs: heavy-tailed gradients ...")
     c = synth.heavy_tailed()
+    dY, X, W = c["dY"].to(dev), c["X"].to(dev), c["W"].to(dev)
+    M, N, K = dY.shape[0], dY.shape[1], X.shape[1]
+    qw, sw, qwt = fq.quantize_weight_dual(W, E4)
+    qxt, sxt = fq.quantize_act_128x1(X, E4)
+    res = {"workload": "dY[16384, 5632] Student-t(3) * 1e-3, X[16384, 2048] (outlier columns), W[5632, 2048]; "
+                       "X and W in E4M3"}
+    fl = 2 * M * N * K
+    for name, fmt in (("e5m2", E5), ("e4m3", E4)):
+        q, sq, qt, sqt = fq.quantize_act_dual(dY, fmt, fmt)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        wsd = fq._workspace(fq.OP_DGRAD_WT, M, N, K, dev)
+        wsw = fq._workspace(fq.OP_WGRAD, M, N, K, dev)
+        ms = time_calls(torch, [fq.prepare(fq.fp8bq_gemm_dgrad_wt, q, sq, fmt, qwt, sw, E4, dx, wsd),
+                                fq.prepare(fq.fp8bq_gemm_wgrad, qt, sqt, fmt, qxt, sxt, E4, dw, wsw)], steps)
+        res[f"dy_{name}"] = {"dgrad_tflops": _rate(fl, ms[0], 1e12), "wgrad_tflops": _rate(fl, ms[1], 1e12),
+                             "dgrad_ms": round(ms[0], 5), "wgrad_ms": round(ms[1], 5)}
+        del q, sq, qt, sqt, dx, dw, wsd, wsw
+    res["quantization_error"] = qerror_report(torch, fq, c, dev)
+    out["heavy_tailed"] = res
+    return out
+
+
+def qerror_report(torch, fq, c, dev):
+    """Relative Frobenius error of the FP8 dgrad and wgrad (FP32 out) against float64 products of
+    the unquantized BF16 inputs, dY in E5M2 and in E4M3 (X, W in E4M3), on 256 sampled rows of dX and
+    128 x 128 sampled entries of dW.  Reported, not graded: the pages give no expected value."""
+    import numpy as np
     dY, X, W = c["dY"], c["X"], c["W"]
     rng = np.random.default_rng(11)
     rows = np.sort(rng.choice(dY.shape[0], 256, replace=False))
@@ -413,7 +510,14 @@ def run_qerror(torch, fq, synth, dev):
         got_dx = dx[torch.from_numpy(rows).to(dev)].double().cpu().numpy()
         got_dw = dw.double().cpu().numpy()[np.ix_(ncols, kcols)]
         out[name] = {"dgrad_rel_frobenius": rel(got_dx, ref_dx), "wgrad_rel_frobenius": rel(got_dw, ref_dw)}
-        log(name, out[name])
+    return out
+
+
+def run_qerror(torch, fq, synth, dev):
+    """The quantization-error report of the heavy-tailed gradient workload alone (see qerror_report)."""
+    out = qerror_report(torch, fq, synth.heavy_tailed(), dev)
+    for name, r in out.items():
+        log(name, r)
     print(json.dumps({"report": "quantization error, heavy-tailed gradients (dY Student-t(3) * 1e-3), "
                                 "FP8 GEMM (FP32 out) vs float64 of the unquantized BF16 inputs",
                       "dy_format": out, "x_w_format": "e4m3",
@@ -492,9 +596,9 @@ def summarize(ops, dur_ms, med_ms=None, min_ms=None):
 _TILE_ARGS = {(128, 128): "128, 128, 2, 2, 2", (128, 256): "128, 256, 2, 4, 2", (256, 128): "256, 128, 4, 2, 2",
               (256, 256): "256, 256, 2, 4, 2"}
 def gemm_kernel(fq, o):
-    """(kernel name, isolated) of a GEMM op: o["plan"] is its plan query (op, M, N, K) and o["kid"]
+    """(kernel name, isolated) of a GEMM call: o["plan"] is its plan query (op, M, N, K) and o["kid"]
     the kernel's (OP, scale mode) template arguments.  Isolated when the call launches that one kernel
-    (a split contraction adds a reduction pass)."""
+    (a split contraction adds a reduction pass after it)."""
     tm, tn, split = fq.fp8bq_gemm_plan(*o["plan"])
     kop, sbm = o["kid"]
     name = (f"void fp8bq::gemm_tn_kernel<{kop}, {_TILE_ARGS[(tm, tn)]}, {sbm}, "
@@ -519,21 +623,26 @@ def _traffic(kernel):
         return None
 
 
-def roofline(fq, ops, dur_ms, with_traffic=True):
-    """The dominant GEMM kernel among those whose every launch in the step is that kernel alone, by
-    FLOPs per step (the first in step order on a tie, so the choice does not depend on timing noise):
-    achieved = its algorithmic FLOPs per launch / its mean launch duration (HIP events on the launch
-    stream, one pair per call), over all of its launches in the step."""
+def roofline(fq, ops, dur_ms, with_traffic=True, copy_gbs=None):
+    """The dominant GEMM kernel and one entry per product kind.
+
+    Dominant kernel: the kernel symbol with the most time per step over the calls that launch it
+    alone (a split contraction adds a reduction pass to a call, so such calls are left out of the
+    symbol's figures); achieved = its algorithmic FLOPs per launch / its mean launch duration (HIP
+    events on the launch stream, one pair per call).
+
+    by_kind: fprop, dgrad and wgrad each as a whole (every call of that kind, reduction passes
+    included: what the product costs the step), and the quantize passes against HBM (algorithmic
+    bytes), with the same run's plain-copy bandwidth beside them when measured."""
     groups = {}
     for o, d in zip(ops, dur_ms):
         if not o["flops"]:
             continue
         name, isolated = gemm_kernel(fq, o)
-        g = groups.setdefault(name, {"ok": True, "sel": []})
-        g["ok"] &= isolated
-        g["sel"].append((o, float(d)))
-    eligible = [(sum(o["flops"] for o, _ in g["sel"]), -i, name, g["sel"])
-                for i, (name, g) in enumerate(groups.items()) if g["ok"]]
+        g = groups.setdefault(name, [])
+        if isolated:
+            g.append((o, float(d)))
+    eligible = [(sum(d for _, d in sel), -i, name, sel) for i, (name, sel) in enumerate(groups.items()) if sel]
     if not eligible:
         return None
     _, _, name, sel = max(eligible, key=lambda e: (e[0], e[1]))
@@ -541,6 +650,25 @@ def roofline(fq, ops, dur_ms, with_traffic=True):
     flops_per_launch = sum(o["flops"] for o, _ in sel) / len(sel)
     ms_per_launch = t / len(sel)
     achieved = flops_per_launch / (ms_per_launch * 1e-3) / 1e12
+    by_kind = {}
+    for kind in ("fprop", "dgrad", "wgrad"):
+        sel_k = [(o, float(d)) for o, d in zip(ops, dur_ms) if o["kind"] == kind]
+        if not sel_k:
+            continue
+        tk = sum(d for _, d in sel_k)
+        ak = sum(o["flops"] for o, _ in sel_k) / (tk * 1e-3) / 1e12
+        split = [o["name"] for o, _ in sel_k if not gemm_kernel(fq, o)[1]]
+        by_kind[kind] = {"bound": "mfma", "achieved": round(ak, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ak / FP8_PEAK_TFLOPS, 4), "ms_per_step": round(tk, 4),
+                         "launches": len(sel_k), "with_reduction_pass": split}
+    q = [(o, float(d)) for o, d in zip(ops, dur_ms) if o["bytes"]]
+    if q:
+        tq = sum(d for _, d in q)
+        gq = sum(o["bytes"] for o, _ in q) / (tq * 1e-3) / 1e9
+        by_kind["quantize"] = {"bound": "hbm", "achieved": round(gq, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(gq / HBM_PEAK_GBS, 4), "ms_per_step": round(tq, 4), "launches": len(q)}
+        if copy_gbs:
+            by_kind["quantize"].update(copy_gbs=round(copy_gbs, 1), frac_of_copy=round(gq / copy_gbs, 4))
     return {
         "bound": "mfma",
         "kernel": name,
@@ -549,11 +677,32 @@ def roofline(fq, ops, dur_ms, with_traffic=True):
         "unit": "TFLOP/s",
         "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
         "traffic": _traffic(name) if with_traffic else None,
+        "selection": "kernel with the most time per step over calls that launch it alone",
         "launches_per_step": len(sel),
         "launches": [o["name"] for o, _ in sel],
         "flops_per_launch": flops_per_launch,
         "mean_launch_ms": round(ms_per_launch, 5),
+        "by_kind": by_kind,
     }
+
+
+def copy_ceiling(torch, dev, mib=1024, reps=10):
+    """GB/s of a plain device copy of `mib` MiB (bytes read + written), timed with HIP events: the
+    bandwidth a streaming kernel can expect on this machine, beside the 8 TB/s peak."""
+    a = torch.empty(mib << 18, dtype=torch.float32, device=dev)
+    a.fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
 # -----------------------------------------------------------------------------------------------
@@ -592,6 +741,7 @@ def cpu_baseline(tokens, desc):
         t_total += time.perf_counter() - t0
         flops += 3 * 2 * tokens * N * K
         log(f"cpu oracle {name}: {t_total:.1f} s so far")
+    per_config = cpu_per_config()
     return {
         "value": round(flops / t_total / 1e12, 6),
         "unit": "TFLOP/s",
@@ -605,7 +755,75 @@ def cpu_baseline(tokens, desc):
         "cpu_model": _cpu_model(),
         "cpu_count": os.cpu_count(),
         "affinity": len(os.sched_getaffinity(0)),
+        "per_config": per_config,
     }
+
+
+def cpu_per_config():
+    """The oracle per workload and operation on bounded samples: quantize GB/s (vectorized NumPy, one
+    core; algorithmic bytes as on the GPU) and GEMM GFLOP/s (float64 BLAS on all the process's threads,
+    BF16 rounding included)."""
+    import numpy as np
+
+    import oracle
+    import synth
+    E4, E5 = oracle.E4M3, oracle.E5M2
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    def qrate(nbytes, sec):
+        return {"gbs": round(nbytes / sec / 1e9, 4), "seconds": round(sec, 3)}
+
+    def grate(fl, sec):
+        return {"gflops": round(fl / sec / 1e9, 2), "seconds": round(sec, 3)}
+
+    out = {}
+    # tiny check (whole workload; FP32 inputs: 4 B in + 1 B code + scales)
+    c = synth.tiny_check()
+    A, W, dY = c["A"].numpy(), c["W"].numpy(), c["dY"].numpy()
+    (qa, sa), t1 = timed(lambda: oracle.quant_act_1x128(A, E4))
+    (qw, sw), t2 = timed(lambda: oracle.quant_weight_128x128(W, E4))
+    _, t3 = timed(lambda: oracle.to_bf16_rne(oracle.gemm_fprop(qa, sa, E4, qw, sw, E4)))
+    out["tiny_check"] = {"sample": "whole workload (256 x 256 x 256)",
+                         "quant_1x128": qrate(A.size * 5 + A.size // 128 * 4, t1),
+                         "quant_128x128": qrate(W.size * 5 + 16, t2), "fprop": grate(2 * 256 ** 3, t3)}
+    # single linear: 512 rows of X, 256 rows of W for the quantizers; 512 rows of Y for the GEMM
+    c = synth.single_linear()
+    X, Wl = c["X"][:512].float().numpy(), c["W"].float().numpy()
+    (qx, sx), t1 = timed(lambda: oracle.quant_act_1x128(X, E4))
+    (qw, sw), t2 = timed(lambda: oracle.quant_weight_128x128(Wl, E4))
+    _, t3 = timed(lambda: oracle.to_bf16_rne(oracle.gemm_fprop(qx, sx, E4, qw, sw, E4)))
+    out["single_linear"] = {"sample": "X rows 0..511 (Y[512, 8192]); all of W",
+                            "quant_1x128": qrate(X.size * 3 + X.size // 128 * 4, t1),
+                            "quant_128x128": qrate(Wl.size * 3 + Wl.size // 16384 * 4, t2),
+                            "fprop": grate(2 * 512 * 8192 * 2048, t3)}
+    # token sweep at its smallest M (whole)
+    Ws, Xs = synth.sweep_weight().float().numpy(), synth.sweep_x(512).float().numpy()
+    (qx, sx), t1 = timed(lambda: oracle.quant_act_1x128(Xs, E4))
+    qw, sw = oracle.quant_weight_128x128(Ws, E4)
+    _, t3 = timed(lambda: oracle.to_bf16_rne(oracle.gemm_fprop(qx, sx, E4, qw, sw, E4)))
+    out["token_sweep_M512"] = {"sample": "whole workload at M = 512",
+                               "quant_1x128": qrate(Xs.size * 3 + Xs.size // 128 * 4, t1),
+                               "fprop": grate(2 * 512 * 2048 * 2048, t3)}
+    # heavy-tailed gradients: the first 512 tokens
+    c = synth.heavy_tailed()
+    dYh, Xh, Wh = c["dY"][:512].float().numpy(), c["X"][:512].float().numpy(), c["W"].float().numpy()
+    (qd, sd), t1 = timed(lambda: oracle.quant_act_1x128(dYh, E5))
+    (qdt, sdt), t2 = timed(lambda: oracle.quant_act_128x1(dYh, E5))
+    qxt, sxt = oracle.quant_act_128x1(Xh, E4)
+    qw, sw = oracle.quant_weight_128x128(Wh, E4)
+    _, t3 = timed(lambda: oracle.to_bf16_rne(oracle.gemm_dgrad(qd, sd, E5, qw, sw, E4)))
+    _, t4 = timed(lambda: oracle.to_bf16_rne(oracle.gemm_wgrad(qdt, sdt, E5, qxt, sxt, E4)))
+    fl = 2 * 512 * 5632 * 2048
+    out["heavy_tailed"] = {"sample": "tokens 0..511, dY in E5M2",
+                           "quant_1x128_e5m2": qrate(dYh.size * 3 + dYh.size // 128 * 4, t1),
+                           "quant_128x1_e5m2": qrate(dYh.size * 3 + dYh.size // 128 * 4, t2),
+                           "dgrad": grate(fl, t3), "wgrad": grate(fl, t4)}
+    log(f"cpu oracle per workload done")
+    return out
 
 
 def _cpu_model():

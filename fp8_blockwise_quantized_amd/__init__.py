@@ -198,8 +198,8 @@ def _expect_all(checks, ws=None):
             raise TypeError(f"{name} must be a torch tensor")
         if t.dtype not in dtypes:
             raise TypeError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
-        if tuple(t.shape) != tuple(int(v) for v in shape):
-            raise ValueError(f"{name} must have shape {tuple(int(v) for v in shape)}, not {tuple(t.shape)}")
+        if t.shape != shape:
+            raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
     device = checks[0][0].device
     if device.type != "cuda":
         raise ValueError(f"{checks[0][1]} must be on a CUDA (HIP) device, not {device}")
@@ -219,37 +219,76 @@ def _expect_all(checks, ws=None):
 # raw entry points
 # ---------------------------------------------------------------------------------------------
 
+_MARSHAL = {}
+
+
+def _entry(marshal):
+    """Make an entry point from a function that validates its tensors and returns the C call's
+    argument tuple: calling the entry point marshals and launches; prepare() keeps the marshalled
+    arguments for repeated launches."""
+    name = marshal.__name__
+    _MARSHAL[name] = marshal
+
+    def call(*args, **kwargs):
+        _check(getattr(lib(), name)(*marshal(*args, **kwargs)), name)
+
+    call.__name__ = name
+    call.__qualname__ = name
+    call.__doc__ = marshal.__doc__
+    return call
+
+
+def prepare(fn, *args, **kwargs):
+    """Validate and marshal the arguments of raw entry point `fn` once and return a function that
+    launches `fn` with them (on the stream current at preparation): the repeated calls of a training
+    or serving loop then cost one C call each.  The tensors must stay alive and keep their storage."""
+    name = fn.__name__
+    cargs = _MARSHAL[name](*args, **kwargs)
+    cfn = getattr(lib(), name)
+
+    def launch():
+        st = cfn(*cargs)
+        if st != 0:
+            raise Fp8bqError(st, name)
+
+    return launch
+
+
+@_entry
 def fp8bq_quantize_act_1x128(x, fmt, q, s):
     R, C = x.shape
     _expect_all([(x, "x", (R, C), _HI), (q, "q", (R, C), _U8), (s, "s", (C // 128, R), _F32)])
-    _check(lib().fp8bq_quantize_act_1x128(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(q), _ld(q), _ptr(s), _ld(s),
-                                          _stream(x)), "fp8bq_quantize_act_1x128")
+    return (_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(q), _ld(q), _ptr(s), _ld(s),
+            _stream(x))
 
 
+@_entry
 def fp8bq_quantize_act_128x1(x, fmt, qt, st):
     R, C = x.shape
     _expect_all([(x, "x", (R, C), _HI), (qt, "qt", (C, R), _U8), (st, "st", (R // 128, C), _F32)])
-    _check(lib().fp8bq_quantize_act_128x1(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(qt), _ld(qt), _ptr(st),
-                                          _ld(st), _stream(x)), "fp8bq_quantize_act_128x1")
+    return (_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(qt), _ld(qt), _ptr(st),
+            _ld(st), _stream(x))
 
 
+@_entry
 def fp8bq_quantize_act_dual(x, fmt_rows, q, s, fmt_cols, qt, st):
     R, C = x.shape
     _expect_all([(x, "x", (R, C), _HI), (q, "q", (R, C), _U8), (s, "s", (C // 128, R), _F32),
                  (qt, "qt", (C, R), _U8), (st, "st", (R // 128, C), _F32)])
-    _check(lib().fp8bq_quantize_act_dual(_ptr(x), _in_type(x), R, C, _ld(x), fmt_rows, _ptr(q), _ld(q), _ptr(s),
-                                         _ld(s), fmt_cols, _ptr(qt), _ld(qt), _ptr(st), _ld(st), _stream(x)),
-           "fp8bq_quantize_act_dual")
+    return (_ptr(x), _in_type(x), R, C, _ld(x), fmt_rows, _ptr(q), _ld(q), _ptr(s),
+            _ld(s), fmt_cols, _ptr(qt), _ld(qt), _ptr(st), _ld(st), _stream(x))
 
 
+@_entry
 def fp8bq_quantize_weight_dual(w, fmt, q, s, qt):
     N, K = w.shape
     _expect_all([(w, "w", (N, K), _HI), (q, "q", (N, K), _U8),
                  (s, "s", (N // 128, K // 128), _F32), (qt, "qt", (K, N), _U8)])
-    _check(lib().fp8bq_quantize_weight_dual(_ptr(w), _in_type(w), N, K, _ld(w), fmt, _ptr(q), _ld(q), _ptr(s), _ld(s),
-                                            _ptr(qt), _ld(qt), _stream(w)), "fp8bq_quantize_weight_dual")
+    return (_ptr(w), _in_type(w), N, K, _ld(w), fmt, _ptr(q), _ld(q), _ptr(s), _ld(s),
+            _ptr(qt), _ld(qt), _stream(w))
 
 
+@_entry
 def fp8bq_quantize_weights_dual(jobs, fmt):
     """jobs: (w, q, s, qt) per weight, as fp8bq_quantize_weight_dual takes them; every w of one dtype.
     One launch on the current stream of the first weight's device."""
@@ -266,15 +305,16 @@ def fp8bq_quantize_weights_dual(jobs, fmt):
         arr[i] = WeightJob(w.data_ptr(), N, K, _ld(w), q.data_ptr(), _ld(q), s.data_ptr(), _ld(s), qt.data_ptr(),
                            _ld(qt))
     stream = _stream(jobs[0][0]) if jobs else ctypes.c_void_p(0)
-    _check(lib().fp8bq_quantize_weights_dual(arr, len(jobs), wt, fmt, stream), "fp8bq_quantize_weights_dual")
+    return (arr, len(jobs), wt, fmt, stream)
 
 
+@_entry
 def fp8bq_quantize_weight_128x128(w, fmt, q, s):
     N, K = w.shape
     _expect_all([(w, "w", (N, K), _HI), (q, "q", (N, K), _U8),
                  (s, "s", (N // 128, K // 128), _F32)])
-    _check(lib().fp8bq_quantize_weight_128x128(_ptr(w), _in_type(w), N, K, _ld(w), fmt, _ptr(q), _ld(q), _ptr(s),
-                                               _ld(s), _stream(w)), "fp8bq_quantize_weight_128x128")
+    return (_ptr(w), _in_type(w), N, K, _ld(w), fmt, _ptr(q), _ld(q), _ptr(s),
+            _ld(s), _stream(w))
 
 
 def fp8bq_gemm_workspace_size(op, M, N, K):
@@ -295,39 +335,40 @@ def _ws_args(ws):
     return _ptr(ws), ws.numel() * ws.element_size()
 
 
+@_entry
 def fp8bq_gemm_fprop(qx, sx, fx, qw, sw, fw, y, ws=None):
     M, K = qx.shape
     N = qw.shape[0]
     _expect_all([(qx, "qx", (M, K), _U8), (sx, "sx", (K // 128, M), _F32), (qw, "qw", (N, K), _U8),
                  (sw, "sw", (N // 128, K // 128), _F32), (y, "y", (M, N), _HI)], ws)
     wsp, wsb = _ws_args(ws)
-    _check(lib().fp8bq_gemm_fprop(M, N, K, _ptr(qx), _ld(qx), _ptr(sx), _ld(sx), fx, _ptr(qw), _ld(qw), _ptr(sw),
-                                  _ld(sw), fw, _ptr(y), _out_type(y), _ld(y), wsp, wsb, _stream(y)),
-           "fp8bq_gemm_fprop")
+    return (M, N, K, _ptr(qx), _ld(qx), _ptr(sx), _ld(sx), fx, _ptr(qw), _ld(qw), _ptr(sw),
+            _ld(sw), fw, _ptr(y), _out_type(y), _ld(y), wsp, wsb, _stream(y))
 
 
+@_entry
 def fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws=None):
     M, N = qdy.shape
     K = qw.shape[1]
     _expect_all([(qdy, "qdy", (M, N), _U8), (sdy, "sdy", (N // 128, M), _F32), (qw, "qw", (N, K), _U8),
                  (sw, "sw", (N // 128, K // 128), _F32), (dx, "dx", (M, K), _HI)], ws)
     wsp, wsb = _ws_args(ws)
-    _check(lib().fp8bq_gemm_dgrad(M, N, K, _ptr(qdy), _ld(qdy), _ptr(sdy), _ld(sdy), fdy, _ptr(qw), _ld(qw),
-                                  _ptr(sw), _ld(sw), fw, _ptr(dx), _out_type(dx), _ld(dx), wsp, wsb, _stream(dx)),
-           "fp8bq_gemm_dgrad")
+    return (M, N, K, _ptr(qdy), _ld(qdy), _ptr(sdy), _ld(sdy), fdy, _ptr(qw), _ld(qw),
+            _ptr(sw), _ld(sw), fw, _ptr(dx), _out_type(dx), _ld(dx), wsp, wsb, _stream(dx))
 
 
+@_entry
 def fp8bq_gemm_dgrad_wt(qdy, sdy, fdy, qwt, sw, fw, dx, ws=None):
     M, N = qdy.shape
     K = qwt.shape[0]
     _expect_all([(qdy, "qdy", (M, N), _U8), (sdy, "sdy", (N // 128, M), _F32), (qwt, "qwt", (K, N), _U8),
                  (sw, "sw", (N // 128, K // 128), _F32), (dx, "dx", (M, K), _HI)], ws)
     wsp, wsb = _ws_args(ws)
-    _check(lib().fp8bq_gemm_dgrad_wt(M, N, K, _ptr(qdy), _ld(qdy), _ptr(sdy), _ld(sdy), fdy, _ptr(qwt), _ld(qwt),
-                                     _ptr(sw), _ld(sw), fw, _ptr(dx), _out_type(dx), _ld(dx), wsp, wsb, _stream(dx)),
-           "fp8bq_gemm_dgrad_wt")
+    return (M, N, K, _ptr(qdy), _ld(qdy), _ptr(sdy), _ld(sdy), fdy, _ptr(qwt), _ld(qwt),
+            _ptr(sw), _ld(sw), fw, _ptr(dx), _out_type(dx), _ld(dx), wsp, wsb, _stream(dx))
 
 
+@_entry
 def fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None, accumulate=False):
     N, M = qdyt.shape
     K = qxt.shape[0]
@@ -335,55 +376,58 @@ def fp8bq_gemm_wgrad(qdyt, sdyt, fdy, qxt, sxt, fx, dw, ws=None, accumulate=Fals
                  (sxt, "sxt", (M // 128, K), _F32), (dw, "dw", (N, K), _F32 if accumulate else _HI)], ws)
     wsp, wsb = _ws_args(ws)
     ot = OUT_F32_ACCUM if accumulate else _out_type(dw)
-    _check(lib().fp8bq_gemm_wgrad(M, N, K, _ptr(qdyt), _ld(qdyt), _ptr(sdyt), _ld(sdyt), fdy, _ptr(qxt), _ld(qxt),
-                                  _ptr(sxt), _ld(sxt), fx, _ptr(dw), ot, _ld(dw), wsp, wsb, _stream(dw)),
-           "fp8bq_gemm_wgrad")
+    return (M, N, K, _ptr(qdyt), _ld(qdyt), _ptr(sdyt), _ld(sdyt), fdy, _ptr(qxt), _ld(qxt),
+            _ptr(sxt), _ld(sxt), fx, _ptr(dw), ot, _ld(dw), wsp, wsb, _stream(dw))
 
 
 def fp8bq_quantize_tensor_workspace_size(R, C):
     return int(lib().fp8bq_quantize_tensor_workspace_size(int(R), int(C)))
 
 
+@_entry
 def fp8bq_quantize_tensor_delayed(x, fmt, amax, beta, q, qt, s, ws):
     R, C = x.shape
     _expect_all([(x, "x", (R, C), _HI), (amax, "amax", (1,), _F32), (q, "q", (R, C), _U8),
                  (qt, "qt", (C, R), _U8), (s, "s", (1,), _F32)], ws)
     wsp, wsb = _ws_args(ws)
-    _check(lib().fp8bq_quantize_tensor_delayed(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(amax), float(beta), _ptr(q),
-                                               _ld(q), _ptr(qt), _ld(qt) if qt is not None else 0, _ptr(s), wsp, wsb,
-                                               _stream(x)), "fp8bq_quantize_tensor_delayed")
+    return (_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(amax), float(beta), _ptr(q),
+            _ld(q), _ptr(qt), _ld(qt) if qt is not None else 0, _ptr(s), wsp, wsb,
+            _stream(x))
 
 
+@_entry
 def fp8bq_quantize_tensor_delayed_noalloc(x, fmt, amax, beta, q, qt, s):
     R, C = x.shape
     _expect_all([(x, "x", (R, C), _HI), (amax, "amax", (1,), _F32), (q, "q", (R, C), _U8),
                  (qt, "qt", (C, R), _U8), (s, "s", (1,), _F32)])
-    _check(lib().fp8bq_quantize_tensor_delayed_noalloc(_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(amax), float(beta),
-                                                       _ptr(q), _ld(q), _ptr(qt), _ld(qt) if qt is not None else 0,
-                                                       _ptr(s), _stream(x)), "fp8bq_quantize_tensor_delayed_noalloc")
+    return (_ptr(x), _in_type(x), R, C, _ld(x), fmt, _ptr(amax), float(beta),
+            _ptr(q), _ld(q), _ptr(qt), _ld(qt) if qt is not None else 0,
+            _ptr(s), _stream(x))
 
 
+@_entry
 def fp8bq_gemm_tensor(qa, sa, fa, qb, sb, fb, out, ws=None):
     M, K = qa.shape
     N = qb.shape[0]
     _expect_all([(qa, "qa", (M, K), _U8), (sa, "sa", (1,), _F32), (qb, "qb", (N, K), _U8), (sb, "sb", (1,), _F32),
                  (out, "out", (M, N), _HI)], ws)
     wsp, wsb = _ws_args(ws)
-    _check(lib().fp8bq_gemm_tensor(M, N, K, _ptr(qa), _ld(qa), _ptr(sa), fa, _ptr(qb), _ld(qb), _ptr(sb), fb,
-                                   _ptr(out), _out_type(out), _ld(out), wsp, wsb, _stream(out)), "fp8bq_gemm_tensor")
+    return (M, N, K, _ptr(qa), _ld(qa), _ptr(sa), fa, _ptr(qb), _ld(qb), _ptr(sb), fb,
+            _ptr(out), _out_type(out), _ld(out), wsp, wsb, _stream(out))
 
 
 def fp8bq_hyperball_workspace_size(R, C):
     return int(lib().fp8bq_hyperball_workspace_size(int(R), int(C)))
 
 
+@_entry
 def fp8bq_hyperball_step(w, g, lr, weight_decay, eps, radius, norms, ws):
     R, C = w.shape
     _expect_all([(w, "w", (R, C), _F32), (g, "g", (R, C), _HI), (norms, "norms", (2,), _F32)], ws)
     wsp, wsb = _ws_args(ws)
-    _check(lib().fp8bq_hyperball_step(_ptr(w), _ld(w), _ptr(g), _in_type(g), _ld(g), R, C, float(lr),
-                                      float(weight_decay), float(eps), float(radius), _ptr(norms), wsp, wsb,
-                                      _stream(w)), "fp8bq_hyperball_step")
+    return (_ptr(w), _ld(w), _ptr(g), _in_type(g), _ld(g), R, C, float(lr),
+            float(weight_decay), float(eps), float(radius), _ptr(norms), wsp, wsb,
+            _stream(w))
 
 
 # ---------------------------------------------------------------------------------------------

@@ -24,7 +24,7 @@ def test_more_than_one_gpu_is_refused(argv, env):
 
 def _decoder_like_ops():
     """fprop, dgrad and wgrad of two 16384-token linears whose fprop and dgrad plans are unsplit
-    256x256 tiles; the wgrad of the first is split (so its kernel is not isolated)."""
+    256x256 tiles; the wgrad of the first is split (that call also launches a reduction pass)."""
     ops = []
     for name, K, N in [("a", 2048, 2560), ("b", 2048, 11264)]:
         M = 16384
@@ -36,29 +36,40 @@ def _decoder_like_ops():
     return ops
 
 
-def test_roofline_kernel_is_chosen_by_flops_not_timing():
+def test_roofline_kernel_is_the_one_with_most_time():
     ops = _decoder_like_ops()
-    # dgrad launches slower than fprop, then faster: the choice stays on the first symbol in step order
-    for scale in (1.3, 0.7):
+    # dgrad slower than fprop: the dgrad symbol carries the most time; faster: the fprop symbol
+    for scale, kop, names in ((1.3, 1, ["a.dgrad", "b.dgrad"]), (0.7, 0, ["a.fprop", "b.fprop"])):
         dur = [0.05 if o["kind"] == "quant_dual" else (0.2 * scale if o["kind"] == "dgrad" else 0.2) for o in ops]
         r = bench.roofline(fq, ops, dur, with_traffic=False)
-        assert r["kernel"].startswith("void fp8bq::gemm_tn_kernel<0, 256, 256, 2, 4, 2, 0, ")
-        assert r["launches"] == ["a.fprop", "b.fprop"]
-        fl = sum(o["flops"] for o in ops if o["kind"] == "fprop") / 2
+        assert r["kernel"].startswith(f"void fp8bq::gemm_tn_kernel<{kop}, 256, 256, 2, 4, 2, 0, ")
+        assert r["launches"] == names
+        fl = sum(o["flops"] for o in ops if o["name"] in names) / 2
+        ms = 0.2 * (scale if kop == 1 else 1.0)
         assert r["flops_per_launch"] == fl
-        assert abs(r["achieved"] - round(fl / 0.2e-3 / 1e12, 1)) < 0.05
+        assert abs(r["achieved"] - round(fl / (ms * 1e-3) / 1e12, 1)) < 0.05
         assert abs(r["frac"] - r["achieved"] / bench.FP8_PEAK_TFLOPS) < 1e-4
 
 
-def test_split_symbol_is_not_eligible():
+def test_split_calls_are_left_out_of_the_kernel_but_counted_in_their_kind():
     ops = _decoder_like_ops()
-    # only the wgrads carry time: the wgrad symbol of the split call is excluded, the other one is not
-    # eligible either if any call of it splits; the result falls back to an isolated symbol
+    # only the wgrads carry time: the split call (a.wgrad, GEMM + reduction pass) cannot stand for its
+    # kernel, the unsplit one (b.wgrad) can; the wgrad kind counts both
     dur = [1.0 if o["kind"] == "wgrad" else 0.1 for o in ops]
     r = bench.roofline(fq, ops, dur, with_traffic=False)
     for name in r["launches"]:
         o = next(x for x in ops if x["name"] == name)
         assert fq.fp8bq_gemm_plan(*o["plan"])[2] == 1
+    assert r["launches"] == ["b.wgrad"]
+    w = r["by_kind"]["wgrad"]
+    fl = sum(o["flops"] for o in ops if o["kind"] == "wgrad")
+    assert w["launches"] == 2 and w["with_reduction_pass"] == ["a.wgrad"]
+    assert abs(w["achieved"] - round(fl / 2e-3 / 1e12, 1)) < 0.05 and w["unit"] == "TFLOP/s"
+    assert set(r["by_kind"]) == {"fprop", "dgrad", "wgrad", "quantize"}
+    q = r["by_kind"]["quantize"]
+    assert q["bound"] == "hbm" and q["peak"] == bench.HBM_PEAK_GBS and "copy_gbs" not in q
+    r2 = bench.roofline(fq, ops, dur, with_traffic=False, copy_gbs=5000.0)
+    assert abs(r2["by_kind"]["quantize"]["frac_of_copy"] - r2["by_kind"]["quantize"]["achieved"] / 5000.0) < 1e-4
 
 
 def test_per_launch_statistics():

@@ -83,3 +83,9 @@ def test_every_entry_point_checks_its_tensors(call):
     with pytest.raises((TypeError, ValueError)) as e:
         call()
     assert "CUDA" not in str(e.value)  # refused for its dtype or shape, before the device check
+
+
+def test_prepare_validates_once_up_front():
+    a = _fprop_args(y=_bf16(M - 1, N))
+    with pytest.raises(ValueError):
+        fq.prepare(fq.fp8bq_gemm_fprop, a["qx"], a["sx"], a["fx"], a["qw"], a["sw"], a["fw"], a["y"])

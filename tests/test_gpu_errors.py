@@ -82,3 +82,17 @@ def test_binding_refuses_mismatched_tensors_on_the_device():
         fq.fp8bq_gemm_fprop(q, s, fq.E4M3, qw, sw, fq.E4M3, y, torch.zeros(1 << 20, dtype=torch.uint8))
     torch.cuda.synchronize()
     assert bool((y == -2.0).all()) and bool((short == -2.0).all())
+
+
+def test_prepared_calls_match_direct_calls():
+    """fq.prepare keeps a call's marshalled arguments: repeated launches give the direct call's output."""
+    M, N, K = 384, 512, 1024
+    q, s, qw, sw, qd, sd = _operands(M, N, K)
+    y1 = torch.full((M, N), -2.0, dtype=torch.bfloat16, device=DEV)
+    y2 = torch.full((M, N), -3.0, dtype=torch.bfloat16, device=DEV)
+    fq.fp8bq_gemm_fprop(q, s, fq.E4M3, qw, sw, fq.E4M3, y1)
+    launch = fq.prepare(fq.fp8bq_gemm_fprop, q, s, fq.E4M3, qw, sw, fq.E4M3, y2)
+    launch()
+    launch()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
