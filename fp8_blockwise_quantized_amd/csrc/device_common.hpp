@@ -3,12 +3,17 @@
 // FP8 formats are the OCP ones the recipe names: E4M3 = float8_e4m3fn (max 448) and
 // E5M2 = float8_e5m2 (max 57344) ("用 RTX 5090 花 $7000 训练 2B 大模型：Puro-2B 低成本预训练技术解析",
 // section "Blackwell 的 FP8 Tensor Core").  gfx950's v_cvt_pk_{fp8,bf8}_f32 convert to exactly these
-// formats with round-to-nearest-even; the quantizer clamps to +-fmt_max first, so the converter never
-// sees an out-of-range value.
+// formats with round-to-nearest-even.  A value above fmt_max but below the midpoint to the next
+// binade step (464 for E4M3, 61440 for E5M2) rounds to the fmt_max code, as the quantize rule's
+// clamp-then-convert gives; past that midpoint the converter gives NaN (E4M3) or Inf (E5M2), so a
+// quotient that can get there is clamped first.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
+#include <utility>
 
 namespace fp8bq {
 
@@ -51,6 +56,13 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
   return __builtin_fmaf(-e, r, q0);
 }
 
+// Quotient x / s of a blockwise group, unclamped.  With |x| <= amax and s = RN(amax / fmt_max), the
+// exact quotient is at most fmt_max / (1 - 2^-24) = fmt_max + 0.875 ulp(fmt_max) (fmt_max = 1.75 x a
+// power of two), so its rounding is at most fmt_max + 1 ulp; with the floored scale it is below
+// fmt_max.  The converter rounds fmt_max + 1 ulp (and its negative) to the fmt_max code, which is the
+// clamped code, so the clamp changes no code and is left out (one VALU op per element and layout).
+__device__ __forceinline__ float blockwise_quotient(float x, float s, float r) { return div_by_scale(x, s, r); }
+
 template <int FMT>
 __device__ __forceinline__ float clamp_fmt(float y) {
   return __builtin_fminf(__builtin_fmaxf(y, -FmtTraits<FMT>::kMax), FmtTraits<FMT>::kMax);
@@ -65,10 +77,12 @@ __device__ __forceinline__ int cvt_pk(float a, float b, int old) {
     return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
 }
 
-// Four values -> one little-endian dword of codes (v0 in the lowest byte).
+// Four values -> one little-endian dword of codes (v0 in the lowest byte).  The first conversion
+// writes the low half over v0's own bits (the high half is overwritten by the second), which spares
+// a register clear per dword.
 template <int FMT>
 __device__ __forceinline__ uint32_t pack4(float v0, float v1, float v2, float v3) {
-  int w = cvt_pk<FMT, false>(v0, v1, 0);
+  int w = cvt_pk<FMT, false>(v0, v1, __float_as_int(v0));
   w = cvt_pk<FMT, true>(v2, v3, w);
   return (uint32_t)w;
 }
@@ -76,16 +90,84 @@ __device__ __forceinline__ uint32_t pack4(float v0, float v1, float v2, float v3
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Max over the 16 lanes of each DPP row (all 16 lanes receive it).  Values are >= 0.
-__device__ __forceinline__ float row16_max(float v) {
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false)));
-  return v;
+// Lane exchanges within DPP rows (16 lanes).  Every pattern used here reads a valid lane for every
+// lane, so bound_ctrl (zero for an invalid source) never applies; with old = 0 it lets the compiler
+// fold the move into the consuming max as one v_max_u32_dpp.
+constexpr int kDppXor8 = 0x128;    // row_ror:8: partner lane ^ 8
+constexpr int kDppMirror8 = 0x141; // row_half_mirror: partner 7 - lane within each half row
+constexpr int kDppXor2 = 0x4E;     // quad_perm [2,3,0,1]: partner lane ^ 2
+constexpr int kDppXor1 = 0xB1;     // quad_perm [1,0,3,2]: partner lane ^ 1
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_read(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+// Max of non-negative finite floats (or +0) held as bits: their order is the unsigned integer order.
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint32_t umax_partner(uint32_t mine, uint32_t sent) {
+  return umax(mine, dpp_read<CTRL>(sent));
 }
 
-// Max over the whole 64-lane wavefront (uniform result).
+// Max over the 16 lanes of each DPP row (all 16 lanes receive it).  Values are >= 0.
+__device__ __forceinline__ float row16_max(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = umax_partner<kDppXor8>(u, u);
+  u = umax_partner<kDppMirror8>(u, u);
+  u = umax_partner<kDppXor2>(u, u);
+  u = umax_partner<kDppXor1>(u, u);
+  return __uint_as_float(u);
+}
+
+// Reduce-scatter over a DPP row: each of the 16 lanes holds partial maxima m[0..NR) of the same NR
+// rows (NR = 1, 2, 4 or 8; values >= 0 as bits).  Stage S exchanges with the partner that differs
+// in lane bit 3 - S; while more than one row is left, a lane keeps the half of its rows picked by
+// that bit and sends the other half, so the rows halve at each stage; the remaining stages take the
+// plain max.  On return lane l holds the 16-lane max of row (l >> (4 - log2 NR)) & (NR - 1), and
+// row r sits in lane r << (4 - log2 NR) (and the lanes up to the next such lane).
+template <int S>
+constexpr int scatter_ctrl() {
+  return S == 0 ? kDppXor8 : S == 1 ? kDppMirror8 : S == 2 ? kDppXor2 : kDppXor1;
+}
+template <int S, int N, int NR>
+__device__ __forceinline__ void scatter_stage(uint32_t (&a)[NR], int lane16) {
+  if constexpr (S < 4) {
+    if constexpr (N > 1) {
+      const bool hi = (lane16 >> (3 - S)) & 1;
+#pragma unroll
+      for (int k = 0; k < N / 2; ++k) {
+        const uint32_t keep = hi ? a[k + N / 2] : a[k];
+        const uint32_t send = hi ? a[k] : a[k + N / 2];
+        a[k] = umax_partner<scatter_ctrl<S>()>(keep, send);
+      }
+      scatter_stage<S + 1, N / 2>(a, lane16);
+    } else {
+      a[0] = umax_partner<scatter_ctrl<S>()>(a[0], a[0]);
+      scatter_stage<S + 1, 1>(a, lane16);
+    }
+  }
+}
+template <int NR>
+__device__ __forceinline__ float row16_max_scatter(const float (&m)[NR], int lane16) {
+  static_assert(NR == 1 || NR == 2 || NR == 4 || NR == 8, "rows per lane");
+  uint32_t a[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) a[k] = __float_as_uint(m[k]);
+  scatter_stage<0, NR>(a, lane16);
+  return __uint_as_float(a[0]);
+}
+// log2 of the lanes that share one row after row16_max_scatter<NR>.
+template <int NR>
+constexpr int scatter_shift() {
+  return NR == 8 ? 1 : NR == 4 ? 2 : NR == 2 ? 3 : 4;
+}
+// Value of lane LANE of this lane's DPP row (row_newbcast).
+template <int LANE>
+__device__ __forceinline__ float row16_bcast(float v) {
+  static_assert(LANE >= 0 && LANE < 16, "lane");
+  return __uint_as_float(dpp_read<0x150 + LANE>(__float_as_uint(v)));
+}
+
+// Max over the whole 64-lane wavefront (uniform result).  Values are >= 0.
 __device__ __forceinline__ float wave_max(float v) {
   v = row16_max(v);
   float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
@@ -93,6 +175,17 @@ __device__ __forceinline__ float wave_max(float v) {
   float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
   float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
   return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
+}
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, in order (a compile-time index, for
+// operands that must be constants such as DPP controls).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Round-to-nearest-even fp32 -> bf16 pair, lo in the low half: one v_cvt_pk_bf16_f32 on gfx950.

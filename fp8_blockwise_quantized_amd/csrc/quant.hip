@@ -13,7 +13,9 @@
 // rotations (1x128, 128x128) or through LDS (128x1, whose groups run down columns), and writes codes
 // with 8- or 16-byte stores.  The division x/s uses the exact reciprocal-and-residual form in
 // div_by_scale (3 VALU ops instead of an IEEE divide sequence), which returns the IEEE quotient bit
-// for bit wherever it can change a code.
+// for bit wherever it can change a code.  The blockwise passes skip the clamp, which changes no code
+// there (blockwise_quotient), and compute each group scale once per group rather than in every lane
+// that holds part of the group (row16_max_scatter).
 
 #include <atomic>
 
@@ -59,12 +61,15 @@ struct Load8<float> {
   }
 };
 
-// Quantize 8 values with the group's (s, r) into two dwords of codes.
-template <int FMT>
+// Quantize 8 values with the group's (s, r) into two dwords of codes.  CLAMP: clamp the quotients to
+// +-fmt_max before converting, which a per-tensor scale from a running amax needs (the tensor can
+// exceed it); a blockwise scale comes from the group's own amax, so the quotients need no clamp
+// (blockwise_quotient).
+template <int FMT, bool CLAMP = false>
 __device__ __forceinline__ uint2 quant8(const float (&v)[8], float s, float r) {
   float y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = clamp_fmt<FMT>(div_by_scale(v[i], s, r));
+  for (int i = 0; i < 8; ++i) y[i] = CLAMP ? clamp_fmt<FMT>(div_by_scale(v[i], s, r)) : blockwise_quotient(v[i], s, r);
   return make_uint2(pack4<FMT>(y[0], y[1], y[2], y[3]), pack4<FMT>(y[4], y[5], y[6], y[7]));
 }
 
@@ -96,20 +101,26 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const TIn* __restrict_
       for (int i = 0; i < 8; ++i) v[p][i] = 0.0f;
     }
   }
+  // Each lane ends with one row's group amax (row l16 / 4) and computes that row's scale; the 16
+  // lanes then take the four rows' scales from lanes 0, 4, 8, 12.
+  float m[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int64_t r = r0 + rsub + 16 * p;
-    float m = 0.0f;
+    m[p] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
-    const float amax = row16_max(m);
-    const float sc = group_scale<FMT>(amax);
-    const float rc = 1.0f / sc;
-    if (r < R) {
-      store_codes8(q + r * ldq + col, quant8<FMT>(v[p], sc, rc));
-      if (l16 == 0) s[g * lds + r] = sc;
-    }
+    for (int i = 0; i < 8; ++i) m[p] = __builtin_fmaxf(m[p], __builtin_fabsf(v[p][i]));
   }
+  const float sc_own = group_scale<FMT>(row16_max_scatter<4>(m, l16));
+  const float rc_own = 1.0f / sc_own;
+  const int own = l16 >> scatter_shift<4>();
+  if ((l16 & 3) == 0 && r0 + rsub + 16 * own < R) s[g * lds + r0 + rsub + 16 * own] = sc_own;
+  static_for<4>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    const float sc = row16_bcast<(p << scatter_shift<4>())>(sc_own);
+    const float rc = row16_bcast<(p << scatter_shift<4>())>(rc_own);
+    const int64_t r = r0 + rsub + 16 * p;
+    if (r < R) store_codes8(q + r * ldq + col, quant8<FMT>(v[p], sc, rc));
+  });
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -190,7 +201,7 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(const TIn* __restrict_
     const float sc = ssc[col_pos(c)], rc = src[col_pos(c)];
     float y[8];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) y[p] = clamp_fmt<FMT>(div_by_scale(v[p][i], sc, rc));
+    for (int p = 0; p < 8; ++p) y[p] = blockwise_quotient(v[p][i], sc, rc);
     const uint2 w = make_uint2(pack4<FMT>(y[0], y[1], y[2], y[3]), pack4<FMT>(y[4], y[5], y[6], y[7]));
     *reinterpret_cast<uint2*>(tileT + qt_off(c, rg)) = w;
   }
@@ -237,21 +248,26 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const TIn* __restrict__
 #pragma unroll
   for (int p = 0; p < 8; ++p) Load8<TIn>::run(x + (rb * kGroup + 8 * rg + p) * ldx + col, v[p]);
 
-  // 1x128 groups: row r = 128*rb + 8*rg + p, columns c0 .. c0+127
-  float rs[8];
+  // 1x128 groups: row r = 128*rb + 8*rg + p, columns c0 .. c0+127.  Each lane ends with one row's
+  // group amax (row cc / 2) and computes that row's scale; the 16 lanes then take the eight rows'
+  // scales from the even lanes.
+  {
+    float m[8];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    float m = 0.0f;
+    for (int p = 0; p < 8; ++p) {
+      m[p] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[p][i]));
-    const float sc = group_scale<FR>(row16_max(m));
-    rs[p] = sc;
-    store_codes8(q + (rb * kGroup + 8 * rg + p) * ldq + col, quant8<FR>(v[p], sc, 1.0f / sc));
-  }
-  if (cc == 0) {
-    f32x4* sp = reinterpret_cast<f32x4*>(s + g * lds + rb * kGroup + 8 * rg);
-    sp[0] = (f32x4){rs[0], rs[1], rs[2], rs[3]};
-    sp[1] = (f32x4){rs[4], rs[5], rs[6], rs[7]};
+      for (int i = 0; i < 8; ++i) m[p] = __builtin_fmaxf(m[p], __builtin_fabsf(v[p][i]));
+    }
+    const float sc_own = group_scale<FR>(row16_max_scatter<8>(m, cc));
+    const float rc_own = 1.0f / sc_own;
+    if ((cc & 1) == 0) s[g * lds + rb * kGroup + 8 * rg + (cc >> scatter_shift<8>())] = sc_own;
+    static_for<8>([&](auto P) {
+      constexpr int p = decltype(P)::value;
+      const float sc = row16_bcast<(p << scatter_shift<8>())>(sc_own);
+      const float rc = row16_bcast<(p << scatter_shift<8>())>(rc_own);
+      store_codes8(q + (rb * kGroup + 8 * rg + p) * ldq + col, quant8<FR>(v[p], sc, rc));
+    });
   }
 
   // 128x1 groups: column c0 + c, rows 128*rb .. +127 (as quant_128x1_kernel)
@@ -279,7 +295,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const TIn* __restrict__
     const float sc = ssc[col_pos(c)], rc = src[col_pos(c)];
     float y[8];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) y[p] = clamp_fmt<FC>(div_by_scale(v[p][i], sc, rc));
+    for (int p = 0; p < 8; ++p) y[p] = blockwise_quotient(v[p][i], sc, rc);
     const uint2 w = make_uint2(pack4<FC>(y[0], y[1], y[2], y[3]), pack4<FC>(y[4], y[5], y[6], y[7]));
     *reinterpret_cast<uint2*>(tileT + qt_off(c, rg)) = w;
   }
@@ -413,7 +429,7 @@ __device__ __forceinline__ void weight_dual_tile(const TIn* __restrict__ w, int6
   uint8_t cb[8][8];  // codes [row p][column i]
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    const uint2 wd = quant8<FMT>(v[p], sc, rc);
+    const uint2 wd = quant8<FMT, TENSOR>(v[p], sc, rc);
     store_codes8(q + (nb * kGroup + 8 * rg + p) * ldq + col, wd);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -529,7 +545,7 @@ __global__ __launch_bounds__(256) void tensor_quant_kernel(const TIn* __restrict
     float b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) b[i] = sizeof(TIn) == 4 ? round_bf16(v[i]) : v[i];
-    store_codes8(q + r * ldq + c, quant8<FMT>(b, sc, rc));
+    store_codes8(q + r * ldq + c, quant8<FMT, true>(b, sc, rc));
   });
 }
 

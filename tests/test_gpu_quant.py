@@ -435,8 +435,65 @@ def test_weights_batch_error_enqueues_nothing():
         fq.fp8bq_quantize_weights_dual([(w0, q0, s0, qt0), (w1, q1, s1, bad_qt1)], fq.E4M3)
     assert e.value.status == 10  # FP8BQ_ERR_OVERLAP
     qt1 = torch.empty((200, 128), dtype=torch.uint8, device=DEV)
+    # tensors of the shapes the binding derives from K = 200, so the call reaches the library's check
     with pytest.raises(fq.Fp8bqError) as e:
-        fq.fp8bq_quantize_weights_dual([(w0, q0, s0, qt0), (w1[:, :200], q1[:, :200], s1, qt1)], fq.E4M3)
+        fq.fp8bq_quantize_weights_dual([(w0, q0, s0, qt0), (w1[:, :200], q1[:, :200], s1[:, :1], qt1)], fq.E4M3)
     assert e.value.status == 2  # FP8BQ_ERR_SHAPE: K = 200
     torch.cuda.synchronize()
     assert bool((q0 == 0xA5).all()) and bool((qt0 == 0x5A).all()) and bool((s0 == -1.0).all())
+
+
+# ------------------------------------------------------------------------------------------
+# group amax whose quotient rounds to just above the format maximum
+# ------------------------------------------------------------------------------------------
+
+def _over_max_amax(fmt, dt):
+    """Positive values a (every BF16 one, or a log-uniform FP32 sample) for which fp32(a / s), with
+    s = max(fp32(a / fmt_max), 1e-12), is above fmt_max: a group whose amax is a then divides a to
+    fmt_max + 1 ulp, and its code must still be the fmt_max code."""
+    m = np.float32(oracle.fmt_max(fmt))
+    if dt == "bf16":
+        a = torch.arange(1, 0x7F80, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).float().numpy()
+    else:
+        rng = np.random.default_rng(23)
+        a = np.exp(rng.uniform(-60.0, 60.0, 400_000)).astype(np.float32)
+    s = np.maximum(a / m, np.float32(1e-12)).astype(np.float32)
+    q = (a / s).astype(np.float32)
+    assert np.all(q <= np.nextafter(m, np.float32(np.inf)))  # never more than one ulp above
+    return a[q > m]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_group_amax_quotient_just_above_the_maximum(fmt, dt):
+    """About one group in twelve has an amax whose quotient rounds above fmt_max.  Rows of +a and -a
+    (each such a) plus smaller values, so that rows, columns and 128x128 tiles all have such an amax:
+    codes and scales of every quantizer bit-identical to the oracle, with the fmt_max codes present."""
+    a = _over_max_amax(fmt, dt)
+    assert a.size > 1000
+    R = 128 * ((a.size + 127) // 128)
+    amax = np.resize(a, R).astype(np.float32)
+    rng = np.random.default_rng(29)
+    x = (rng.uniform(-1.0, 1.0, (R, 128)).astype(np.float32) * amax[:, None]).astype(np.float32)
+    r = np.arange(R)
+    x[r, r % 128] = amax
+    x[r, (r + 1) % 128] = -amax
+    xt = torch.from_numpy(x).to(torch.bfloat16) if dt == "bf16" else torch.from_numpy(x)
+    xf = xt.float().numpy()
+    assert np.array_equal(np.abs(xf).max(axis=1), amax)
+    say(f"over-max quotients {fmt} {dt}: {a.size} amax values, {R} rows")
+    top = oracle.encode(np.array([oracle.fmt_max(fmt), -oracle.fmt_max(fmt)], np.float32), fmt)
+    e_rows, e_cols = oracle.quant_act_1x128(xf, fmt), oracle.quant_act_128x1(xf, fmt)
+    g_rows = gpu_1x128(xt, fmt)
+    assert np.all((g_rows[0] == top[0]).sum(axis=1) >= 1) and np.all((g_rows[0] == top[1]).sum(axis=1) >= 1)
+    same(g_rows, e_rows, "1x128")
+    same(gpu_128x1(xt, fmt), e_cols, "128x1")
+    d_rows, d_cols = gpu_dual(xt, fmt, fmt)
+    same(d_rows, e_rows, "dual 1x128")
+    same(d_cols, e_cols, "dual 128x1")
+    e_w = oracle.quant_weight_128x128(xf, fmt)
+    same(gpu_w(xt, fmt), e_w, "128x128")
+    q, s, qt = fq.quantize_weight_dual(xt.to(DEV), FP[fmt])
+    torch.cuda.synchronize()
+    same((q.cpu().numpy(), s.cpu().numpy()), e_w, "128x128 dual")
+    assert np.array_equal(qt.cpu().numpy(), e_w[0].T), "transposed weight codes"
