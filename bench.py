@@ -24,7 +24,7 @@ Prints ONE JSON line on stdout.  `value` = GEMM FLOPs of the step / wall time of
 quantize passes are inside the timed step).  `breakdown` holds per-product TFLOP/s and per-pass GB/s
 from HIP events recorded on the launch stream.  `roofline` is for the GEMM kernel with the most time
 per step, with `by_kind` entries for fprop, dgrad, wgrad (each against the FP8 peak) and the quantize
-passes (against HBM, beside the same run's plain-copy bandwidth).  After the timed steps, `configs`
+passes (against HBM, beside the same run's streaming-copy and torch-copy bandwidths).  After the timed steps, `configs`
 times the other workloads: the single 8192 x 8192 x 2048 linear, the token sweep K = N = 2048 with its
 knee, and the heavy-tailed gradients (dgrad / wgrad with dY in E5M2 and E4M3, and their quantization
 error).  `cpu_baseline` times the CPU oracle on a bounded sample of the same path (first 4096 tokens)
@@ -142,8 +142,9 @@ def main():
 
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     breakdown = summarize(ops, dur_ms, np.median(per, axis=0), per.min(axis=0))
-    copy_gbs = copy_ceiling(torch, dev) if args.workload == "decoder" else None
-    roof = roofline(fq, ops, dur_ms, with_traffic=args.workload == "decoder", copy_gbs=copy_gbs)
+    copies = copy_ceiling(torch, fq, dev) if args.workload == "decoder" else {}
+    roof = roofline(fq, ops, dur_ms, with_traffic=args.workload == "decoder", copy_gbs=copies.get("stream"),
+                    torch_copy_gbs=copies.get("torch"))
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -623,7 +624,7 @@ def _traffic(kernel):
         return None
 
 
-def roofline(fq, ops, dur_ms, with_traffic=True, copy_gbs=None):
+def roofline(fq, ops, dur_ms, with_traffic=True, copy_gbs=None, torch_copy_gbs=None):
     """The dominant GEMM kernel and one entry per product kind.
 
     Dominant kernel: the kernel symbol with the most time per step over the calls that launch it
@@ -633,7 +634,9 @@ def roofline(fq, ops, dur_ms, with_traffic=True, copy_gbs=None):
 
     by_kind: fprop, dgrad and wgrad each as a whole (every call of that kind, reduction passes
     included: what the product costs the step), and the quantize passes against HBM (algorithmic
-    bytes), with the same run's plain-copy bandwidth beside them when measured."""
+    bytes), with the same run's copy bandwidths beside them when measured: copy_gbs, the library's
+    streaming copy (the fastest plain copy measured on this GPU, the ceiling frac_of_copy is taken
+    against), and torch_copy_gbs, torch's device copy, for context."""
     groups = {}
     for o, d in zip(ops, dur_ms):
         if not o["flops"]:
@@ -669,6 +672,8 @@ def roofline(fq, ops, dur_ms, with_traffic=True, copy_gbs=None):
                                "frac": round(gq / HBM_PEAK_GBS, 4), "ms_per_step": round(tq, 4), "launches": len(q)}
         if copy_gbs:
             by_kind["quantize"].update(copy_gbs=round(copy_gbs, 1), frac_of_copy=round(gq / copy_gbs, 4))
+        if torch_copy_gbs:
+            by_kind["quantize"].update(torch_copy_gbs=round(torch_copy_gbs, 1))
     return {
         "bound": "mfma",
         "kernel": name,
@@ -686,23 +691,27 @@ def roofline(fq, ops, dur_ms, with_traffic=True, copy_gbs=None):
     }
 
 
-def copy_ceiling(torch, dev, mib=1024, reps=10):
-    """GB/s of a plain device copy of `mib` MiB (bytes read + written), timed with HIP events: the
-    bandwidth a streaming kernel can expect on this machine, beside the 8 TB/s peak."""
+def copy_ceiling(torch, fq, dev, mib=1024, reps=10):
+    """GB/s (bytes read + written) of two device copies of `mib` MiB, timed with HIP events on the
+    launch stream: "stream", the library's streaming copy (16-byte non-temporal accesses), the
+    bandwidth a streaming kernel can reach on this GPU; "torch", torch's device copy."""
     a = torch.empty(mib << 18, dtype=torch.float32, device=dev)
     a.fill_(1.0)
     b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, fn in (("stream", fq.prepare(fq.fp8bq_stream_copy, a, b)), ("torch", lambda: b.copy_(a))):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = 2 * (mib << 20) / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
     del a, b
-    return 2 * (mib << 20) / (ms * 1e-3) / 1e9
+    return out
 
 
 # -----------------------------------------------------------------------------------------------

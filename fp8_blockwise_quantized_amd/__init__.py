@@ -108,6 +108,7 @@ _SIGS = {
                              ctypes.c_double, ctypes.c_double, _c_vp, _c_vp, _c_sz, _c_vp],
     "fp8bq_gemm_workspace_size": [_c_int, _c_i64, _c_i64, _c_i64],
     "fp8bq_gemm_plan": [_c_int, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
+    "fp8bq_stream_copy": [_c_vp, _c_vp, _c_sz, _c_vp],
     "fp8bq_status_string": [_c_int],
     "fp8bq_version": [],
 }
@@ -428,6 +429,21 @@ def fp8bq_hyperball_step(w, g, lr, weight_decay, eps, radius, norms, ws):
     return (_ptr(w), _ld(w), _ptr(g), _in_type(g), _ld(g), R, C, float(lr),
             float(weight_decay), float(eps), float(radius), _ptr(norms), wsp, wsb,
             _stream(w))
+
+
+@_entry
+def fp8bq_stream_copy(src, dst):
+    """Copy the bytes of contiguous tensor src into dst (same byte size): the streaming-copy
+    bandwidth reference, not an operation of the layer."""
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous torch tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must hold the same number of bytes")
+    if src.device.type != "cuda" or dst.device != src.device:
+        raise ValueError("src and dst must be on the same CUDA (HIP) device")
+    return (_ptr(src), _ptr(dst), nbytes, _stream(src))
 
 
 # ---------------------------------------------------------------------------------------------

@@ -320,6 +320,15 @@ int fp8bq_hyperball_step(float* w, int64_t ldw, const void* g, fp8bq_in gt, int6
                                         (hipStream_t)stream));
 }
 
+int fp8bq_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  bool empty = false;
+  int st = validate_stream_copy(src, dst, bytes, &empty);
+  if (st != kOk || empty) return st;
+  int cus = 0;
+  if ((st = current_device(&cus)) != kOk) return st;
+  return launched(launch_stream_copy(src, dst, bytes, cus, (hipStream_t)stream));
+}
+
 size_t fp8bq_gemm_workspace_size(fp8bq_op op, int64_t M, int64_t N, int64_t K) {
   if ((int)op < 0 || (int)op > 4 || M < 0 || N < 0 || K < 0) return 0;
   return plan_gemm((int)op, M, N, K, cu_count_or_default()).ws_total();

@@ -55,6 +55,10 @@ hipError_t launch_quant_tensor_delayed(const void* x, int xt, int64_t R, int64_t
                                        double beta, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s,
                                        void* ws, hipStream_t st);
 
+// Streaming copy of bytes (a multiple of 16; both pointers 16-byte aligned, ranges disjoint) with a
+// grid sized from the device's compute-unit count: the bandwidth reference.
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, int cus, hipStream_t st);
+
 // One scaled FP8 GEMM in "TN" form: C[m, n] = sum_kb sa(kb, m) * sb(kb, n) * sum_{k in kb} A[m, k] B[n, k],
 // where A [Mr, K] and B [Nc, K] are both contiguous along the contraction.
 //   sa(kb, m) = sa[kb * ldsa + m * sa_mstride]

@@ -221,6 +221,20 @@ int validate_hyperball(const void* w, int64_t ldw, const void* g, int gt, int64_
   return kOk;
 }
 
+int validate_stream_copy(const void* src, const void* dst, size_t bytes, bool* empty) {
+  *empty = false;
+  if (bytes % 16 != 0 || bytes >= ((size_t)1 << 48)) return kErrShape;
+  if (bytes == 0) {
+    *empty = true;
+    return kOk;
+  }
+  if (!src || !dst) return kErrNull;
+  if (!aligned16(src) || !aligned16(dst)) return kErrAlign;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return kErrOverlap;
+  return kOk;
+}
+
 int validate_gemm(const GemmArgs& g, size_t ws_needed, bool* empty, bool* zero_fill) {
   *empty = false;
   *zero_fill = false;

@@ -71,6 +71,10 @@ int validate_hyperball(const void* w, int64_t ldw, const void* g, int gt, int64_
                        double lr, double wd, double eps, double radius, const void* norms, const void* ws,
                        size_t ws_bytes, size_t ws_needed, bool* empty);
 
+// Streaming copy: src and dst non-null and 16-byte aligned, bytes a multiple of 16 below 2^48, the two
+// ranges disjoint.
+int validate_stream_copy(const void* src, const void* dst, size_t bytes, bool* empty);
+
 // The three GEMMs share one validator: op selects the operand shapes.
 struct GemmArgs {
   int op;

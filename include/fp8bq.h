@@ -387,6 +387,21 @@ size_t fp8bq_gemm_workspace_size(fp8bq_op op, int64_t M, int64_t N, int64_t K);
 int fp8bq_gemm_plan(fp8bq_op op, int64_t M, int64_t N, int64_t K, int32_t* tile_m, int32_t* tile_n,
                     int32_t* split_k);
 
+/*
+ * Streaming copy of `bytes` bytes from src to dst (device memory): the bandwidth reference that the
+ * quantize passes are measured against.  It is not an operation of the layer: the pages define no
+ * copy, and no other entry point uses it.  16-byte non-temporal loads and stores with a grid sized
+ * from the device's compute units.
+ *
+ *   src, dst  16-byte aligned device pointers; the ranges [src, src+bytes) and [dst, dst+bytes)
+ *             must not overlap.
+ *   bytes     a multiple of 16, below 2^48; 0 is a no-op.
+ *
+ * Errors: FP8BQ_ERR_SHAPE (bytes not a multiple of 16, or too large), FP8BQ_ERR_NULL,
+ * FP8BQ_ERR_ALIGN, FP8BQ_ERR_OVERLAP, FP8BQ_ERR_DEVICE, FP8BQ_ERR_LAUNCH.
+ */
+int fp8bq_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fp8bq_status_string(int status);
 

@@ -58,6 +58,10 @@ int main(void) {
   static float w[256 * 256];
   EXPECT(fp8bq_hyperball_step(w, 256, x, FP8BQ_IN_BF16, 256, 256, 256, 1e-4, 0.1, 0.0, 0.0, NULL, ws, sizeof ws,
                               NULL) == FP8BQ_ERR_VALUE);     /* eps must be > 0 */
+  /* the streaming-copy reference: a size not a multiple of 16, overlapping ranges, empty */
+  EXPECT(fp8bq_stream_copy(w, q, 100, NULL) == FP8BQ_ERR_SHAPE);
+  EXPECT(fp8bq_stream_copy(w, (uint8_t*)w + 256, 1024, NULL) == FP8BQ_ERR_OVERLAP);
+  EXPECT(fp8bq_stream_copy(NULL, NULL, 0, NULL) == FP8BQ_OK);
   /* several weights: a job array from C, checked job by job and across jobs */
   static uint8_t qt[256 * 256], q2[256 * 256], qt2[256 * 256];
   static float s2[4];

@@ -36,7 +36,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fq.lib()
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -318,6 +318,19 @@ def test_gemm_tensor_validation():
 def hb(w=P(0), ldw=256, g=P(1), gt=0, ldg=256, R=256, C=256, lr=1e-4, wd=0.1, eps=1e-8, radius=0.0, norms=P(2),
        ws=P(3), ws_bytes=1 << 16):
     return fq.lib().fp8bq_hyperball_step(w, ldw, g, gt, ldg, R, C, lr, wd, eps, radius, norms, ws, ws_bytes, S0)
+
+
+def test_stream_copy_validation():
+    c = lambda src=P(0), dst=P(1), n=4096: fq.lib().fp8bq_stream_copy(src, dst, n, S0)
+    assert c(n=0) == OK and c(src=NUL, dst=NUL, n=0) == OK  # empty: a no-op, pointers unread
+    assert c(n=100) == SHAPE
+    assert c(n=1 << 48) == SHAPE
+    assert c(src=NUL) == NULL and c(dst=NUL) == NULL
+    assert c(src=ctypes.c_void_p(0x100008)) == ALIGN
+    assert c(dst=ctypes.c_void_p(0x100000 + 2048)) == OVERLAP  # dst starts inside src's 4096 bytes
+    assert c(src=ctypes.c_void_p(0x200000 - 2048)) == OVERLAP  # src ends inside dst
+    valid(lambda: c())
+    valid(lambda: c(src=ctypes.c_void_p(0x200000 - 4096)))  # adjacent ranges are fine
 
 
 def test_hyperball_validation():

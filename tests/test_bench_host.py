@@ -68,8 +68,9 @@ def test_split_calls_are_left_out_of_the_kernel_but_counted_in_their_kind():
     assert set(r["by_kind"]) == {"fprop", "dgrad", "wgrad", "quantize"}
     q = r["by_kind"]["quantize"]
     assert q["bound"] == "hbm" and q["peak"] == bench.HBM_PEAK_GBS and "copy_gbs" not in q
-    r2 = bench.roofline(fq, ops, dur, with_traffic=False, copy_gbs=5000.0)
-    assert abs(r2["by_kind"]["quantize"]["frac_of_copy"] - r2["by_kind"]["quantize"]["achieved"] / 5000.0) < 1e-4
+    r2 = bench.roofline(fq, ops, dur, with_traffic=False, copy_gbs=6000.0, torch_copy_gbs=5000.0)
+    q2 = r2["by_kind"]["quantize"]
+    assert abs(q2["frac_of_copy"] - q2["achieved"] / 6000.0) < 1e-4 and q2["torch_copy_gbs"] == 5000.0
 
 
 def test_per_launch_statistics():

@@ -96,3 +96,23 @@ def test_prepared_calls_match_direct_calls():
     launch()
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+def test_stream_copy_copies_every_byte():
+    """The bandwidth reference copies exactly: sizes that leave a partial last iteration, a size
+    past one grid stride, and an overlap refused with nothing written."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    for nbytes in (16, 4096 + 48, 3 << 20, (257 << 20) + 16 * 7):
+        src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV, generator=g)
+        dst = torch.zeros_like(src)
+        fq.fp8bq_stream_copy(src, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst), nbytes
+    buf = torch.arange(4096, dtype=torch.uint8, device=DEV)
+    before = buf.clone()
+    with pytest.raises(fq.Fp8bqError) as e:
+        fq.fp8bq_stream_copy(buf[:2048], buf[1024:3072])
+    assert e.value.status == 10  # FP8BQ_ERR_OVERLAP
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
