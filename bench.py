@@ -24,7 +24,9 @@ Prints ONE JSON line on stdout.  `value` = GEMM FLOPs of the step / wall time of
 quantize passes are inside the timed step).  `breakdown` holds per-product TFLOP/s and per-pass GB/s
 from HIP events recorded on the launch stream.  `roofline` is for the GEMM kernel with the most time
 per step, with `by_kind` entries for fprop, dgrad, wgrad (each against the FP8 peak) and the quantize
-passes (against HBM, beside the same run's streaming-copy and torch-copy bandwidths).  After the timed steps, `configs`
+passes (against HBM, beside the same run's streaming-copy and torch-copy bandwidths; `scrubbed` times
+each quantize launch again on its own after a 512 MiB read that evicts the caches, so that no launch
+reads from the caches or pays for the write-back of an earlier kernel's output).  After the timed steps, `configs`
 times the other workloads: the single 8192 x 8192 x 2048 linear, the token sweep K = N = 2048 with its
 knee, and the heavy-tailed gradients (dgrad / wgrad with dY in E5M2 and E4M3, and their quantization
 error).  `cpu_baseline` times the CPU oracle on a bounded sample of the same path (first 4096 tokens)
@@ -145,6 +147,8 @@ def main():
     copies = copy_ceiling(torch, fq, dev) if args.workload == "decoder" else {}
     roof = roofline(fq, ops, dur_ms, with_traffic=args.workload == "decoder", copy_gbs=copies.get("stream"),
                     torch_copy_gbs=copies.get("torch"))
+    if roof and "quantize" in roof["by_kind"] and args.workload == "decoder":
+        roof["by_kind"]["quantize"]["scrubbed"] = quant_scrubbed(torch, dev, ops, copies.get("stream"))
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -689,6 +693,38 @@ def roofline(fq, ops, dur_ms, with_traffic=True, copy_gbs=None, torch_copy_gbs=N
         "mean_launch_ms": round(ms_per_launch, 5),
         "by_kind": by_kind,
     }
+
+
+def quant_scrubbed(torch, dev, ops, copy_gbs=None, reps=5, scrub_mib=512):
+    """Each quantize launch of the step timed on its own with cold caches: before every timed launch a
+    read of `scrub_mib` MiB (twice the 256 MB Infinity Cache) evicts them, writing back what the
+    earlier kernels left dirty, outside the event pair.  In the step a launch also pays for the
+    write-back of the outputs of the kernels before it; here it does not.  GB/s at the algorithmic
+    bytes, over all launches (total bytes / total time) and per launch (mean of `reps`)."""
+    import numpy as np
+    q = [o for o in ops if o["bytes"]]
+    scrub = torch.ones(scrub_mib << 18, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in q]
+          for _ in range(reps)]
+    sink = []
+    for r in range(reps):
+        for (e0, e1), o in zip(ev[r], q):
+            sink.append(scrub.sum())
+            e0.record(stream)
+            o["fn"]()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([[e0.elapsed_time(e1) for e0, e1 in row] for row in ev]).mean(axis=0)
+    del scrub, sink
+    gbs = sum(o["bytes"] for o in q) / (ms.sum() * 1e-3) / 1e9
+    out = {"achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "method": f"each launch alone after a {scrub_mib} MiB read that evicts the caches (mean of {reps})",
+           "per_launch": [{"op": o["name"], "ms": round(float(m), 5), "gbs": _rate(o["bytes"], float(m), 1e9)}
+                          for o, m in zip(q, ms)]}
+    if copy_gbs:
+        out["frac_of_copy"] = round(gbs / copy_gbs, 4)
+    return out
 
 
 def copy_ceiling(torch, fq, dev, mib=1024, reps=10):
