@@ -423,3 +423,54 @@ def test_short_contraction_on_large_tiles(K):
     Xw = synth.random_bf16((K, M), seed=703 + K, outliers=True)
     checked(run_wgrad(dY, Xw, ncols=_sample(N, 96, K + 1), kcols=_sample(M, 96, K + 2)),
             f"wgrad over {K} tokens on 256x256 tiles")
+
+
+# ------------------------------------------------------------------------------------------
+# every operand-format pair through every product, on each kernel form the planner picks
+# ------------------------------------------------------------------------------------------
+
+PAIRS = [(E4, E4), (E4, E5), (E5, E4), (E5, E5)]
+
+
+def _expect_plan(op, shape, plan):
+    if not TILE_FORCED:
+        assert fq.fp8bq_gemm_plan(op, *shape) == plan, (shape, fq.fp8bq_gemm_plan(op, *shape))
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS)
+@pytest.mark.parametrize("shape,plan", [((256, 384, 256), (128, 128, 1)), ((2048, 512, 4096), (128, 128, 3)),
+                                        ((4096, 4096, 256), (256, 256, 1))])
+def test_fprop_every_format_pair(fa, fb, shape, plan):
+    """Each of the four instruction format pairs (the MFMA's per-operand format fields) on the
+    128x128 kernel, its split contraction and the 256x256 kernel."""
+    M, N, K = shape
+    _expect_plan(fq.OP_FPROP, shape, plan)
+    X = synth.random_bf16((M, K), seed=3001 + M + K, outliers=True)
+    W = synth.random_bf16((N, K), seed=3002 + N + K, std=0.02)
+    rows = _sample(M, 192, seed=M) if M > 512 else None
+    checked(run_fprop(X, W, fa, fb, rows=rows), f"fprop {shape} {fa}x{fb}")
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS)
+@pytest.mark.parametrize("shape,plan", [((256, 384, 256), (128, 128, 1)), ((4096, 4096, 256), (128, 128, 3)),
+                                        ((8192, 256, 2048), (256, 256, 1))])
+def test_dgrad_every_format_pair(fa, fb, shape, plan):
+    M, N, K = shape
+    _expect_plan(fq.OP_DGRAD, shape, plan)
+    dY = synth.random_bf16((M, N), seed=3003 + M + N, std=1e-3)
+    W = synth.random_bf16((N, K), seed=3004 + N + K, std=0.02)
+    rows = _sample(M, 192, seed=M + 1) if M > 512 else None
+    checked(run_dgrad(dY, W, fa, fb, rows=rows), f"dgrad {shape} {fa}x{fb}")
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS)
+@pytest.mark.parametrize("shape,plan", [((256, 384, 256), (128, 128, 1)), ((4096, 2048, 512), (128, 128, 3)),
+                                        ((2048, 4096, 4096), (256, 256, 1))])
+def test_wgrad_every_format_pair(fa, fb, shape, plan):
+    M, N, K = shape
+    _expect_plan(fq.OP_WGRAD, shape, plan)
+    dY = synth.random_bf16((M, N), seed=3005 + M + N, std=1e-3)
+    X = synth.random_bf16((M, K), seed=3006 + M + K, outliers=True)
+    ncols = _sample(N, 160, seed=N) if N > 512 else None
+    kcols = _sample(K, 160, seed=K + 1) if K > 512 else None
+    checked(run_wgrad(dY, X, fa, fb, ncols=ncols, kcols=kcols), f"wgrad {shape} {fa}x{fb}")
