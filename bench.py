@@ -352,7 +352,8 @@ def build_delayed(torch, fq, synth, dev):
 
 
 def run_hyperball(args, torch, fq, synth, dev):
-    """Hyperball update with projection of the four decoder weights (FP32 masters, BF16 gradients).
+    """Hyperball update with projection of the four decoder weights (FP32 masters, BF16 gradients),
+    all four in one batched call per step (per weight and one call per weight for comparison).
     Algorithmic bytes per element: the norms (of g, of w and of their product) must be known before
     any element is written, so g and w are read once for them (2 + 4) and then read again and w
     written in one update pass (2 + 4 + 4) = 16."""
@@ -368,19 +369,26 @@ def run_hyperball(args, torch, fq, synth, dev):
 
     calls = [fq.prepare(fq.fp8bq_hyperball_step, w, g, 1e-4, 0.1, 1e-8, radius, norms, ws)
              for _, w, g, radius, norms, ws, _ in items]
+    wsb = torch.empty(fq.fp8bq_hyperball_batch_workspace_size(len(items)), dtype=torch.uint8, device=dev)
+    batched = fq.prepare(fq.fp8bq_hyperball_step_batch, [(w, g, radius, norms) for _, w, g, radius, norms, _, _ in items],
+                         1e-4, 0.1, 1e-8, wsb)
 
-    def step():
+    def one_by_one():
         for c in calls:
             c()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    def timed(step):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t0) / args.steps
+
+    ms = timed(batched)  # the step: all four weights in one batched call (two launches)
+    ms_single = timed(one_by_one)  # for comparison: one call (two launches) per weight
     total = sum(it[-1] for it in items)
     gbs = total / (ms * 1e-3) / 1e9
     stream = torch.cuda.current_stream(dev)
@@ -398,6 +406,9 @@ def run_hyperball(args, torch, fq, synth, dev):
     print(json.dumps({"metric": "Hyperball update with fixed-radius projection, GB/s (16 B per weight element)",
                       "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(ms, 4),
                       "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "steps": args.steps,
+                      "step": "the four weights in one fp8bq_hyperball_step_batch call (two launches)",
+                      "one_call_per_weight": {"ms_per_step": round(ms_single, 4),
+                                              "gbs": round(total / (ms_single * 1e-3) / 1e9, 1)},
                       "config": {"workload": "decoder-block weights (QKV, O, gate+up, down), FP32 masters, "
                                              "BF16 gradients"},
                       "per_weight": per}), flush=True)

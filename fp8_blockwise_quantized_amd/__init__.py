@@ -13,6 +13,7 @@ Raw entry points (same names and argument order as the C ABI, tensors in place o
     fp8bq_quantize_weight_128x128(w, fmt, q, s)
     fp8bq_quantize_weight_dual(w, fmt, q, s, qt)
     fp8bq_quantize_weights_dual(jobs, fmt)    jobs: up to 16 (w, q, s, qt) tuples, one launch
+    fp8bq_hyperball_step_batch(jobs, lr, wd, eps, ws)  jobs: up to 32 (w, g, radius, norms) tuples, two launches
     fp8bq_gemm_fprop(qx, sx, fx, qw, sw, fw, y, ws=None)
     fp8bq_gemm_dgrad(qdy, sdy, fdy, qw, sw, fw, dx, ws=None)
     fp8bq_gemm_dgrad_wt(qdy, sdy, fdy, qwt, sw, fw, dx, ws=None)
@@ -78,6 +79,15 @@ class WeightJob(ctypes.Structure):
 
 MAX_WEIGHT_JOBS = 16
 
+
+class HyperballJob(ctypes.Structure):
+    """fp8bq_hyperball_job of the C ABI: one matrix of fp8bq_hyperball_step_batch."""
+    _fields_ = [("w", ctypes.c_void_p), ("ldw", ctypes.c_int64), ("g", ctypes.c_void_p), ("ldg", ctypes.c_int64),
+                ("R", ctypes.c_int64), ("C", ctypes.c_int64), ("radius", ctypes.c_double), ("norms", ctypes.c_void_p)]
+
+
+MAX_HYPERBALL_JOBS = 32
+
 _SIGS = {
     "fp8bq_quantize_act_1x128": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
     "fp8bq_quantize_act_128x1": [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp],
@@ -109,11 +119,15 @@ _SIGS = {
     "fp8bq_gemm_workspace_size": [_c_int, _c_i64, _c_i64, _c_i64],
     "fp8bq_gemm_plan": [_c_int, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
     "fp8bq_stream_copy": [_c_vp, _c_vp, _c_sz, _c_vp],
+    "fp8bq_hyperball_batch_workspace_size": [_c_int],
+    "fp8bq_hyperball_step_batch": [ctypes.POINTER(HyperballJob), _c_int, _c_int, ctypes.c_double, ctypes.c_double,
+                                   ctypes.c_double, _c_vp, _c_sz, _c_vp],
     "fp8bq_status_string": [_c_int],
     "fp8bq_version": [],
 }
 _RESTYPES = {"fp8bq_gemm_workspace_size": _c_sz, "fp8bq_quantize_tensor_workspace_size": _c_sz,
              "fp8bq_hyperball_workspace_size": _c_sz,
+             "fp8bq_hyperball_batch_workspace_size": _c_sz,
              "fp8bq_status_string": ctypes.c_char_p}
 
 _lib = None
@@ -446,6 +460,31 @@ def fp8bq_stream_copy(src, dst):
     return (_ptr(src), _ptr(dst), nbytes, _stream(src))
 
 
+def fp8bq_hyperball_batch_workspace_size(count):
+    return int(lib().fp8bq_hyperball_batch_workspace_size(int(count)))
+
+
+@_entry
+def fp8bq_hyperball_step_batch(jobs, lr, weight_decay, eps, ws):
+    """jobs: (w, g, radius, norms) per matrix, as fp8bq_hyperball_step takes them (norms None or a
+    two-element FP32 tensor); every g of one dtype.  Two launches on the current stream of the first
+    weight's device for all of them."""
+    jobs = list(jobs)
+    arr = (HyperballJob * max(len(jobs), 1))()
+    gt = _in_type(jobs[0][1]) if jobs else IN_BF16
+    if any(_in_type(job[1]) != gt for job in jobs):
+        raise TypeError("all gradients of one fp8bq_hyperball_step_batch call must share one dtype")
+    for i, (w, g, radius, norms) in enumerate(jobs):
+        R, C = w.shape
+        _expect_all([(jobs[0][0], "jobs[0].w", jobs[0][0].shape, _F32), (w, f"jobs[{i}].w", (R, C), _F32),
+                     (g, f"jobs[{i}].g", (R, C), _HI), (norms, f"jobs[{i}].norms", (2,), _F32)], ws)
+        arr[i] = HyperballJob(w.data_ptr(), _ld(w), g.data_ptr(), _ld(g), R, C, float(radius),
+                              norms.data_ptr() if norms is not None else None)
+    wsp, wsb = _ws_args(ws)
+    stream = _stream(jobs[0][0]) if jobs else ctypes.c_void_p(0)
+    return (arr, len(jobs), gt, float(lr), float(weight_decay), float(eps), wsp, wsb, stream)
+
+
 # ---------------------------------------------------------------------------------------------
 # allocating helpers
 # ---------------------------------------------------------------------------------------------
@@ -599,4 +638,29 @@ def hyperball_step(w, g, lr=1e-4, weight_decay=0.1, eps=1e-8, radius=0.0, ws=Non
     if ws is None:
         ws = torch.empty(max(fp8bq_hyperball_workspace_size(*w.shape), 16), dtype=torch.uint8, device=w.device)
     fp8bq_hyperball_step(w, g, lr, weight_decay, eps, radius, norms, ws)
+    return norms
+
+
+def hyperball_step_batch(weights, grads, lr=1e-4, weight_decay=0.1, eps=1e-8, radii=None, ws=None):
+    """In-place Hyperball updates of many FP32 weights, MAX_HYPERBALL_JOBS per launch pair; grads
+    of one dtype; radii: None (no projection) or one radius per weight.  Returns an [n, 2] FP32
+    device tensor of (||g||, ||w|| after the update and before the projection) per weight."""
+    weights, grads = list(weights), list(grads)
+    if len(weights) != len(grads):
+        raise ValueError("one gradient per weight")
+    radii = [0.0] * len(weights) if radii is None else [float(r) for r in radii]
+    if len(radii) != len(weights):
+        raise ValueError("one radius per weight")
+    if not weights:
+        return torch.empty((0, 2), dtype=torch.float32)
+    dev = weights[0].device
+    norms = torch.empty((len(weights), 2), dtype=torch.float32, device=dev)
+    n = min(len(weights), MAX_HYPERBALL_JOBS)
+    if ws is None:
+        ws = torch.empty(fp8bq_hyperball_batch_workspace_size(n), dtype=torch.uint8, device=dev)
+    for i in range(0, len(weights), MAX_HYPERBALL_JOBS):
+        sl = slice(i, i + MAX_HYPERBALL_JOBS)
+        fp8bq_hyperball_step_batch([(w, g, r, norms[k]) for k, (w, g, r) in
+                                    zip(range(i, i + MAX_HYPERBALL_JOBS), zip(weights[sl], grads[sl], radii[sl]))],
+                                   lr, weight_decay, eps, ws)
     return norms

@@ -320,6 +320,46 @@ int fp8bq_hyperball_step(float* w, int64_t ldw, const void* g, fp8bq_in gt, int6
                                         (hipStream_t)stream));
 }
 
+size_t fp8bq_hyperball_batch_workspace_size(int count) {
+  return (count < 0 || count > kMaxHyperballJobs) ? 0 : (size_t)count * kHyperballWorkspace;
+}
+
+int fp8bq_hyperball_step_batch(const fp8bq_hyperball_job* jobs, int count, fp8bq_in gt, double lr,
+                               double weight_decay, double eps, void* ws, size_t ws_bytes, void* stream) {
+  static_assert(FP8BQ_MAX_HYPERBALL_JOBS == kMaxHyperballJobs, "batch limit");
+  HyperballJobArgs a[kMaxHyperballJobs];
+  bool empty[kMaxHyperballJobs] = {};
+  const int n = (count >= 0 && count <= kMaxHyperballJobs) ? count : 0;
+  for (int j = 0; j < n; ++j)
+    a[j] = HyperballJobArgs{jobs ? jobs[j].w : nullptr, jobs ? jobs[j].ldw : 0, jobs ? jobs[j].g : nullptr,
+                            jobs ? jobs[j].ldg : 0, jobs ? jobs[j].R : 0, jobs ? jobs[j].C : 0,
+                            jobs ? jobs[j].radius : 0.0, jobs ? jobs[j].norms : nullptr};
+  int st = validate_hyperball_batch(jobs ? a : nullptr, count, kMaxHyperballJobs, (int)gt, lr, weight_decay, eps, ws,
+                                    ws_bytes, fp8bq_hyperball_batch_workspace_size(count), empty);
+  if (st != kOk) return st;
+  HyperballBatch b{};
+  b.partial = reinterpret_cast<double*>(ws);
+  uint32_t blocks = 0;
+  for (int j = 0; j < count; ++j) {
+    if (empty[j]) continue;
+    const int k = b.count++;
+    b.w[k] = jobs[j].w;
+    b.g[k] = jobs[j].g;
+    b.ldw[k] = jobs[j].ldw;
+    b.ldg[k] = jobs[j].ldg;
+    b.R[k] = jobs[j].R;
+    b.C[k] = jobs[j].C;
+    b.radius[k] = jobs[j].radius;
+    b.norms[k] = jobs[j].norms;
+    b.start[k] = blocks;
+    blocks += (uint32_t)hyperball_blocks(jobs[j].R);
+  }
+  if (b.count == 0) return kOk;
+  b.start[b.count] = blocks;
+  if ((st = current_device(nullptr)) != kOk) return st;
+  return launched(launch_hyperball_batch(b, (int)gt, lr, weight_decay, eps, (hipStream_t)stream));
+}
+
 int fp8bq_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
   bool empty = false;
   int st = validate_stream_copy(src, dst, bytes, &empty);

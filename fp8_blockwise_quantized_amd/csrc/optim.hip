@@ -63,22 +63,22 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 
 // Visit 8-element chunks: rows strided by the grid, kRowsPerIter rows per iteration so each thread
 // keeps several loads in flight.
+// (bid, nblk): this block's index among the nblk blocks that sweep the matrix.
 template <typename F>
-__device__ __forceinline__ void for_rows(int64_t R, int64_t C, F&& f) {
+__device__ __forceinline__ void for_rows(int64_t R, int64_t C, uint32_t bid, uint32_t nblk, F&& f) {
   const int64_t chunks = C / 8;
-  for (int64_t r0 = (int64_t)blockIdx.x * kRowsPerIter; r0 < R; r0 += (int64_t)gridDim.x * kRowsPerIter)
+  for (int64_t r0 = (int64_t)bid * kRowsPerIter; r0 < R; r0 += (int64_t)nblk * kRowsPerIter)
     for (int64_t c8 = threadIdx.x; c8 < chunks; c8 += blockDim.x) f(r0, 8 * c8);
 }
 
-// Pass 1: the block's fp64 sums of g*g and, with WITH_W, of w*w and w*g, into partial[b],
-// partial[kHyperballBlocks + b] and partial[2 * kHyperballBlocks + b].
+// Pass 1: block bid's fp64 sums of g*g and, with WITH_W, of w*w and w*g, into partial[bid],
+// partial[kHyperballBlocks + bid] and partial[2 * kHyperballBlocks + bid].
 template <typename TG, bool WITH_W>
-__global__ __launch_bounds__(256) void hyperball_sums_kernel(const float* __restrict__ w, int64_t ldw,
-                                                             const TG* __restrict__ g, int64_t ldg, int64_t R,
-                                                             int64_t C, double* __restrict__ partial) {
-  __shared__ double red[4];
+__device__ __forceinline__ void sums_body(const float* __restrict__ w, int64_t ldw, const TG* __restrict__ g,
+                                          int64_t ldg, int64_t R, int64_t C, double* __restrict__ partial,
+                                          uint32_t bid, uint32_t nblk, double* red) {
   double sgg = 0.0, sww = 0.0, swg = 0.0;
-  for_rows(R, C, [&](int64_t r0, int64_t c) {
+  for_rows(R, C, bid, nblk, [&](int64_t r0, int64_t c) {
     float gv[kRowsPerIter][8], wv[kRowsPerIter][8];
 #pragma unroll
     for (int i = 0; i < kRowsPerIter; ++i)
@@ -102,15 +102,23 @@ __global__ __launch_bounds__(256) void hyperball_sums_kernel(const float* __rest
       }
   });
   double t = block_sum(sgg, red);
-  if (threadIdx.x == 0) partial[blockIdx.x] = t;
+  if (threadIdx.x == 0) partial[bid] = t;
   if constexpr (WITH_W) {
     __syncthreads();
     t = block_sum(sww, red);
-    if (threadIdx.x == 0) partial[kHyperballBlocks + blockIdx.x] = t;
+    if (threadIdx.x == 0) partial[kHyperballBlocks + bid] = t;
     __syncthreads();
     t = block_sum(swg, red);
-    if (threadIdx.x == 0) partial[2 * kHyperballBlocks + blockIdx.x] = t;
+    if (threadIdx.x == 0) partial[2 * kHyperballBlocks + bid] = t;
   }
+}
+
+template <typename TG, bool WITH_W>
+__global__ __launch_bounds__(256) void hyperball_sums_kernel(const float* __restrict__ w, int64_t ldw,
+                                                             const TG* __restrict__ g, int64_t ldg, int64_t R,
+                                                             int64_t C, double* __restrict__ partial) {
+  __shared__ double red[4];
+  sums_body<TG, WITH_W>(w, ldw, g, ldg, R, C, partial, blockIdx.x, gridDim.x, red);
 }
 
 // Fixed-order sum of n partials by one block of 256 threads; every thread gets the result.
@@ -131,12 +139,11 @@ __device__ __forceinline__ double sum_partials(const double* partial, int n, dou
 // With WITH_W the updated weight's norm comes from the sums of pass 1; block 0 reports ||g|| and
 // that norm if asked.
 template <typename TG, bool WITH_W, bool PROJ>
-__global__ __launch_bounds__(256) void hyperball_update_kernel(float* __restrict__ w, int64_t ldw,
-                                                               const TG* __restrict__ g, int64_t ldg, int64_t R,
-                                                               int64_t C, float d, const double* __restrict__ partial,
-                                                               int np, double lr, double eps, double radius,
-                                                               float* __restrict__ norms) {
-  __shared__ double red[4];
+__device__ __forceinline__ void update_body(float* __restrict__ w, int64_t ldw, const TG* __restrict__ g, int64_t ldg,
+                                            int64_t R, int64_t C, float d, const double* __restrict__ partial,
+                                            double lr, double eps, double radius, float* __restrict__ norms,
+                                            uint32_t bid, uint32_t nblk, double* red) {
+  const int np = (int)nblk;
   const double sgg = sum_partials(partial, np, red);
   const double gn = __builtin_sqrt(sgg);
   const double n = gn > eps ? gn : eps;
@@ -150,10 +157,10 @@ __global__ __launch_bounds__(256) void hyperball_update_kernel(float* __restrict
     wn2 = wn2 > 0.0 ? wn2 : 0.0;  // (rounding can only push an exactly zero weight below zero)
     const double wn = __builtin_sqrt(wn2);
     if (PROJ && wn > 0.0) f = (float)(radius / wn);
-    if (norms && blockIdx.x == 0 && threadIdx.x == 0) norms[1] = (float)wn;
+    if (norms && bid == 0 && threadIdx.x == 0) norms[1] = (float)wn;
   }
-  if (norms && blockIdx.x == 0 && threadIdx.x == 0) norms[0] = (float)gn;
-  for_rows(R, C, [&](int64_t r0, int64_t col) {
+  if (norms && bid == 0 && threadIdx.x == 0) norms[0] = (float)gn;
+  for_rows(R, C, bid, nblk, [&](int64_t r0, int64_t col) {
     float wv[kRowsPerIter][8], gv[kRowsPerIter][8];
 #pragma unroll
     for (int i = 0; i < kRowsPerIter; ++i)
@@ -175,6 +182,59 @@ __global__ __launch_bounds__(256) void hyperball_update_kernel(float* __restrict
 }
 
 template <typename TG, bool WITH_W, bool PROJ>
+__global__ __launch_bounds__(256) void hyperball_update_kernel(float* __restrict__ w, int64_t ldw,
+                                                               const TG* __restrict__ g, int64_t ldg, int64_t R,
+                                                               int64_t C, float d, const double* __restrict__ partial,
+                                                               double lr, double eps, double radius,
+                                                               float* __restrict__ norms) {
+  __shared__ double red[4];
+  update_body<TG, WITH_W, PROJ>(w, ldw, g, ldg, R, C, d, partial, lr, eps, radius, norms, blockIdx.x, gridDim.x, red);
+}
+
+// Several matrices per launch: the blocks of job j are start[j] .. start[j+1]-1, hyperball_blocks(R)
+// of them as a single call would launch, each with that call's block index, so every job gets the
+// single call's partial sums, reduction order and results, bit for bit.  A job uses the projection
+// when its radius is positive and the w sums when it has a radius or reports norms, as a single
+// call does; the job search is a scalar scan over at most kMaxHyperballJobs prefix sums.
+__device__ __forceinline__ int batch_job(const HyperballBatch& b, uint32_t blk) {
+  int j = 0;
+  while (j + 1 < b.count && blk >= b.start[j + 1]) ++j;
+  return __builtin_amdgcn_readfirstlane(j);
+}
+
+template <typename TG>
+__global__ __launch_bounds__(256) void hyperball_sums_batch_kernel(HyperballBatch b) {
+  __shared__ double red[4];
+  const int j = batch_job(b, blockIdx.x);
+  const uint32_t bid = blockIdx.x - b.start[j], nblk = b.start[j + 1] - b.start[j];
+  double* partial = b.partial + (size_t)j * 3 * kHyperballBlocks;
+  const TG* g = (const TG*)b.g[j];
+  if (b.radius[j] > 0.0 || b.norms[j] != nullptr)
+    sums_body<TG, true>(b.w[j], b.ldw[j], g, b.ldg[j], b.R[j], b.C[j], partial, bid, nblk, red);
+  else
+    sums_body<TG, false>(b.w[j], b.ldw[j], g, b.ldg[j], b.R[j], b.C[j], partial, bid, nblk, red);
+}
+
+template <typename TG>
+__global__ __launch_bounds__(256) void hyperball_update_batch_kernel(HyperballBatch b, float d, double lr,
+                                                                     double eps) {
+  __shared__ double red[4];
+  const int j = batch_job(b, blockIdx.x);
+  const uint32_t bid = blockIdx.x - b.start[j], nblk = b.start[j + 1] - b.start[j];
+  const double* partial = b.partial + (size_t)j * 3 * kHyperballBlocks;
+  const TG* g = (const TG*)b.g[j];
+  if (b.radius[j] > 0.0)
+    update_body<TG, true, true>(b.w[j], b.ldw[j], g, b.ldg[j], b.R[j], b.C[j], d, partial, lr, eps, b.radius[j],
+                                b.norms[j], bid, nblk, red);
+  else if (b.norms[j] != nullptr)
+    update_body<TG, true, false>(b.w[j], b.ldw[j], g, b.ldg[j], b.R[j], b.C[j], d, partial, lr, eps, 0.0,
+                                 b.norms[j], bid, nblk, red);
+  else
+    update_body<TG, false, false>(b.w[j], b.ldw[j], g, b.ldg[j], b.R[j], b.C[j], d, partial, lr, eps, 0.0,
+                                  nullptr, bid, nblk, red);
+}
+
+template <typename TG, bool WITH_W, bool PROJ>
 hipError_t launch_pair(float* w, int64_t ldw, const TG* g, int64_t ldg, int64_t R, int64_t C, float d, double lr,
                        double eps, double radius, float* norms, double* partial, int nb, hipStream_t st) {
   hipLaunchKernelGGL((hyperball_sums_kernel<TG, WITH_W>), dim3(nb), dim3(256), 0, st, (const float*)w, ldw, g, ldg, R,
@@ -182,7 +242,17 @@ hipError_t launch_pair(float* w, int64_t ldw, const TG* g, int64_t ldg, int64_t 
   const hipError_t e = hipGetLastError();  // a failed launch stops the call before the update
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((hyperball_update_kernel<TG, WITH_W, PROJ>), dim3(nb), dim3(256), 0, st, w, ldw, g, ldg, R, C, d,
-                     (const double*)partial, nb, lr, eps, radius, norms);
+                     (const double*)partial, lr, eps, radius, norms);
+  return hipGetLastError();
+}
+
+template <typename TG>
+hipError_t launch_batch_t(const HyperballBatch& b, float d, double lr, double eps, hipStream_t st) {
+  const unsigned grid = b.start[b.count];
+  hipLaunchKernelGGL((hyperball_sums_batch_kernel<TG>), dim3(grid), dim3(256), 0, st, b);
+  const hipError_t e = hipGetLastError();  // a failed launch stops the call before the update
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((hyperball_update_batch_kernel<TG>), dim3(grid), dim3(256), 0, st, b, d, lr, eps);
   return hipGetLastError();
 }
 
@@ -210,6 +280,12 @@ hipError_t launch_hyperball_step(float* w, int64_t ldw, const void* g, int gt, i
                                  hipStream_t st) {
   if (gt == 0) return launch_t<uint16_t>(w, ldw, g, ldg, R, C, lr, wd, eps, radius, norms, ws, st);
   return launch_t<float>(w, ldw, g, ldg, R, C, lr, wd, eps, radius, norms, ws, st);
+}
+
+hipError_t launch_hyperball_batch(const HyperballBatch& b, int gt, double lr, double wd, double eps, hipStream_t st) {
+  const float d = (float)(1.0 - lr * wd);
+  if (gt == 0) return launch_batch_t<uint16_t>(b, d, lr, eps, st);
+  return launch_batch_t<float>(b, d, lr, eps, st);
 }
 
 }  // namespace fp8bq

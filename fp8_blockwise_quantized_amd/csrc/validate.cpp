@@ -221,6 +221,45 @@ int validate_hyperball(const void* w, int64_t ldw, const void* g, int gt, int64_
   return kOk;
 }
 
+int validate_hyperball_batch(const HyperballJobArgs* jobs, int count, int max_jobs, int gt, double lr, double wd,
+                             double eps, const void* ws, size_t ws_bytes, size_t ws_needed, bool* empty) {
+  if (count < 0 || count > max_jobs) return kErrValue;
+  if (count > 0 && jobs == nullptr) return kErrNull;
+  if (in_esize(gt) == 0) return kErrDtype;
+  if (!finite_nonneg(lr) || !finite_nonneg(wd) || !(finite_nonneg(eps) && eps > 0.0)) return kErrValue;
+  bool any = false;
+  for (int j = 0; j < count; ++j) {
+    const HyperballJobArgs& a = jobs[j];
+    // each job alone, with a stand-in workspace (the batch's is checked once below)
+    alignas(16) static const double kStandIn[2] = {0.0, 0.0};
+    int st = validate_hyperball(a.w, a.ldw, a.g, gt, a.ldg, a.R, a.C, lr, wd, eps, a.radius, a.norms, kStandIn,
+                                ws_needed, 0, &empty[j]);
+    if (st != kOk) return st;
+    any = any || !empty[j];
+  }
+  if (!any) return kOk;
+  if (ws == nullptr) return kErrNull;
+  if (!aligned16(ws)) return kErrAlign;
+  if (ws_bytes < ws_needed) return kErrWorkspace;
+  const Mat mws{ws, 1, (int64_t)ws_needed, (int64_t)ws_needed, 1};
+  const int es = in_esize(gt);
+  for (int j = 0; j < count; ++j) {
+    if (empty[j]) continue;
+    const HyperballJobArgs& a = jobs[j];
+    const Mat wj{a.w, a.R, a.C, a.ldw, 4}, gj{a.g, a.R, a.C, a.ldg, es}, nj{a.norms, 1, 2, 2, 4};
+    if (overlaps(wj, mws) || overlaps(gj, mws) || (a.norms && overlaps(nj, mws))) return kErrOverlap;
+    for (int k = 0; k < count; ++k) {
+      if (k == j || empty[k]) continue;
+      const HyperballJobArgs& b = jobs[k];
+      const Mat wk{b.w, b.R, b.C, b.ldw, 4}, gk{b.g, b.R, b.C, b.ldg, es}, nk{b.norms, 1, 2, 2, 4};
+      // job j writes w and norms: neither may touch anything job k reads or writes
+      if (overlaps(wj, wk) || overlaps(wj, gk) || (b.norms && overlaps(wj, nk))) return kErrOverlap;
+      if (a.norms && (overlaps(nj, wk) || overlaps(nj, gk) || (b.norms && overlaps(nj, nk)))) return kErrOverlap;
+    }
+  }
+  return kOk;
+}
+
 int validate_stream_copy(const void* src, const void* dst, size_t bytes, bool* empty) {
   *empty = false;
   if (bytes % 16 != 0 || bytes >= ((size_t)1 << 48)) return kErrShape;

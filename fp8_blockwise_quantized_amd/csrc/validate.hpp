@@ -75,6 +75,19 @@ int validate_hyperball(const void* w, int64_t ldw, const void* g, int gt, int64_
 // ranges disjoint.
 int validate_stream_copy(const void* src, const void* dst, size_t bytes, bool* empty);
 
+// Several Hyperball steps: count in [0, max_jobs]; each job as validate_hyperball (empty[j] set per
+// job; lr, wd, eps shared); no job's written memory (w, norms) may overlap another job's w, g or
+// norms, or the workspace.  ws >= ws_needed bytes when any job is non-empty.
+struct HyperballJobArgs {
+  const void* w; int64_t ldw;
+  const void* g; int64_t ldg;
+  int64_t R, C;
+  double radius;
+  const void* norms;
+};
+int validate_hyperball_batch(const HyperballJobArgs* jobs, int count, int max_jobs, int gt, double lr, double wd,
+                             double eps, const void* ws, size_t ws_bytes, size_t ws_needed, bool* empty);
+
 // The three GEMMs share one validator: op selects the operand shapes.
 struct GemmArgs {
   int op;

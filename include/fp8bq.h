@@ -27,8 +27,8 @@
  *   launched before it stay enqueued.
  * - Outputs are fully overwritten, with three documented exceptions that update caller memory in
  *   place: FP8BQ_OUT_F32_ACCUM (fp8bq_gemm_wgrad adds its result to the FP32 output), the running
- *   amax of fp8bq_quantize_tensor_delayed[_noalloc] (read and updated), and the weight of
- *   fp8bq_hyperball_step (read and updated).
+ *   amax of fp8bq_quantize_tensor_delayed[_noalloc] (read and updated), and the weights of
+ *   fp8bq_hyperball_step and fp8bq_hyperball_step_batch (read and updated).
  * - Calls are thread-safe and re-entrant; there is no mutable global state besides a per-device
  *   cache of the device's architecture check.  Calls that write overlapping outputs on the same
  *   device must be ordered by the caller (same stream or events).
@@ -372,6 +372,39 @@ size_t fp8bq_hyperball_workspace_size(int64_t R, int64_t C);
 int fp8bq_hyperball_step(float* w, int64_t ldw, const void* g, fp8bq_in gt, int64_t ldg, int64_t R, int64_t C,
                          double lr, double weight_decay, double eps, double radius, float* norms, void* ws,
                          size_t ws_bytes, void* stream);
+
+/*
+ * Several Hyperball steps in one launch pair, for many weight matrices (callers that update a model
+ * layer by layer would otherwise pay two launches per matrix).  Each job is exactly one
+ * fp8bq_hyperball_step call: same rule, same per-matrix norms, and bit-identical weights and norms
+ * (the same block decomposition and reduction order per matrix).  Defining passages as for
+ * fp8bq_hyperball_step.
+ *
+ *   jobs[j]  w [R, C] FP32 (ldw >= C), read and written; g [R, C] of element type gt (ldg >= C);
+ *            C % 8 == 0; radius >= 0 and finite (0: no projection); norms NULL or two 4-byte-aligned
+ *            device floats (||g||, ||w|| after the update, before the projection).  A job with
+ *            R == 0 or C == 0 is skipped (its pointers are not read).
+ *   count    0 .. FP8BQ_MAX_HYPERBALL_JOBS (else FP8BQ_ERR_VALUE); 0 is a no-op.
+ *   gt, lr, weight_decay, eps  shared by every job, as for fp8bq_hyperball_step.
+ *   ws       at least fp8bq_hyperball_batch_workspace_size(count) bytes, 16-byte aligned (may be NULL
+ *            when every job is empty).
+ * The host array jobs is read during the call only.  Errors: as fp8bq_hyperball_step for any job
+ * (the first failing job's status); FP8BQ_ERR_OVERLAP also when a job's w or norms overlaps another
+ * job's w, g or norms, or any job's memory overlaps ws.  On an error nothing is enqueued.
+ */
+#define FP8BQ_MAX_HYPERBALL_JOBS 32
+typedef struct {
+  float* w;
+  int64_t ldw;
+  const void* g;
+  int64_t ldg;
+  int64_t R, C;
+  double radius;
+  float* norms;
+} fp8bq_hyperball_job;
+size_t fp8bq_hyperball_batch_workspace_size(int count);
+int fp8bq_hyperball_step_batch(const fp8bq_hyperball_job* jobs, int count, fp8bq_in gt, double lr,
+                               double weight_decay, double eps, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes the given GEMM needs at these sizes on the current device (0 if none).
  * Returns 0 for invalid arguments too; the GEMM call itself reports those. */

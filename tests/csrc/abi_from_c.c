@@ -58,6 +58,16 @@ int main(void) {
   static float w[256 * 256];
   EXPECT(fp8bq_hyperball_step(w, 256, x, FP8BQ_IN_BF16, 256, 256, 256, 1e-4, 0.1, 0.0, 0.0, NULL, ws, sizeof ws,
                               NULL) == FP8BQ_ERR_VALUE);     /* eps must be > 0 */
+  /* several Hyperball steps: too many jobs, one job's weights on another's gradient, none */
+  fp8bq_hyperball_job hj[2] = {{w, 256, x, 256, 256, 256, 0.0, NULL}, {w + 256 * 256 / 2, 256, x, 256, 128, 256, 1.0, NULL}};
+  EXPECT(fp8bq_hyperball_batch_workspace_size(FP8BQ_MAX_HYPERBALL_JOBS + 1) == 0);
+  EXPECT(fp8bq_hyperball_step_batch(hj, FP8BQ_MAX_HYPERBALL_JOBS + 1, FP8BQ_IN_BF16, 1e-4, 0.1, 1e-8, ws, sizeof ws,
+                                    NULL) == FP8BQ_ERR_VALUE);
+  static double hws[2 * 3 * 1024];                          /* two jobs' partial sums (16-byte aligned) */
+  EXPECT(fp8bq_hyperball_batch_workspace_size(2) <= sizeof hws);
+  EXPECT(fp8bq_hyperball_step_batch(hj, 2, FP8BQ_IN_BF16, 1e-4, 0.1, 1e-8, hws, sizeof hws, NULL) ==
+         FP8BQ_ERR_OVERLAP);                                  /* job 1's w lies inside job 0's w */
+  EXPECT(fp8bq_hyperball_step_batch(hj, 0, FP8BQ_IN_BF16, 1e-4, 0.1, 1e-8, NULL, 0, NULL) == FP8BQ_OK);
   /* the streaming-copy reference: a size not a multiple of 16, overlapping ranges, empty */
   EXPECT(fp8bq_stream_copy(w, q, 100, NULL) == FP8BQ_ERR_SHAPE);
   EXPECT(fp8bq_stream_copy(w, (uint8_t*)w + 256, 1024, NULL) == FP8BQ_ERR_OVERLAP);

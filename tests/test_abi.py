@@ -36,7 +36,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fq.lib()
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -350,6 +350,44 @@ def test_hyperball_validation():
     assert hb(ws_bytes=need - 1) == WORKSPACE
     assert hb(g=P(0)) == OVERLAP  # gradient on top of the weights
     assert hb(norms=ctypes.c_void_p(0x100000 + 64)) == OVERLAP  # norms inside w
+
+
+def hbb(jobs, count=None, gt=0, lr=1e-4, wd=0.1, eps=1e-8, ws=P(9), ws_bytes=None):
+    """fp8bq_hyperball_step_batch on fake pointers; jobs: dicts of HyperballJob fields."""
+    n = len(jobs) if count is None else count
+    arr = (fq.HyperballJob * max(len(jobs), 1))()
+    for i, j in enumerate(jobs):
+        arr[i] = fq.HyperballJob(**j)
+    need = fq.fp8bq_hyperball_batch_workspace_size(max(n, 0))
+    return fq.lib().fp8bq_hyperball_step_batch(arr, n, gt, lr, wd, eps, ws, need if ws_bytes is None else ws_bytes, S0)
+
+
+def hbjob(i, R=256, C=256, radius=0.0, norms=None):
+    """Job i on fake buffers 0x100000 * (2i + 1) (w) and 0x100000 * (2i + 2) (g)."""
+    return dict(w=0x100000 * (2 * i + 1), ldw=C, g=0x100000 * (2 * i + 2), ldg=C, R=R, C=C, radius=radius,
+                norms=norms)
+
+
+def test_hyperball_batch_validation():
+    assert fq.fp8bq_hyperball_batch_workspace_size(4) == 4 * fq.fp8bq_hyperball_workspace_size(256, 256)
+    assert fq.fp8bq_hyperball_batch_workspace_size(33) == 0 and fq.fp8bq_hyperball_batch_workspace_size(-1) == 0
+    two = [hbjob(0), hbjob(1, R=7, C=264, radius=2.0, norms=0x10000000)]
+    valid(lambda: hbb(two))
+    assert hbb([]) == OK and hbb([hbjob(0, R=0), hbjob(1, C=0)], ws=NUL) == OK  # nothing to do: ws unread
+    assert hbb(two, count=33) == VALUE and hbb(two, count=-1) == VALUE
+    assert fq.lib().fp8bq_hyperball_step_batch(None, 2, 0, 1e-4, 0.1, 1e-8, P(9), 1 << 20, S0) == NULL
+    assert hbb(two, gt=2) == DTYPE
+    assert hbb(two, eps=0.0) == VALUE and hbb([hbjob(0), hbjob(1, radius=-1.0)]) == VALUE
+    assert hbb([hbjob(0), hbjob(1, C=100)]) == SHAPE  # the second job's error
+    assert hbb(two, ws=NUL) == NULL and hbb(two, ws_bytes=1024) == WORKSPACE
+    assert hbb(two, ws=ctypes.c_void_p(0x900008)) == ALIGN
+    # one job's weights on top of another job's gradient, weights or norms; norms inside the workspace
+    assert hbb([hbjob(0), dict(hbjob(1), w=0x100000 * 2)]) == OVERLAP
+    assert hbb([hbjob(0), dict(hbjob(1), w=0x100000 * 1)]) == OVERLAP
+    assert hbb([hbjob(0, norms=0x10000000), dict(hbjob(1), w=0x10000000 - 64)]) == OVERLAP
+    assert hbb([hbjob(0, norms=0xA00000 + 64), hbjob(1)]) == OVERLAP  # the workspace is P(9) = 0xA00000
+    # two jobs may read one gradient
+    valid(lambda: hbb([hbjob(0), dict(hbjob(1), g=0x100000 * 2)]))
 
 
 def test_planner_decisions_documented_for_the_decoder_block():

@@ -96,3 +96,76 @@ def test_full_size_weight():
     norms = fq.hyperball_step(w, g.to(DEV), 1e-3, 0.1, 1e-8, radius)
     torch.cuda.synchronize()
     _check_step(w0, g, 1e-3, 0.1, 1e-8, radius, w.cpu().numpy(), norms.cpu().numpy(), "gate_up 11264x2048")
+
+
+# ------------------------------------------------------------------------------------------
+# several matrices per launch pair
+# ------------------------------------------------------------------------------------------
+
+def _batch_case(gdtype, n, seed):
+    """n matrices of mixed shapes (ragged rows, one past the 1024-block cap), radius and norms
+    mixed: with a radius and norms, norms only, neither."""
+    shapes = [(128, 128), (300, 264), (1, 8), (1027, 520), (4100, 64), (256, 2048)]
+    ws, gs, radii, want_norms = [], [], [], []
+    for i in range(n):
+        R, C = shapes[i % len(shapes)]
+        ws.append(synth.random_f32((R, C), seed=seed + 2 * i, std=0.02).to(DEV))
+        gs.append(synth.random_f32((R, C), seed=seed + 2 * i + 1, std=1e-3).to(gdtype).to(DEV))
+        radii.append([0.0, 3.0, 0.0][i % 3])
+        want_norms.append(i % 3 != 2)
+    return ws, gs, radii, want_norms
+
+
+@pytest.mark.parametrize("gdtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("n", [1, 5, fq.MAX_HYPERBALL_JOBS])
+def test_batch_matches_single_calls(gdtype, n):
+    """Weights and norms of one batched call equal those of one call per matrix, bit for bit, and
+    each matrix against the oracle."""
+    lr, wd, eps = 1e-2, 0.1, 1e-8
+    ws, gs, radii, want = _batch_case(gdtype, n, seed=700 + n)
+    w_single = [w.clone() for w in ws]
+    n_single = []
+    for w, g, r, k in zip(w_single, gs, radii, want):
+        norms = torch.zeros(2, dtype=torch.float32, device=DEV)
+        ws_buf = torch.empty(max(fq.fp8bq_hyperball_workspace_size(*w.shape), 16), dtype=torch.uint8, device=DEV)
+        fq.fp8bq_hyperball_step(w, g, lr, wd, eps, r, norms if k else None, ws_buf)
+        n_single.append(norms)
+    w0 = [w.cpu().numpy().copy() for w in ws]
+    norms_b = torch.zeros((n, 2), dtype=torch.float32, device=DEV)
+    wsb = torch.empty(fq.fp8bq_hyperball_batch_workspace_size(n), dtype=torch.uint8, device=DEV)
+    fq.fp8bq_hyperball_step_batch([(w, g, r, norms_b[i] if k else None) for i, (w, g, r, k) in
+                                   enumerate(zip(ws, gs, radii, want))], lr, wd, eps, wsb)
+    torch.cuda.synchronize()
+    for i in range(n):
+        assert torch.equal(ws[i], w_single[i]), f"weights of job {i}"
+        assert torch.equal(norms_b[i], n_single[i]), f"norms of job {i}"
+        if want[i]:
+            _check_step(w0[i], gs[i].cpu(), lr, wd, eps, radii[i], ws[i].cpu().numpy(), norms_b[i].cpu().numpy(),
+                        f"batch {n} job {i} {tuple(ws[i].shape)} R={radii[i]}")
+
+
+def test_batch_helper_over_the_job_limit():
+    """hyperball_step_batch splits more than MAX_HYPERBALL_JOBS matrices over several launch pairs."""
+    n = fq.MAX_HYPERBALL_JOBS + 3
+    ws, gs, _, _ = _batch_case(torch.bfloat16, n, seed=900)
+    ref = [w.clone() for w in ws]
+    ref_norms = torch.stack([fq.hyperball_step(w, g, 1e-3, 0.1, 1e-8, 2.0) for w, g in zip(ref, gs)])
+    norms = fq.hyperball_step_batch(ws, gs, 1e-3, 0.1, 1e-8, radii=[2.0] * n)
+    torch.cuda.synchronize()
+    assert torch.equal(norms, ref_norms)
+    assert all(torch.equal(a, b) for a, b in zip(ws, ref))
+
+
+def test_batch_error_enqueues_nothing():
+    """A batch whose second job writes onto the first job's gradient fails as a whole: nothing is
+    written, the valid job included."""
+    w0 = torch.full((256, 256), 1.5, dtype=torch.float32, device=DEV)
+    g0 = torch.full((256, 256), 0.25, dtype=torch.float32, device=DEV)
+    w1 = g0[:128]  # job 1's weights are job 0's gradient
+    g1 = torch.ones((128, 256), dtype=torch.float32, device=DEV)
+    wsb = torch.empty(fq.fp8bq_hyperball_batch_workspace_size(2), dtype=torch.uint8, device=DEV)
+    with pytest.raises(fq.Fp8bqError) as e:
+        fq.fp8bq_hyperball_step_batch([(w0, g0, 0.0, None), (w1, g1, 0.0, None)], 1e-2, 0.1, 1e-8, wsb)
+    assert e.value.status == 10  # FP8BQ_ERR_OVERLAP
+    torch.cuda.synchronize()
+    assert bool((w0 == 1.5).all()) and bool((g0 == 0.25).all())
