@@ -81,6 +81,14 @@ int main() {
       j = WeightJobArgs{pick_ptr(), R, C, pick_ld(C), pick_ptr(), pick_ld(C), pick_ptr(), pick_ld(C / 128),
                         pick_ptr(), pick_ld(R)};
     EXPECT(documented(validate_quant_weights_dual(jobs, (int)(rng() % 5) - 1, 16, xt, fmt, je)));
+    HyperballJobArgs hjobs[3];
+    bool he[3];
+    for (auto& j : hjobs)
+      j = HyperballJobArgs{pick_ptr(), pick_ld(C), pick_ptr(), pick_ld(C), rng() % 2 ? R : pick_size(), C,
+                           (double)(rng() % 3) - 0.5, rng() % 2 ? pick_ptr() : nullptr};
+    EXPECT(documented(validate_hyperball_batch(rng() % 8 ? hjobs : nullptr, (int)(rng() % 5) - 1, 32, xt, 1e-3, 0.1,
+                                               1e-8, pick_ptr(), (size_t)(rng() % 200000), 3 * 24576, he)));
+    EXPECT(documented(validate_stream_copy(pick_ptr(), pick_ptr(), (size_t)pick_size() * (rng() % 2 ? 16 : 1), &empty)));
 
     // the planner for any sizes, then the GEMM validator with its workspace requirement
     const int op = (int)(rng() % 5);
