@@ -609,8 +609,8 @@ def summarize(ops, dur_ms, med_ms=None, min_ms=None):
 
 # Kernel instance names as profilers print them: gemm_tn_kernel<OP, BM, BN, waves_m, waves_n, LDS
 # stages, scale mode, fmtA, fmtB, f32 out>; the tile shape comes from the library's plan query.
-_TILE_ARGS = {(128, 128): "128, 128, 2, 2, 2", (128, 256): "128, 256, 2, 4, 2", (256, 128): "256, 128, 4, 2, 2",
-              (256, 256): "256, 256, 2, 4, 2"}
+_TILE_ARGS = {(64, 64): "64, 64, 4, 1, 2", (128, 128): "128, 128, 2, 2, 2", (128, 256): "128, 256, 2, 4, 2",
+              (256, 128): "256, 128, 4, 2, 2", (256, 256): "256, 256, 2, 4, 2"}
 def gemm_kernel(fq, o):
     """(kernel name, isolated) of a GEMM call: o["plan"] is its plan query (op, M, N, K) and o["kid"]
     the kernel's (OP, scale mode) template arguments.  Isolated when the call launches that one kernel

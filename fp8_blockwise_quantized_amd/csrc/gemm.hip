@@ -177,7 +177,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   constexpr int MI = WTM / 16;
   constexpr int NI = WTN / 16;
   constexpr int SA_OFF = (BM + BN) * 128;
-  constexpr int NSB = SBM == kSbColumn ? BN : (BN / kGroup);
+  constexpr int NSB = SBM == kSbColumn ? BN : ((BN + kGroup - 1) / kGroup);  // (a 64-wide tile: one block)
   constexpr int SB_OFF = SA_OFF + BM * 4;
   constexpr int SINK_OFF = SB_OFF + (NSB > 64 ? NSB : 64) * 4;
   constexpr int STAGE = SINK_OFF + 256;
@@ -194,6 +194,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
   static_assert(ACHUNKS % NW == 0 && BCHUNKS % NW == 0, "tile chunks must split evenly over waves");
   static_assert(BM % 64 == 0 && (NSB <= 64 || NSB % 64 == 0), "scale jobs are 64 lanes wide");
   static_assert(SBM != kSbBlock128 || WTN <= 128, "a wave's columns must share one weight block");
+  static_assert(SBM != kSbBlock128 || BN % kGroup == 0 || kGroup % BN == 0, "a narrow tile lies in one weight block");
   static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "LDS ring does not fit");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
 
@@ -581,6 +582,7 @@ static hipError_t launch_fmt(const GemmDesc& d, const GemmPlan& p, float* partia
     case k128x256: return launch_variant<OP, 128, 256, 2, 4, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
     case k256x128: return launch_variant<OP, 256, 128, 4, 2, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
     case k256x256: return launch_variant<OP, 256, 256, 2, 4, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
+    case k64x64: return launch_variant<OP, 64, 64, 4, 1, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
     default: return launch_variant<OP, 128, 128, 2, 2, 2, SBM, FA, FB, OUTF32>(d, p, partial, st);
   }
 }

@@ -5,12 +5,12 @@
 
 namespace fp8bq {
 
-// FP8BQ_GEMM_TILE=<0|1|2|3> forces a tile shape (tuning aid); read once.
+// FP8BQ_GEMM_TILE=<0..4> forces a tile shape (a TileShape value; tuning aid); read once.
 static int forced_shape() {
   static const int v = [] {
     const char* e = std::getenv("FP8BQ_GEMM_TILE");
     const int x = e ? std::atoi(e) : -1;
-    return (x >= 0 && x <= 3) ? x : -1;
+    return (x >= 0 && x <= 4) ? x : -1;
   }();
   return v;
 }
@@ -19,8 +19,10 @@ static int64_t cdiv(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0);
 
 // Time of one contraction block for one round of resident work units, in microseconds, measured
 // on MI355X: two 128x128 workgroups per CU take ~1.2 us per block, one 256x256 workgroup ~2.05 us
-// (4x the work for 1.7x the time: half the operand traffic per flop).
-static double block_us(int shape) { return shape == k256x256 ? 2.05 : 1.2; }
+// (4x the work for 1.7x the time: half the operand traffic per flop), four 64x64 workgroups ~0.94 us
+// (half the work of two 128x128 ones for 0.8 of the time: that tile pays off only where the larger
+// ones leave compute units idle, i.e. few output rows).
+static double block_us(int shape) { return shape == k256x256 ? 2.05 : shape == k64x64 ? 0.94 : 1.2; }
 
 // Cost model in microseconds: rounds of resident units x blocks per unit x block time, plus, for a
 // split, a pass that writes and re-reads split x rows x cols FP32 partials and writes the output
@@ -83,11 +85,13 @@ GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count) {
   if (forced_shape() >= 0) {
     p.shape = forced_shape();
   } else if (work) {
-    // the faster of the two tile shapes under the cost model (ties go to the larger tile)
-    double c128 = 0.0, c256 = 0.0;
+    // the fastest tile shape under the cost model (ties go to the larger tile)
+    double c64 = 0.0, c128 = 0.0, c256 = 0.0;
+    best_split(rows, cols, nkb, cus * blocks_per_cu(k64x64), k64x64, &c64);
     best_split(rows, cols, nkb, cus * blocks_per_cu(k128x128), k128x128, &c128);
     best_split(rows, cols, nkb, cus * blocks_per_cu(k256x256), k256x256, &c256);
     p.shape = c256 <= c128 ? k256x256 : k128x128;
+    if (c64 < (p.shape == k256x256 ? c256 : c128)) p.shape = k64x64;
   } else {
     p.shape = k128x128;
   }

@@ -16,13 +16,19 @@ enum SbMode : int { kSbBlock128 = 0, kSbColumn = 1 };
 // fprop kernel with broadcast scales, planned as fprop.
 enum Op : int { kOpFprop = 0, kOpDgrad = 1, kOpWgrad = 2, kOpDgradWt = 3, kOpTensor = 4 };
 
-// Workgroup tile shapes (output rows x columns of one work unit).  All use 64x64 wave tiles:
-//   k128x128: 4 waves, two workgroups per CU;  k128x256 / k256x128 / k256x256: 8 waves, one
-//   workgroup per CU (k256x256 with 128x64 wave tiles).
-enum TileShape : int { k128x128 = 0, k128x256 = 1, k256x128 = 2, k256x256 = 3 };
-inline int tile_rows(int shape) { return (shape == k256x128 || shape == k256x256) ? 256 : 128; }
-inline int tile_cols(int shape) { return (shape == k128x256 || shape == k256x256) ? 256 : 128; }
-inline int blocks_per_cu(int shape) { return shape == k128x128 ? 2 : 1; }
+// Workgroup tile shapes (output rows x columns of one work unit):
+//   k128x128: 4 waves of 64x64, two workgroups per CU;
+//   k128x256 / k256x128: 8 waves of 64x64, one workgroup per CU (tuning shapes, never planned);
+//   k256x256: 8 waves of 128x64, one workgroup per CU;
+//   k64x64: 4 waves of 16x64, four workgroups per CU (few output rows: 4x the tiles of 128x128).
+enum TileShape : int { k128x128 = 0, k128x256 = 1, k256x128 = 2, k256x256 = 3, k64x64 = 4 };
+inline int tile_rows(int shape) {
+  return shape == k64x64 ? 64 : (shape == k256x128 || shape == k256x256) ? 256 : 128;
+}
+inline int tile_cols(int shape) {
+  return shape == k64x64 ? 64 : (shape == k128x256 || shape == k256x256) ? 256 : 128;
+}
+inline int blocks_per_cu(int shape) { return shape == k64x64 ? 4 : shape == k128x128 ? 2 : 1; }
 constexpr int kMaxSplit = 8;
 
 struct GemmPlan {

@@ -184,7 +184,7 @@ def test_gemm_plan_query():
         for (M, N, K) in [(256, 256, 256), (512, 2048, 2048), (16384, 2560, 2048), (16384, 11264, 2048),
                           (16384, 2048, 5632)]:
             tm, tn, sk = fq.fp8bq_gemm_plan(op, M, N, K)
-            assert (tm, tn) in [(128, 128), (128, 256), (256, 128), (256, 256)]
+            assert (tm, tn) in [(64, 64), (128, 128), (256, 256)]
             assert 1 <= sk <= 8
             rows, cols = {fq.OP_FPROP: (M, N), fq.OP_DGRAD: (M, K), fq.OP_WGRAD: (N, K), fq.OP_DGRAD_WT: (M, K),
                           fq.OP_TENSOR: (M, N)}[op]
@@ -394,7 +394,8 @@ def test_planner_decisions_documented_for_the_decoder_block():
     """Plans the design records (device of 256 compute units; no GPU here, or an MI355X): the step's
     fprop/dgrad on 256x256 tiles unsplit (the QKV fprop's half-filled last round is charged half a
     round, which moves it off 128x128); small-token fprops are not split (the reduction pass costs a
-    fixed launch); long-contraction wgrads with few output tiles are."""
+    fixed launch) and take 64x64 tiles up to 1024 tokens; long-contraction wgrads with few output
+    tiles are split."""
     if HAVE_GPU and torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("plans are recorded for 256 compute units")
     M = 16384
@@ -403,8 +404,10 @@ def test_planner_decisions_documented_for_the_decoder_block():
         assert fq.fp8bq_gemm_plan(fq.OP_DGRAD_WT, M, N, K) == (256, 256, 1), (K, N)
     assert fq.fp8bq_gemm_plan(fq.OP_WGRAD, M, 2560, 2048) == (256, 256, 3)
     assert fq.fp8bq_gemm_plan(fq.OP_WGRAD, M, 2048, 2048) == (128, 128, 2)
-    for tokens in (512, 1024, 2048, 4096):
-        assert fq.fp8bq_gemm_plan(fq.OP_FPROP, tokens, 2048, 2048)[2] == 1, tokens
+    # token sweep (N = K = 2048): 64x64 tiles while 128x128 ones would leave most CUs idle
+    for tokens, plan in ((512, (64, 64, 1)), (1024, (64, 64, 1)), (2048, (128, 128, 1)), (4096, (128, 128, 1)),
+                         (8192, (256, 256, 1))):
+        assert fq.fp8bq_gemm_plan(fq.OP_FPROP, tokens, 2048, 2048) == plan, tokens
     # the plan is a pure function of its arguments
     assert all(fq.fp8bq_gemm_plan(fq.OP_WGRAD, 8192, 4096, 1024) == fq.fp8bq_gemm_plan(fq.OP_WGRAD, 8192, 4096, 1024)
                for _ in range(3))

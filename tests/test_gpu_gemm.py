@@ -312,6 +312,22 @@ def test_large_tile_ragged_edges(out_dtype):
     checked(run_dgrad(dY, Wd, out_dtype=out_dtype), "256x256 ragged dgrad", f32)
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_mid_tile_ragged_edges(out_dtype):
+    """Shapes the planner runs on 128x128 tiles whose last tile row reaches past the output
+    (1100 = 8*128 + 76 rows); every output compared."""
+    f32 = out_dtype == torch.float32
+    M, N, K = 1100, 3072, 768
+    assert TILE_FORCED or fq.fp8bq_gemm_plan(fq.OP_FPROP, M, N, K) == (128, 128, 1)
+    X = synth.random_bf16((M, K), seed=311, outliers=True)
+    W = synth.random_bf16((N, K), seed=312, std=0.02)
+    checked(run_fprop(X, W, out_dtype=out_dtype), "128x128 ragged fprop", f32)
+    assert TILE_FORCED or fq.fp8bq_gemm_plan(fq.OP_DGRAD, M, K, N) == (128, 128, 1)
+    dY = synth.random_bf16((M, K), seed=313, std=1e-3)
+    Wd = synth.random_bf16((K, N), seed=314, std=0.02)
+    checked(run_dgrad(dY, Wd, out_dtype=out_dtype), "128x128 ragged dgrad", f32)
+
+
 @pytest.mark.parametrize("shape", [(4096, 4480, 2432), (16384, 2944, 1664)])
 def test_large_tile_wgrad(shape):
     """wgrad on 256x256 tiles: ragged output columns (2432 = 9.5 tiles) without a split, and ragged
@@ -356,7 +372,7 @@ def test_dgrad_wt_matches_dgrad_and_oracle(shape, out_dtype):
 # FP32 main-grad accumulation (wgrad epilogue option)
 # ------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("shape", [(2048, 256, 256), (512, 2048, 1536), (4096, 4480, 2432)])
+@pytest.mark.parametrize("shape", [(4096, 256, 256), (512, 2048, 1536), (4096, 4480, 2432)])
 def test_wgrad_fp32_accumulate(shape):
     """Two micro-batches accumulated into one FP32 buffer that starts non-zero:
     out = out0 + dW1 + dW2, each GEMM as accurate as the FP32-output wgrad (1e-4 of |a||b|) and each
@@ -395,7 +411,7 @@ def test_wgrad_fp32_accumulate(shape):
 
 
 def test_wgrad_accumulate_paths_and_empty_sum():
-    splits = {fq.fp8bq_gemm_plan(fq.OP_WGRAD, *s)[2] > 1 for s in [(2048, 256, 256), (512, 2048, 1536)]}
+    splits = {fq.fp8bq_gemm_plan(fq.OP_WGRAD, *s)[2] > 1 for s in [(4096, 256, 256), (512, 2048, 1536)]}
     assert splits == {True, False}  # the cases above reach both epilogues
     # a zero-length contraction adds nothing: the buffer is left as it was
     out = torch.full((128, 256), 3.25, dtype=torch.float32, device=DEV)
@@ -438,11 +454,13 @@ def _expect_plan(op, shape, plan):
 
 
 @pytest.mark.parametrize("fa,fb", PAIRS)
-@pytest.mark.parametrize("shape,plan", [((256, 384, 256), (128, 128, 1)), ((2048, 512, 4096), (128, 128, 3)),
+@pytest.mark.parametrize("shape,plan", [((256, 384, 256), (64, 64, 1)), ((256, 256, 3072), (64, 64, 6)),
+                                        ((1024, 4096, 1024), (128, 128, 1)), ((128, 4096, 4096), (128, 128, 4)),
                                         ((4096, 4096, 256), (256, 256, 1))])
 def test_fprop_every_format_pair(fa, fb, shape, plan):
-    """Each of the four instruction format pairs (the MFMA's per-operand format fields) on the
-    128x128 kernel, its split contraction and the 256x256 kernel."""
+    """Each of the four instruction format pairs (the MFMA's per-operand format fields) on every
+    kernel form the planner picks: 64x64 and 128x128 tiles, each whole and with a split
+    contraction, and 256x256 tiles."""
     M, N, K = shape
     _expect_plan(fq.OP_FPROP, shape, plan)
     X = synth.random_bf16((M, K), seed=3001 + M + K, outliers=True)
@@ -452,7 +470,8 @@ def test_fprop_every_format_pair(fa, fb, shape, plan):
 
 
 @pytest.mark.parametrize("fa,fb", PAIRS)
-@pytest.mark.parametrize("shape,plan", [((256, 384, 256), (128, 128, 1)), ((4096, 4096, 256), (128, 128, 3)),
+@pytest.mark.parametrize("shape,plan", [((256, 384, 256), (64, 64, 1)), ((256, 3072, 256), (64, 64, 6)),
+                                        ((1024, 1024, 4096), (128, 128, 1)), ((128, 4096, 4096), (128, 128, 4)),
                                         ((8192, 256, 2048), (256, 256, 1))])
 def test_dgrad_every_format_pair(fa, fb, shape, plan):
     M, N, K = shape
@@ -464,7 +483,8 @@ def test_dgrad_every_format_pair(fa, fb, shape, plan):
 
 
 @pytest.mark.parametrize("fa,fb", PAIRS)
-@pytest.mark.parametrize("shape,plan", [((256, 384, 256), (128, 128, 1)), ((4096, 2048, 512), (128, 128, 3)),
+@pytest.mark.parametrize("shape,plan", [((256, 384, 256), (64, 64, 1)), ((3072, 256, 256), (64, 64, 6)),
+                                        ((1024, 1024, 4096), (128, 128, 1)), ((4096, 128, 4096), (128, 128, 4)),
                                         ((2048, 4096, 4096), (256, 256, 1))])
 def test_wgrad_every_format_pair(fa, fb, shape, plan):
     M, N, K = shape
