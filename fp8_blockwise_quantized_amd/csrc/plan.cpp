@@ -101,6 +101,8 @@ GemmPlan plan_gemm(int op, int64_t M, int64_t N, int64_t K, int cu_count) {
   p.tiles_m = cdiv(rows, p.tile_m);
   p.tiles_n = cdiv(cols, p.tile_n);
   p.split_k = work ? best_split(rows, cols, nkb, slots, p.shape, nullptr) : 1;
+  // (a split is only chosen for few tiles; this keeps the unit count in 31 bits whatever the tile)
+  if (p.split_k > 1 && p.tiles_m * p.tiles_n > (((int64_t)1 << 31) - 1) / p.split_k) p.split_k = 1;
   p.units = p.tiles_m * p.tiles_n * p.split_k;
   // persistent grid: one workgroup per slot (a multiple of 8, so each workgroup stays on one XCD's
   // range of tiles), or one per unit when there are fewer units

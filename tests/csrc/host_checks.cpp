@@ -96,6 +96,8 @@ int main() {
     const int cus = (int)(rng() % 4 == 0 ? rng() % 400 : 256);
     const GemmPlan p = plan_gemm(op, M, N, K, cus);
     EXPECT(p.split_k >= 1 && p.split_k <= kMaxSplit);
+    EXPECT(p.units <= ((int64_t)1 << 31) - 1);  // the kernels count work units in 32 bits
+    EXPECT(p.tile_m == tile_rows(p.shape) && p.tile_n == tile_cols(p.shape));
     if (p.units > 0) {
       EXPECT(p.grid >= 1 && p.grid <= p.units);
       EXPECT((p.split_k > 1) == (p.ws_gemm > 0));
