@@ -408,6 +408,19 @@ def test_planner_decisions_documented_for_the_decoder_block():
     for tokens, plan in ((512, (64, 64, 1)), (1024, (64, 64, 1)), (2048, (128, 128, 1)), (4096, (128, 128, 1)),
                          (8192, (256, 256, 1))):
         assert fq.fp8bq_gemm_plan(fq.OP_FPROP, tokens, 2048, 2048) == plan, tokens
+    # the kernel forms the GPU format-pair tests run (64x64 and 128x128 tiles, whole and split; 256x256)
+    forms = {fq.OP_FPROP: [((256, 384, 256), (64, 64, 1)), ((256, 256, 3072), (64, 64, 6)),
+                           ((1024, 4096, 1024), (128, 128, 1)), ((128, 4096, 4096), (128, 128, 4)),
+                           ((4096, 4096, 256), (256, 256, 1))],
+             fq.OP_DGRAD: [((256, 384, 256), (64, 64, 1)), ((256, 3072, 256), (64, 64, 6)),
+                           ((1024, 1024, 4096), (128, 128, 1)), ((128, 4096, 4096), (128, 128, 4)),
+                           ((8192, 256, 2048), (256, 256, 1))],
+             fq.OP_WGRAD: [((256, 384, 256), (64, 64, 1)), ((3072, 256, 256), (64, 64, 6)),
+                           ((1024, 1024, 4096), (128, 128, 1)), ((4096, 128, 4096), (128, 128, 4)),
+                           ((2048, 4096, 4096), (256, 256, 1))]}
+    for op, cases in forms.items():
+        for shape, plan in cases:
+            assert fq.fp8bq_gemm_plan(op, *shape) == plan, (op, shape)
     # the plan is a pure function of its arguments
     assert all(fq.fp8bq_gemm_plan(fq.OP_WGRAD, 8192, 4096, 1024) == fq.fp8bq_gemm_plan(fq.OP_WGRAD, 8192, 4096, 1024)
                for _ in range(3))
