@@ -19,6 +19,10 @@ Frobenius error of dgrad and wgrad against float64 products of the unquantized B
 in E5M2 and in E4M3 (sampled rows / columns).
 `--workload hyperball` times the Hyperball update (with the fixed-radius projection) of the decoder
 block's four FP32 master weights from BF16 gradients, and reports GB/s.
+`--workload planner` checks the tile planner: each GEMM of a fixed list (small-token fprops and
+dgrads, split and decoder-block wgrads) is timed under the library's plan and under every tile shape
+forced in turn (one child process per tile, since the override is read once per process), and the
+line reports for how many the planned tile (timed with the forced runs) is within 3% of the fastest.
 
 Prints ONE JSON line on stdout.  `value` = GEMM FLOPs of the step / wall time of the step (the
 quantize passes are inside the timed step).  `breakdown` holds per-product TFLOP/s and per-pass GB/s
@@ -57,8 +61,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", choices=["decoder", "delayed", "hyperball", "linear", "sweep", "qerror"],
-                   default="decoder")
+    p.add_argument("--workload", choices=["decoder", "delayed", "hyperball", "linear", "sweep", "qerror",
+                                          "planner", "planner-child"], default="decoder")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the single-linear, token-sweep and heavy-tailed workloads after the decoder step")
@@ -75,6 +79,9 @@ def main():
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the GEMMs would shard by tokens, with one all-reduce of dW per step).", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "planner":
+        return run_planner(args)  # spawns the timing children before this process touches the GPU
 
     import numpy as np
     import torch
@@ -106,6 +113,8 @@ def main():
         return run_qerror(torch, fq, synth, dev)
     elif args.workload == "linear":
         ops, bufs, desc = build_linear(torch, fq, synth, dev)
+    elif args.workload == "planner-child":
+        return run_planner_child(args, torch, fq, synth, dev)
     else:
         return run_sweep(args, torch, fq, synth, dev)
 
@@ -570,6 +579,99 @@ def run_sweep(args, torch, fq, synth, dev):
         res.append({"M": M, "ms": round(ms, 5), "tflops": round(tf, 1), "pct_peak": round(100 * tf / FP8_PEAK_TFLOPS, 1)})
         log(res[-1])
     print(json.dumps({"workload": "square-weight fprop sweep K=N=2048", "points": res}))
+
+
+# (op, M, N, K) in the C-ABI's meaning of each product: the small end of the token sweep, small and
+# split products, and the decoder block's GEMMs at 16384 tokens
+PLANNER_SHAPES = [
+    ("fprop", 512, 2048, 2048), ("fprop", 1024, 2048, 2048), ("fprop", 2048, 2048, 2048), ("fprop", 4096, 2048, 2048),
+    ("fprop", 2048, 512, 4096), ("fprop", 8192, 256, 2048), ("fprop", 16384, 2560, 2048), ("fprop", 16384, 11264, 2048),
+    ("dgrad", 512, 2048, 2048), ("dgrad", 1024, 2048, 2048), ("dgrad", 4096, 4096, 256), ("dgrad", 4096, 2048, 512),
+    ("dgrad", 16384, 2048, 5632),
+    ("wgrad", 8192, 256, 2048), ("wgrad", 4096, 2048, 512), ("wgrad", 16384, 256, 256), ("wgrad", 4096, 1024, 1024),
+    ("wgrad", 16384, 2048, 2048), ("wgrad", 16384, 2560, 2048), ("wgrad", 16384, 2048, 5632),
+    ("wgrad", 16384, 11264, 2048),
+]
+PLANNER_TILES = [("planner", None), ("64x64", 4), ("128x128", 0), ("256x256", 3)]  # FP8BQ_GEMM_TILE values
+
+
+def run_planner(args):
+    """Parent of the planner check: one child per tile choice, then the comparison."""
+    import subprocess
+    got = {}
+    for name, tile in PLANNER_TILES:
+        env = dict(os.environ)
+        env.pop("FP8BQ_GEMM_TILE", None)
+        if tile is not None:
+            env["FP8BQ_GEMM_TILE"] = str(tile)
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", "planner-child",
+               "--steps", str(args.steps), "--warmup", str(args.warmup)]
+        r = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=900)
+        if r.returncode != 0:
+            log(r.stderr[-3000:])
+            sys.exit(r.returncode)
+        got[name] = json.loads(r.stdout.strip().splitlines()[-1])["points"]
+        log(f"planner check: {name} timed")
+    points, within = [], 0
+    for i, (op, M, N, K) in enumerate(PLANNER_SHAPES):
+        us = {name: got[name][i]["us"] for name, _ in PLANNER_TILES}
+        forced = {name: v for name, v in us.items() if name != "planner"}
+        plans = {name: got[name][i]["plan"] for name in forced}
+        best = min(forced, key=forced.get)
+        # the planner's plan is one of the forced tiles' plans (that tile with its own best split):
+        # compare the timings of the same process kind, so process-to-process noise does not count
+        chosen = next((n for n in forced if plans[n] == got["planner"][i]["plan"]), None)
+        ratio = (forced[chosen] if chosen else us["planner"]) / forced[best]
+        within += ratio <= 1.03
+        points.append({"op": op, "shape": [M, N, K], "plan": got["planner"][i]["plan"], "us": us,
+                       "forced_plans": plans, "fastest_forced": best, "planned_tile": chosen,
+                       "planner_over_fastest": round(ratio, 3)})
+    print(json.dumps({
+        "metric": "GEMM tile planner: share of products whose planned tile is within 3% of the fastest tile",
+        "value": round(within / len(points), 3), "unit": "fraction", "n_gpus": 1, "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "dtype": "fp8_e4m3",
+        "data": "synthetic (N(0,1) activations, N(0,0.02) weights, N(0,1e-3) gradients, drawn on the device)",
+        "config": {"workload": "GEMM planner check: each product timed under the plan and under each forced "
+                               "tile shape (its own best split), median of per-call HIP events"},
+        "worst_planner_over_fastest": max(p["planner_over_fastest"] for p in points),
+        "points": points}), flush=True)
+
+
+def run_planner_child(args, torch, fq, synth, dev):
+    """Times each product of PLANNER_SHAPES under this process's plan (FP8BQ_GEMM_TILE forces a tile)."""
+    import numpy as np
+    E4 = fq.E4M3
+    res = []
+    for i, (op, M, N, K) in enumerate(PLANNER_SHAPES):
+        if op == "fprop":
+            qa, sa = fq.quantize_act_1x128(synth.device_normal_bf16((M, K), 500 + i, dev))
+            qb, sb = fq.quantize_weight_128x128(synth.device_normal_bf16((N, K), 600 + i, dev, std=0.02))
+            out, code = torch.empty((M, N), dtype=torch.bfloat16, device=dev), fq.OP_FPROP
+            fn = fq.prepare(fq.fp8bq_gemm_fprop, qa, sa, E4, qb, sb, E4, out, fq._workspace(code, M, N, K, dev))
+        elif op == "dgrad":
+            qa, sa = fq.quantize_act_1x128(synth.device_normal_bf16((M, N), 700 + i, dev, std=1e-3))
+            _, sb, qb = fq.quantize_weight_dual(synth.device_normal_bf16((N, K), 800 + i, dev, std=0.02))
+            out, code = torch.empty((M, K), dtype=torch.bfloat16, device=dev), fq.OP_DGRAD_WT
+            fn = fq.prepare(fq.fp8bq_gemm_dgrad_wt, qa, sa, E4, qb, sb, E4, out, fq._workspace(code, M, N, K, dev))
+        else:
+            qa, sa = fq.quantize_act_128x1(synth.device_normal_bf16((M, N), 900 + i, dev, std=1e-3))
+            qb, sb = fq.quantize_act_128x1(synth.device_normal_bf16((M, K), 1000 + i, dev))
+            out, code = torch.empty((N, K), dtype=torch.bfloat16, device=dev), fq.OP_WGRAD
+            fn = fq.prepare(fq.fp8bq_gemm_wgrad, qa, sa, E4, qb, sb, E4, out, fq._workspace(code, M, N, K, dev))
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+        res.append({"op": op, "shape": [M, N, K], "plan": list(fq.fp8bq_gemm_plan(code, M, N, K)), "us": round(us, 2)})
+        log(res[-1])
+        del qa, sa, qb, sb, out, fn
+    print(json.dumps({"points": res}), flush=True)
 
 
 # -----------------------------------------------------------------------------------------------
