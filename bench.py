@@ -157,7 +157,7 @@ def main():
     roof = roofline(fq, ops, dur_ms, with_traffic=args.workload == "decoder", copy_gbs=copies.get("stream"),
                     torch_copy_gbs=copies.get("torch"))
     if roof and "quantize" in roof["by_kind"] and args.workload == "decoder":
-        roof["by_kind"]["quantize"]["scrubbed"] = quant_scrubbed(torch, dev, ops, copies.get("stream"))
+        roof["by_kind"]["quantize"]["scrubbed"] = quant_scrubbed(torch, dev, ops, copies.get("stream"), fq=fq)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -808,28 +808,38 @@ def roofline(fq, ops, dur_ms, with_traffic=True, copy_gbs=None, torch_copy_gbs=N
     }
 
 
-def quant_scrubbed(torch, dev, ops, copy_gbs=None, reps=5, scrub_mib=512):
+def quant_scrubbed(torch, dev, ops, copy_gbs=None, reps=5, scrub_mib=512, fq=None):
     """Each quantize launch of the step timed on its own with cold caches: before every timed launch a
     read of `scrub_mib` MiB (twice the 256 MB Infinity Cache) evicts them, writing back what the
     earlier kernels left dirty, outside the event pair.  In the step a launch also pays for the
     write-back of the outputs of the kernels before it; here it does not.  GB/s at the algorithmic
-    bytes, over all launches (total bytes / total time) and per launch (mean of `reps`)."""
+    bytes, over all launches (total bytes / total time) and per launch (mean of `reps`).
+    With `fq`, the library's streaming copy of each launch's own byte count (half read, half written)
+    is timed the same way beside it: a copy's bandwidth depends on its size (the launch ramp weighs
+    on the shorter ones), so that is the like-for-like ceiling of each launch."""
     import numpy as np
     q = [o for o in ops if o["bytes"]]
     scrub = torch.ones(scrub_mib << 18, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in q]
+    runs = [o["fn"] for o in q]
+    if fq is not None:
+        for o in q:
+            n = (o["bytes"] // 2) // 16 * 16
+            a = torch.ones(n, dtype=torch.uint8, device=dev)
+            runs.append(fq.prepare(fq.fp8bq_stream_copy, a, torch.empty_like(a)))
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in runs]
           for _ in range(reps)]
     sink = []
     for r in range(reps):
-        for (e0, e1), o in zip(ev[r], q):
+        for (e0, e1), fn in zip(ev[r], runs):
             sink.append(scrub.sum())
             e0.record(stream)
-            o["fn"]()
+            fn()
             e1.record(stream)
     torch.cuda.synchronize()
-    ms = np.array([[e0.elapsed_time(e1) for e0, e1 in row] for row in ev]).mean(axis=0)
-    del scrub, sink
+    times = np.array([[e0.elapsed_time(e1) for e0, e1 in row] for row in ev]).mean(axis=0)
+    ms, cms = times[:len(q)], times[len(q):]
+    del scrub, sink, runs
     gbs = sum(o["bytes"] for o in q) / (ms.sum() * 1e-3) / 1e9
     out = {"achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
            "method": f"each launch alone after a {scrub_mib} MiB read that evicts the caches (mean of {reps})",
@@ -837,6 +847,11 @@ def quant_scrubbed(torch, dev, ops, copy_gbs=None, reps=5, scrub_mib=512):
                           for o, m in zip(q, ms)]}
     if copy_gbs:
         out["frac_of_copy"] = round(gbs / copy_gbs, 4)
+    if len(cms):
+        for r, c in zip(out["per_launch"], cms):
+            r.update(same_bytes_copy_ms=round(float(c), 5), frac_of_same_bytes_copy=round(float(c) / float(r["ms"]), 4))
+        out["same_bytes_copy_gbs"] = round(sum(o["bytes"] for o in q) / (cms.sum() * 1e-3) / 1e9, 1)
+        out["frac_of_same_bytes_copy"] = round(float(cms.sum()) / float(ms.sum()), 4)
     return out
 
 
