@@ -30,7 +30,8 @@ from HIP events recorded on the launch stream.  `roofline` is for the GEMM kerne
 per step, with `by_kind` entries for fprop, dgrad, wgrad (each against the FP8 peak) and the quantize
 passes (against HBM, beside the same run's streaming-copy and torch-copy bandwidths; `scrubbed` times
 each quantize launch again on its own after a 512 MiB read that evicts the caches, so that no launch
-reads from the caches or pays for the write-back of an earlier kernel's output).  After the timed steps, `configs`
+reads from the caches or pays for the write-back of an earlier kernel's output, each beside a streaming
+copy of its own byte count timed the same way).  After the timed steps, `configs`
 times the other workloads: the single 8192 x 8192 x 2048 linear, the token sweep K = N = 2048 with its
 knee, and the heavy-tailed gradients (dgrad / wgrad with dY in E5M2 and E4M3, and their quantization
 error).  `cpu_baseline` times the CPU oracle on a bounded sample of the same path (first 4096 tokens)
