@@ -162,10 +162,12 @@ __device__ __forceinline__ Unit unit_of(uint32_t u, uint32_t tiles_m, uint32_t t
 // offset 16*l, i.e. row l/8 and physical chunk l%8, whose logical chunk is (l%8) ^ swz(row).  Every
 // wave issues the same number of loads per stage (scale jobs are padded with loads into the sink), so
 // one s_waitcnt vmcnt(loads per stage) leaves exactly the newest stage in flight.
+// Workgroups per CU that the LDS ring allows for a 4-wave tile (the planner's slots per CU: four for
+// 64x64, two for 128x128); the launch bound then keeps the registers low enough for that residency.
 template <int BM, int BN, int NW, int NSTAGE>
 struct StageMinBlocks {
   static constexpr int kStage = (BM + BN) * 128 + BM * 4 + 64 * 4 + 256;  // lower bound of STAGE
-  static constexpr int value = (NW == 4 && 2 * NSTAGE * kStage <= 160 * 1024) ? 2 : 1;
+  static constexpr int value = NW != 4 ? 1 : 4 * NSTAGE * kStage <= 160 * 1024 ? 4 : 2 * NSTAGE * kStage <= 160 * 1024 ? 2 : 1;
 };
 
 template <int OP, int BM, int BN, int WGM, int WGN, int NSTAGE, int SBM, int FA, int FB, int OUTF32>
@@ -418,11 +420,11 @@ __global__ __launch_bounds__(WGM* WGN * 64, (StageMinBlocks<BM, BN, WGM * WGN, N
         sbc[j] = *reinterpret_cast<const v4f*>(ssb + wn * WTN + 16 * j + 4 * (lane >> 4));
     }
     v4f p[NTILE];
-    // Two workgroups per CU (one wave of each per SIMD): a wave runs its MFMA steps at raised
-    // priority and drops back at the stage barrier, so the two workgroups drift out of phase instead
-    // of contending for the matrix pipe and the refill at the same time (+6% on a 128x128-tile
-    // wgrad; neutral with one workgroup per CU, where it is not used).
-    constexpr bool PRIO = StageMinBlocks<BM, BN, NW, NSTAGE>::value == 2;
+    // Several workgroups per CU (one wave of each per SIMD): a wave runs its MFMA steps at raised
+    // priority and drops back at the stage barrier, so the workgroups drift out of phase instead of
+    // contending for the matrix pipe and the refill at the same time (+6% on a 128x128-tile wgrad;
+    // neutral with one workgroup per CU, where it is not used).
+    constexpr bool PRIO = StageMinBlocks<BM, BN, NW, NSTAGE>::value >= 2;
     if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
