@@ -613,6 +613,20 @@ def run_planner(args):
             sys.exit(r.returncode)
         got[name] = json.loads(r.stdout.strip().splitlines()[-1])["points"]
         log(f"planner check: {name} timed")
+    value, points = planner_summary(got)
+    print(json.dumps({
+        "metric": "GEMM tile planner: share of products whose planned tile is within 3% of the fastest tile",
+        "value": value, "unit": "fraction", "n_gpus": 1, "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "dtype": "fp8_e4m3",
+        "data": "synthetic (N(0,1) activations, N(0,0.02) weights, N(0,1e-3) gradients, drawn on the device)",
+        "config": {"workload": "GEMM planner check: each product timed under the plan and under each forced "
+                               "tile shape (its own best split), median of per-call HIP events"},
+        "worst_planner_over_fastest": max(p["planner_over_fastest"] for p in points),
+        "points": points}), flush=True)
+
+
+def planner_summary(got):
+    """(share within 3%, per-product records) from the children's points, keyed by PLANNER_TILES name."""
     points, within = [], 0
     for i, (op, M, N, K) in enumerate(PLANNER_SHAPES):
         us = {name: got[name][i]["us"] for name, _ in PLANNER_TILES}
@@ -627,15 +641,7 @@ def run_planner(args):
         points.append({"op": op, "shape": [M, N, K], "plan": got["planner"][i]["plan"], "us": us,
                        "forced_plans": plans, "fastest_forced": best, "planned_tile": chosen,
                        "planner_over_fastest": round(ratio, 3)})
-    print(json.dumps({
-        "metric": "GEMM tile planner: share of products whose planned tile is within 3% of the fastest tile",
-        "value": round(within / len(points), 3), "unit": "fraction", "n_gpus": 1, "higher_is_better": True,
-        "steps": args.steps, "warmup": args.warmup, "dtype": "fp8_e4m3",
-        "data": "synthetic (N(0,1) activations, N(0,0.02) weights, N(0,1e-3) gradients, drawn on the device)",
-        "config": {"workload": "GEMM planner check: each product timed under the plan and under each forced "
-                               "tile shape (its own best split), median of per-call HIP events"},
-        "worst_planner_over_fastest": max(p["planner_over_fastest"] for p in points),
-        "points": points}), flush=True)
+    return round(within / len(points), 3), points
 
 
 def run_planner_child(args, torch, fq, synth, dev):

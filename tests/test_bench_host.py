@@ -80,3 +80,23 @@ def test_per_launch_statistics():
     assert b["per_launch"][1] == {"op": "a.fprop", "ms": 0.2, "ms_median": 0.19, "ms_min": 0.18,
                                   "tflops": round(ops[1]["flops"] / 0.2e-3 / 1e12, 1)}
     assert b["fprop"]["launches"] == 1 and b["quant_dual"]["gbs"] == round(ops[0]["bytes"] / 0.05e-3 / 1e9, 1)
+
+
+def test_planner_summary_compares_like_with_like():
+    """The planner check counts a product as planned well when the forced run with the planner's own
+    plan is within 3% of the fastest forced run (so noise between processes does not count); the
+    planner's own timing only stands in when no forced tile reproduces its plan."""
+    n = len(bench.PLANNER_SHAPES)
+    tiles = {"64x64": [64, 64, 1], "128x128": [128, 128, 1], "256x256": [256, 256, 1]}
+    got = {name: [{"plan": plan, "us": 10.0} for _ in range(n)] for name, plan in tiles.items()}
+    got["planner"] = [{"plan": [128, 128, 1], "us": 12.0} for _ in range(n)]  # slower process, same plan
+    got["64x64"][0]["us"] = 9.0       # product 0: a faster tile than the planned one (11% off)
+    got["256x256"][1]["us"] = 9.8     # product 1: faster by 2%, still within 3%
+    got["planner"][2]["plan"] = [32, 32, 1]  # product 2: no forced tile has that plan -> planner's time
+    value, points = bench.planner_summary(got)
+    assert points[0]["fastest_forced"] == "64x64" and points[0]["planned_tile"] == "128x128"
+    assert abs(points[0]["planner_over_fastest"] - 10.0 / 9.0) < 1e-3
+    assert points[1]["planner_over_fastest"] == round(10.0 / 9.8, 3)
+    assert points[2]["planned_tile"] is None and points[2]["planner_over_fastest"] == 1.2
+    assert all(p["planner_over_fastest"] == 1.0 for p in points[3:])
+    assert value == round((n - 2) / n, 3)
